@@ -1,0 +1,473 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula or re-calls the routine it
+uses; each compares it with something independent: a brute-force matrix
+built from the definition, a different library routine, a closed form, an
+invariant, a hand-constructed quantizer case, an exhaustive enumeration, a
+statistic, or a value the pages print.  ``tests/test_oracle_mutants.py``
+plants plausible mistakes in the oracle and checks that these pins catch
+them.
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def _random_signs(n, seed):
+    return (1 - 2 * _rng(seed).integers(0, 2, n)).astype(np.int8)
+
+
+# ---------------------------------------------------------------- signs ----
+
+def check_splitmix64():
+    with open(os.path.join(GOLDEN, "splitmix64_seed1234567.txt")) as f:
+        lines = [l.strip() for l in f if l.strip() and not l.startswith("#")]
+    seed = int(lines[0].split()[1])
+    want = [int(v) for v in lines[1:]]
+    assert O.splitmix64(seed, len(want)) == want
+
+
+def test_splitmix64_published_outputs():
+    check_splitmix64()
+
+
+def test_sign_vector_lengths_and_values():
+    for D in (2, 4, 128, 256):
+        s = O.plan_signs(D, O.SRFT, 7)
+        assert s.shape == (D // 2,) and set(np.unique(s)) <= {-1, 1}
+        s = O.plan_signs(D, O.SRHT, 7)
+        assert s.shape == (D,)
+    # bit i of word i // 64 -> sign 1 - 2 bit: word 0 of seed 1234567 is odd
+    # (6457827717110365317 ends in binary ...101), so the first sign is -1,
+    # the second +1, the third -1.
+    s = O.plan_signs(256, O.SRHT, 1234567)
+    assert list(s[:3]) == [-1, 1, -1]
+    # bit 64 comes from word 1 = 3203168211198807973 (odd) -> -1
+    assert s[64] == -1
+
+
+# ------------------------------------------------------------ rotations ----
+
+def check_srft_bruteforce(Ds=(2, 4, 8, 16)):
+    for D in Ds:
+        s = _random_signs(D // 2, D)
+        R = O.rotation_matrix(D, O.SRFT, s)
+        Rb = np.array(O.srft_matrix_bruteforce(D, [int(v) for v in s]))
+        assert np.max(np.abs(R - Rb)) < 1e-12, D
+
+
+def check_srht_bruteforce(Ds=(2, 4, 8, 16)):
+    for D in Ds:
+        s = _random_signs(D, D + 1)
+        R = O.rotation_matrix(D, O.SRHT, s)
+        Rb = np.array(O.srht_matrix_bruteforce(D, [int(v) for v in s]))
+        assert np.max(np.abs(R - Rb)) < 1e-12, D
+        # scipy's Sylvester Hadamard, scaled to be orthogonal
+        Rs = scipy.linalg.hadamard(D) / math.sqrt(D) * s[None, :]
+        assert np.max(np.abs(R - Rs)) < 1e-12, D
+
+
+def check_srft_against_dft_matrix(Ds=(8, 128, 256)):
+    """pack(F diag(s) x) with F = scipy's explicit unitary DFT matrix."""
+    for D in Ds:
+        M = D // 2
+        s = _random_signs(M, 3 * D)
+        F = scipy.linalg.dft(M, scale="sqrtn")
+        x = _rng(D).standard_normal((5, D))
+        z = x[:, 0::2] + 1j * x[:, 1::2]
+        Z = (F @ (s[:, None] * z.T)).T
+        want = np.empty_like(x)
+        want[:, 0::2] = Z.real
+        want[:, 1::2] = Z.imag
+        got = O.rotate_forward(x, O.SRFT, s)
+        assert np.max(np.abs(got - want)) < 1e-12, D
+
+
+def check_srft_one_hot(D=128):
+    """Closed-form columns: e_{2k} and e_{2k+1} through the unitary DFT."""
+    M = D // 2
+    s = _random_signs(M, 99)
+    c = 1 / math.sqrt(M)
+    for k in (0, 1, 5, M - 1):
+        m = np.arange(M)
+        ang = 2 * math.pi * k * m / M
+        x = np.zeros(D)
+        x[2 * k] = 1
+        y = O.rotate_forward(x, O.SRFT, s)
+        assert np.allclose(y[0::2], s[k] * np.cos(ang) * c, atol=1e-14)
+        assert np.allclose(y[1::2], -s[k] * np.sin(ang) * c, atol=1e-14)
+        x = np.zeros(D)
+        x[2 * k + 1] = 1
+        y = O.rotate_forward(x, O.SRFT, s)
+        assert np.allclose(y[0::2], s[k] * np.sin(ang) * c, atol=1e-14)
+        assert np.allclose(y[1::2], s[k] * np.cos(ang) * c, atol=1e-14)
+    # e_0 -> half the channels equal s_0 / sqrt(M), the rest zero
+    y = O.rotate_forward(np.eye(D)[0], O.SRFT, s)
+    assert np.allclose(y[0::2], s[0] * c) and np.allclose(y[1::2], 0)
+
+
+def check_orthogonal_and_inverse(Ds=(16, 128, 256)):
+    for D in Ds:
+        for rot in (O.SRFT, O.SRHT):
+            s = O.plan_signs(D, rot, 5 + D)
+            R = O.rotation_matrix(D, rot, s)
+            assert np.max(np.abs(R @ R.T - np.eye(D))) < 1e-12
+            x = _rng(D).standard_normal((7, D)) * 3
+            y = O.rotate_forward(x, rot, s)
+            assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+            assert np.max(np.abs(O.rotate_inverse(y, rot, s) - x)) < 1e-12
+            # row i of the inverse applied to I is R^T e_i = row i of R
+            assert np.max(np.abs(O.rotate_inverse(np.eye(D), rot, s) - R)) < 1e-12
+
+
+def test_srft_equals_bruteforce_matrix():
+    check_srft_bruteforce()
+
+
+def test_srht_equals_closed_form_and_scipy():
+    check_srht_bruteforce()
+
+
+def test_srft_equals_explicit_dft_matrix():
+    check_srft_against_dft_matrix()
+
+
+def test_srft_one_hot_closed_form():
+    check_srft_one_hot(128)
+    check_srft_one_hot(256)
+
+
+def test_rotations_orthogonal_inverse_exact():
+    check_orthogonal_and_inverse()
+
+
+def test_identity_rotation():
+    x = _rng(1).standard_normal((3, 64))
+    assert np.array_equal(O.rotate_forward(x, O.IDENTITY, O.plan_signs(64, O.IDENTITY, 0)), x)
+
+
+# ------------------------------------------------------------ quantizer ----
+
+def _ident_encode(x_vals, lam_vals):
+    """Encode one vector with the identity rotation: w = lambda * x."""
+    x = np.asarray(x_vals, dtype=np.float16)[None, :]
+    lam = np.asarray(lam_vals, dtype=np.float32)[None, :]
+    codes, scales, w = O.encode(x, lam, O.IDENTITY, O.plan_signs(x.shape[-1], O.IDENTITY, 0))
+    return codes[0], scales[0], w[0]
+
+
+def check_exact_construction():
+    """w_j = k_j * sigma with max |k_j| = 7 gives sigma and k back exactly."""
+    rng = _rng(11)
+    D = 64
+    for sigma in (np.float16(0.0137), np.float16(1.0), np.float16(3.75), np.float16(611.5)):
+        k = rng.integers(-7, 8, D)
+        k[3] = 7
+        k[40] = -7
+        codes, scales, _ = _ident_encode(k.astype(np.float16), np.full(D, np.float32(sigma)))
+        assert np.all(scales == sigma), (sigma, scales)
+        assert np.array_equal(O.unpack_nibbles(codes[None])[0], k.astype(np.int8))
+
+
+def check_half_even_ties():
+    D = 32
+    x = np.zeros(D, dtype=np.float16)
+    x[:8] = [7, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5]   # a = 7 -> sigma = 1
+    codes, scales, _ = _ident_encode(x, np.ones(D))
+    assert scales[0] == 1
+    q = O.unpack_nibbles(codes[None])[0]
+    assert list(q[:8]) == [7, 0, 2, 2, 0, -2, -2, 4]
+
+
+def check_zero_group():
+    D = 64
+    x = np.zeros(D, dtype=np.float16)
+    x[32:] = np.linspace(-3, 3, 32).astype(np.float16)
+    codes, scales, _ = _ident_encode(x, np.ones(D))
+    assert scales[0] == 0 and not np.signbit(scales[0])
+    assert np.all(codes[:16] == 0x88)
+
+
+def check_subnormal_scale():
+    """a / 7 below the fp16 normal range: the scale rounds to a subnormal and
+    the clamp to [-8, 7] engages; expected values by exact rational
+    arithmetic."""
+    D = 32
+    ulp = Fraction(1, 2 ** 24)                 # fp16 subnormal spacing
+    mult = [10, -10, 3, -3, 1, 0, 7, -6] + [0] * 24
+    x = np.array([float(m * ulp) for m in mult], dtype=np.float16)
+    codes, scales, _ = _ident_encode(x, np.ones(D))
+    a = max(abs(m) for m in mult) * ulp
+    t = a / 7                                   # 10/7 ulp -> rounds to 1 ulp
+    sig = Fraction(round(t / ulp)) * ulp        # nearest multiple (no tie here)
+    assert Fraction(float(scales[0])) == sig
+    want = []
+    for m in mult:
+        r = Fraction(m) * ulp / sig
+        k = math.floor(r + Fraction(1, 2))
+        want.append(max(-8, min(7, k)))
+    assert list(O.unpack_nibbles(codes[None])[0]) == want
+    assert -8 in want and 7 in want
+
+
+def check_error_bound(n=4000, D=128, seed=3):
+    rng = _rng(seed)
+    x = (rng.standard_normal((n, D)) * np.exp(0.5 * rng.standard_normal(D))).astype(np.float16)
+    lam = np.exp(0.3 * rng.standard_normal(D)).astype(np.float32)
+    for rot in (O.SRFT, O.SRHT):
+        s = O.plan_signs(D, rot, 42)
+        codes, scales, w = O.encode(x, lam, rot, s)
+        q = O.unpack_nibbles(codes).astype(np.float64)
+        sig = np.repeat(scales.astype(np.float64), O.GROUP, axis=-1)
+        normal = sig >= 2.0 ** -14
+        err = np.abs(w - q * sig)
+        slack = np.abs(w) * 2.0 ** -23               # float32 rounding of w
+        assert np.all((err <= sig / 2 + slack)[normal])
+        # x-domain bound through orthogonality: ||x - x^||_2 <= ||sigma/(2 lambda)||_2
+        xh = O.decode(codes, scales, lam, rot, s)
+        lhs = np.linalg.norm(x.astype(np.float64) - xh, axis=-1)
+        rhs = np.linalg.norm(sig / (2 * lam.astype(np.float64)), axis=-1)
+        assert np.all(lhs <= rhs * (1 + 1e-6) + 1e-9)
+
+
+def check_nibbles_exhaustive():
+    pairs = np.array([[a, b] for a in range(-8, 8) for b in range(-8, 8)], dtype=np.int8)
+    packed = O.pack_nibbles(pairs)
+    assert sorted(packed[:, 0].tolist()) == list(range(256))
+    assert np.array_equal(O.unpack_nibbles(packed), pairs)
+    allb = np.arange(256, dtype=np.uint8)[:, None]
+    assert np.array_equal(O.pack_nibbles(O.unpack_nibbles(allb)), allb)
+    # layout: even channel low nibble, offset binary
+    assert O.pack_nibbles(np.array([[-8, 7]]))[0, 0] == 0xF0
+    assert O.pack_nibbles(np.array([[7, -8]]))[0, 0] == 0x0F
+    assert O.pack_nibbles(np.array([[0, 0]]))[0, 0] == 0x88
+    assert O.pack_nibbles(np.array([[1, -1]]))[0, 0] == 0x79
+
+
+def test_exact_quantizer_construction():
+    check_exact_construction()
+
+
+def test_round_half_to_even():
+    check_half_even_ties()
+
+
+def test_all_zero_group():
+    check_zero_group()
+
+
+def test_subnormal_scale_exact_codes():
+    check_subnormal_scale()
+
+
+def test_error_bound_scale_over_two():
+    check_error_bound()
+
+
+def test_nibble_layout_exhaustive():
+    check_nibbles_exhaustive()
+
+
+def check_uniform_noise_statistic(n=12000, D=128, seed=5):
+    """Away from the group maximum the rounding error behaves like uniform
+    noise of width sigma: E[(w - q sigma)^2] / (sigma^2 / 12) ~ 1 (the
+    bounded-noise model behind the rank-reduction paper's perturbation
+    argument).  Sanity check within 5% on ~1.5e6 samples."""
+    rng = _rng(seed)
+    x = (rng.standard_normal((n, D))).astype(np.float16)
+    lam = np.ones(D, dtype=np.float32)
+    s = O.plan_signs(D, O.SRFT, 1)
+    codes, scales, w = O.encode(x, lam, O.SRFT, s)
+    q = O.unpack_nibbles(codes).astype(np.float64)
+    sig = np.repeat(scales.astype(np.float64), O.GROUP, axis=-1)
+    wg = np.abs(w).reshape(n, D // O.GROUP, O.GROUP)
+    is_max = (wg == wg.max(axis=-1, keepdims=True)).reshape(n, D)
+    ratio = ((w - q * sig) ** 2 / (sig ** 2 / 12))[~is_max]
+    assert ratio.size > 1_000_000
+    assert abs(ratio.mean() - 1) < 0.05, ratio.mean()
+
+
+def test_uniform_noise_statistic():
+    check_uniform_noise_statistic()
+
+
+def check_compression_figure():
+    vals = {}
+    with open(os.path.join(GOLDEN, "compression.txt")) as f:
+        for l in f:
+            if l.strip() and not l.startswith("#"):
+                k, v = l.split()
+                vals[k] = float(v)
+    G = int(vals["group"])
+    for D in (128, 256):
+        r = O.compression_ratio(D, G)
+        assert round(r, 2) == vals["explainer_max"]
+        assert r >= vals["abstract_min"]
+    # the oracle's actual buffers have exactly that many bytes
+    x = np.zeros((1, 128), dtype=np.float16)
+    codes, scales, _ = O.encode(x, np.ones(128), O.SRFT, O.plan_signs(128, O.SRFT, 0))
+    assert x.nbytes / (codes.nbytes + scales.nbytes) == O.compression_ratio(128, G)
+
+
+def test_compression_matches_printed_figure():
+    check_compression_figure()
+
+
+# ------------------------------------------------------------ boundaries ---
+
+def test_boundary_distances_on_constructed_values():
+    D = 32
+    w = np.zeros((1, D))
+    w[0, :4] = [7.0, 0.5, 2.25, -3.4999]
+    code_d, scale_d = O.boundary_distances(w, np.array([[1.0]], dtype=np.float16))
+    assert code_d[0, 1] == 0 and abs(code_d[0, 2] - 0.25) < 1e-15
+    assert abs(code_d[0, 3] - 1e-4) < 1e-12
+    # a / 7 exactly at an fp16 midpoint: 1 + 2^-11 lies between 1 and 1 + 2^-10
+    w2 = np.zeros((1, D))
+    w2[0, 0] = 7 * (1 + 2.0 ** -11)
+    _, sd = O.boundary_distances(w2, np.array([[1.0]], dtype=np.float16))
+    assert sd[0, 0] == 0
+
+
+# ------------------------------------------------------------- decode -----
+
+def test_decode_of_exact_construction():
+    D = 64
+    k = _rng(2).integers(-8, 8, D).astype(np.int8)
+    sig = np.array([0.75, 0.03125], dtype=np.float16)
+    lam = np.exp(0.3 * _rng(3).standard_normal(D))
+    codes = O.pack_nibbles(k[None])
+    got = O.decode(codes, sig[None], lam, O.IDENTITY, O.plan_signs(D, O.IDENTITY, 0))[0]
+    want = k * np.repeat(sig.astype(np.float64), 32) / lam
+    assert np.max(np.abs(got - want)) < 1e-15
+
+
+def test_decode_inverts_rotation_on_grid_values():
+    """If lambda*Rx already sits on the code grid, decode returns x."""
+    D = 128
+    for rot in (O.SRFT, O.SRHT):
+        s = O.plan_signs(D, rot, 9)
+        k = _rng(rot).integers(-7, 8, (3, D)).astype(np.int8)
+        k[:, ::32] = 7
+        sig = np.float16(0.5)
+        lam = np.ones(D)
+        y = k * float(sig)
+        x = O.rotate_inverse(y, rot, s)
+        codes = O.pack_nibbles(k)
+        got = O.decode(codes, np.full((3, D // 32), sig), lam, rot, s)
+        assert np.max(np.abs(got - x)) < 1e-12
+
+
+# ------------------------------------------------------------ attention ---
+
+def _tiny_cache(B, Hkv, T, D, rot, seed):
+    rng = _rng(seed)
+    s = O.plan_signs(D, rot, seed)
+    x = (rng.standard_normal((B, Hkv, T, D)) * 2).astype(np.float16)
+    lam = np.exp(0.3 * rng.standard_normal((Hkv, D))).astype(np.float32)
+    codes, scales, _ = O.encode(x, lam[None, :, None, :], rot, s)
+    return codes, scales, lam, s
+
+
+def _brute_attention(q16, kc, ks, lk, vc, vs, lv, L, sm_scale, D, signs):
+    """Pure-Python loops: unpack by hand, rescale, apply the brute-force
+    SRFT matrix transposed, exponentiate and average."""
+    R = O.srft_matrix_bruteforce(D, [int(v) for v in signs])
+    def dec(code_row, scale_row, lam):
+        y = []
+        for j in range(D):
+            byte = int(code_row[j // 2])
+            nib = (byte & 0xF) if j % 2 == 0 else (byte >> 4)
+            y.append((nib - 8) * float(scale_row[j // 32]) / float(lam[j]))
+        return [sum(R[i][c] * y[i] for i in range(D)) for c in range(D)]
+    B, Hq, _ = q16.shape
+    Hkv = kc.shape[1]
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            Ks = [dec(kc[b, g, t], ks[b, g, t], lk[g]) for t in range(L)]
+            Vs = [dec(vc[b, g, t], vs[b, g, t], lv[g]) for t in range(L)]
+            qv = [float(v) for v in q16[b, h]]
+            e = [sm_scale * sum(qv[i] * Kt[i] for i in range(D)) for Kt in Ks]
+            mx = max(e)
+            p = [math.exp(v - mx) for v in e]
+            tot = sum(p)
+            for c in range(D):
+                out[b, h, c] = sum(p[t] * Vs[t][c] for t in range(L)) / tot
+    return out
+
+
+def check_attention_bruteforce():
+    D, B, Hkv, Hq, T = 32, 2, 2, 4, 6
+    kc, ks, lk, s = _tiny_cache(B, Hkv, T, D, O.SRFT, 21)
+    vc, vs, lv, _ = _tiny_cache(B, Hkv, T, D, O.SRFT, 21)
+    vc, vs, lv = vc[:, :, ::-1].copy(), vs[:, :, ::-1].copy(), lv[::-1].copy()
+    q = (_rng(4).standard_normal((B, Hq, D))).astype(np.float16)
+    for L in (1, 3, T):
+        sm = 1 / math.sqrt(D)
+        got = O.attention_int4(q, kc, ks, lk, vc, vs, lv, L, sm, O.SRFT, s)
+        want = _brute_attention(q, kc, ks, lk, vc, vs, lv, L, sm, D, s)
+        assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_attention_bruteforce_loops():
+    check_attention_bruteforce()
+
+
+def test_attention_special_cases():
+    D, B, Hkv, Hq, T = 128, 1, 2, 8, 16
+    kc, ks, lk, s = _tiny_cache(B, Hkv, T, D, O.SRFT, 5)
+    vc, vs, lv, _ = _tiny_cache(B, Hkv, T, D, O.SRFT, 6)
+    q = (_rng(8).standard_normal((B, Hq, D))).astype(np.float16)
+    V = np.stack([O.decode(vc[0, g], vs[0, g], lv[g], O.SRFT, s) for g in range(Hkv)])
+    # seq_len = 1: the output is the single decoded value vector
+    o = O.attention_int4(q, kc, ks, lk, vc, vs, lv, 1, 0.1, O.SRFT, s)
+    for h in range(Hq):
+        assert np.max(np.abs(o[0, h] - V[h // 4, 0])) < 1e-12
+    # q = 0: uniform weights, the mean of the decoded values
+    o = O.attention_int4(np.zeros_like(q), kc, ks, lk, vc, vs, lv, T, 0.1, O.SRFT, s)
+    for h in range(Hq):
+        assert np.max(np.abs(o[0, h] - V[h // 4].mean(0))) < 1e-12
+    # all keys equal: uniform weights again
+    kc2 = np.repeat(kc[:, :, :1], T, axis=2)
+    ks2 = np.repeat(ks[:, :, :1], T, axis=2)
+    o = O.attention_int4(q, kc2, ks2, lk, vc, vs, lv, T, 0.1, O.SRFT, s)
+    for h in range(Hq):
+        assert np.max(np.abs(o[0, h] - V[h // 4].mean(0))) < 1e-12
+    # a dominant key picks its value
+    k16 = np.zeros((B, Hkv, T, D), dtype=np.float16)
+    v16 = (_rng(9).standard_normal((B, Hkv, T, D))).astype(np.float16)
+    k16[0, :, 5, :] = 4.0
+    qq = np.full((B, Hq, D), 4.0, dtype=np.float16)
+    o = O.attention_f16(qq, k16, v16, T, 1.0)
+    assert np.max(np.abs(o[0, 0] - v16[0, 0, 5].astype(np.float64))) < 1e-12
+
+
+def test_attention_f16_matches_scipy_softmax():
+    import scipy.special
+    rng = _rng(12)
+    B, Hkv, Hq, T, D = 2, 2, 4, 40, 64
+    k = rng.standard_normal((B, Hkv, T, D)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, T, D)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    got = O.attention_f16(q, k, v, 33, 0.125)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // 2
+            e = 0.125 * (k[b, g, :33].astype(np.float64) @ q[b, h].astype(np.float64))
+            p = scipy.special.softmax(e)
+            assert np.max(np.abs(got[b, h] - p @ v[b, g, :33].astype(np.float64))) < 1e-12
