@@ -1,0 +1,256 @@
+"""Benchmark of the int4 KV-cache hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+  1. encode  the Qwen2.5-1.5B-shaped prefix (28 layers x {K,V} x 2 KV heads x
+             4096 tokens, D=128: 458,752 vectors) with SRFT;
+  2. decode  those codes back to fp16;
+  3. a decode step on the int4 cache (batch 64, 8 query heads over 2 KV
+     heads, D=128, 32768 cached tokens): append one token per sequence for K
+     and V with kvq_encode, then int4 decode-step attention over 32769 tokens.
+Steps rotate over four prefix batches and two int4 caches, so the working
+set (about 1.8 GB) is far beyond the 256 MB Infinity Cache.  The fp16-cache
+comparator (same attention over an unquantized cache) is timed in its own
+loop right after the timed region.
+
+Prints ONE JSON line.  `value` is the encode throughput (Mvec/s) over the
+timed region, measured with HIP events around each encode launch on the
+stream the kernels run on; ns/vec, GB/s and the attention microseconds per
+step are extra fields.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=4, help="prefix batches rotated over")
+    return ap.parse_args()
+
+
+def cpu_baseline(n_vec: int = 458752):
+    """The CPU oracle as it stands on the Qwen prefix workload (by default all
+    458,752 vectors of one step's encode and decode, about 10 s of
+    single-threaded numpy)."""
+    import numpy as np
+    import oracle as O
+    from kv_cache_int4_amd import workloads as W
+    cfg = W.CONFIGS["qwen"]
+    T = 4096
+    nb = min(cfg.B, max(1, -(-n_vec // (cfg.H * T))))
+    x, lam = W.prefix_inputs(W.Config(cfg.name, cfg.D, nb, cfg.H, T, cfg.law, cfg.index))
+    xs = x.numpy().reshape(-1, cfg.D)[:n_vec]
+    lv = np.repeat(lam.numpy()[:, :, None, :], T, axis=2).reshape(-1, cfg.D)[:n_vec]
+    signs = O.plan_signs(cfg.D, O.SRFT, cfg.sign_seed)
+    t0 = time.perf_counter()
+    codes, scales, _ = O.encode(xs, lv, O.SRFT, signs)
+    t1 = time.perf_counter()
+    O.decode(codes, scales, lv, O.SRFT, signs)
+    t2 = time.perf_counter()
+    return {
+        "value": n_vec / (t1 - t0) / 1e6,
+        "unit": "Mvec/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n_vec} vectors of the Qwen2.5-1.5B prefix workload (D=128, SRFT), "
+                  f"numpy float64 oracle; encode {(t1 - t0):.2f} s, decode {(t2 - t1):.2f} s",
+        "decode_Mvec_s": n_vec / (t2 - t1) / 1e6,
+    }
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the int4 KV-cache path is per-GPU work with no collectives", file=sys.stderr)
+        sys.exit(2)
+    # single-threaded numpy for the oracle leg
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
+    import torch
+    import kv_cache_int4_amd as K
+    from kv_cache_int4_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- prefix batches (Qwen2.5-1.5B shape) ----
+    cfg = W.CONFIGS["qwen"]
+    D = cfg.D
+    plan = K.Plan(D, 32, "srft", cfg.sign_seed)
+    sets = []
+    for i in range(args.sets):
+        c = W.Config(cfg.name, D, cfg.B, cfg.H, cfg.T, cfg.law, cfg.index + 10 * i)
+        x, lam = W.prefix_inputs(c, dev)
+        codes = torch.empty((cfg.B, cfg.H, cfg.T, D // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((cfg.B, cfg.H, cfg.T, D // 32), dtype=torch.float16, device=dev)
+        y = torch.empty_like(x)
+        sets.append((x, lam, codes, scales, y))
+    n_vec = cfg.vectors
+    log(f"prefix batches ready ({args.sets} x {n_vec} vectors)")
+
+    # ---- decode step (batch 64, Hq 8, Hkv 2, 32768 cached tokens) ----
+    dc = W.CONFIGS["decode"]
+    B, Hkv, Hq, T0 = dc.B, dc.H, 8, dc.T
+    L = T0 + 1
+    Tcap = T0 + 256
+    aplan = K.Plan(D, 32, "srft", dc.sign_seed)
+    k16, v16, lam_k, lam_v, q = W.decode_inputs(B, Hkv, Hq, Tcap, D, dc.data_seed, dev)
+    caches = []
+    for _ in range(2):
+        kc = torch.empty((B, Hkv, Tcap, D // 2), dtype=torch.uint8, device=dev)
+        ks = torch.empty((B, Hkv, Tcap, D // 32), dtype=torch.float16, device=dev)
+        vc, vs = torch.empty_like(kc), torch.empty_like(ks)
+        K.encode(aplan, k16[:, :, :T0], lam_k, kc, ks, 0)
+        K.encode(aplan, v16[:, :, :T0], lam_v, vc, vs, 0)
+        caches.append((kc, ks, vc, vs))
+    k_new = k16[:, :, T0:T0 + 1]
+    v_new = v16[:, :, T0:T0 + 1]
+    ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    sm = 1.0 / math.sqrt(D)
+    torch.cuda.synchronize()
+    log("decode-step caches ready")
+
+    phases = ("encode", "decode", "append", "attn")
+
+    def step(i, ev):
+        x, lam, codes, scales, y = sets[i % len(sets)]
+        kc, ks, vc, vs = caches[i % 2]
+        if ev: ev[0].record(stream)
+        K.encode(plan, x, lam, codes, scales)
+        if ev: ev[1].record(stream)
+        K.decode(plan, codes, scales, lam, y)
+        if ev: ev[2].record(stream)
+        K.encode(aplan, k_new, lam_k, kc, ks, T0)
+        K.encode(aplan, v_new, lam_v, vc, vs, T0)
+        if ev: ev[3].record(stream)
+        K.attn_decode(aplan, q, kc, ks, lam_k, vc, vs, lam_v, L, sm, out, ws)
+        if ev: ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    ms = {p: 0.0 for p in phases}
+    for ev in events:
+        for j, p in enumerate(phases):
+            ms[p] += ev[j].elapsed_time(ev[j + 1])
+    ms = {p: v / args.steps for p, v in ms.items()}
+
+    # ---- fp16-cache comparator, same shape ----
+    for _ in range(3):
+        K.attn_decode_f16(q, k16, v16, L, sm, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n16 = max(5, args.steps // 2)
+    e0.record(stream)
+    for _ in range(n16):
+        K.attn_decode_f16(q, k16, v16, L, sm, out, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    f16_us = e0.elapsed_time(e1) / n16 * 1e3
+
+    # ---- algorithmic bytes ----
+    enc_bytes = n_vec * (2 * D + D // 2 + 2 * (D // 32))          # 328 B / vector
+    attn_bytes = B * Hkv * L * 2 * (D // 2 + 2 * (D // 32))        # K and V codes + scales
+    attn16_bytes = B * Hkv * L * 2 * 2 * D
+    enc_s = ms["encode"] / 1e3
+    dec_s = ms["decode"] / 1e3
+    attn_us = (ms["append"] + ms["attn"]) * 1e3
+    enc_gbs = enc_bytes / enc_s / 1e9
+    dec_gbs = enc_bytes / dec_s / 1e9
+    attn_gbs = attn_bytes / (ms["attn"] / 1e3) / 1e9
+
+    # dominant launch of the step: the one with the largest share of step time
+    shares = {"attn": ms["attn"], "encode": ms["encode"], "decode": ms["decode"]}
+    dom = max(shares, key=shares.get)
+    if dom == "attn":
+        rl = {"kernel": "kvq_attn_decode (qrot + split-K stream + combine)", "bytes": attn_bytes,
+              "seconds": ms["attn"] / 1e3}
+    elif dom == "encode":
+        rl = {"kernel": "kvq_encode", "bytes": enc_bytes, "seconds": enc_s}
+    else:
+        rl = {"kernel": "kvq_decode", "bytes": enc_bytes, "seconds": dec_s}
+    achieved = rl["bytes"] / rl["seconds"] / 1e9
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "kernel": rl["kernel"], "algorithmic_bytes_per_launch": rl["bytes"],
+        "avg_launch_us": round(rl["seconds"] * 1e6, 2),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline()
+
+    res = {
+        "metric": "encode Mvec/s + ns/vec and HBM GB/s at D=128; int4 vs fp16 decode-attn µs/step",
+        "value": round(n_vec / enc_s / 1e6, 2),
+        "unit": "Mvec/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen2.5-1.5B-shaped prefix encode+decode (28 layers x {K,V} x 2 KV heads x 4096 "
+                        "tokens, D=128, SRFT, group 32) + GQA decode step on the int4 cache (batch 64, "
+                        "Hq 8 / Hkv 2, D=128, 32768 cached tokens + 1 appended)",
+            "vectors_per_step": n_vec, "D": D, "group": 32, "rotation": "srft",
+            "decode_step": {"B": B, "Hq": Hq, "Hkv": Hkv, "seq_len": L},
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "encode": {"us": round(ms["encode"] * 1e3, 2), "Mvec_s": round(n_vec / enc_s / 1e6, 1),
+                   "ns_per_vec": round(enc_s / n_vec * 1e9, 4), "GB_s": round(enc_gbs, 1),
+                   "frac_hbm": round(enc_gbs / HBM_PEAK_GBS, 4),
+                   "GFLOPS_5MlogM": round(n_vec * 5 * (D // 2) * math.log2(D // 2) / enc_s / 1e9, 1)},
+        "decode": {"us": round(ms["decode"] * 1e3, 2), "Mvec_s": round(n_vec / dec_s / 1e6, 1),
+                   "ns_per_vec": round(dec_s / n_vec * 1e9, 4), "GB_s": round(dec_gbs, 1),
+                   "frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4)},
+        "attention": {"int4_us_per_step": round(attn_us, 2), "append_us": round(ms["append"] * 1e3, 2),
+                      "int4_attn_us": round(ms["attn"] * 1e3, 2), "int4_attn_GB_s": round(attn_gbs, 1),
+                      "fp16_us_per_step": round(f16_us, 2),
+                      "fp16_GB_s": round(attn16_bytes / (f16_us / 1e6) / 1e9, 1),
+                      "int4_over_fp16": round(attn_us / f16_us, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * kvq.h -- C ABI of the MI355X int4 KV-cache quantizer (libkvq.so).
+ *
+ * The method ("When Quantization Is Free: An int4 KV Cache That Outruns fp16
+ * on Apple Silicon", M. A. Bergach, arXiv 2605.05699): every head vector of D
+ * channels is rotated by a sign-randomized FFT (SRFT), or optionally by a
+ * sign-randomized Walsh-Hadamard transform (SRHT), rescaled per channel by
+ * lambda, split into groups of 32 channels that each get one fp16 abs-max
+ * scale, and rounded to signed int4 codes packed two per byte.  The read side
+ * undoes it: unpack, rescale, inverse rotation -- alone (kvq_decode) or fused
+ * into decode-step attention (kvq_attn_decode).
+ *
+ * Sources, by page and section:
+ *   [abstract]  the paper's abstract (paperdance.org and mlsanity.com pages):
+ *               the fused pipeline, SRFT vs SRHT, the HuggingFace Cache role;
+ *   [M1]        gist.science explainer, "Methodik" 1: SRFT(x) =
+ *               pack(F . diag(s) . x), F the unitary DFT, s fixed random signs;
+ *   [M2]        same page, "Methodik" 2: load and sign, log2(d/2) FFT passes,
+ *               pack, per-channel lambda, per-group abs-max, round to int4,
+ *               two nibbles per byte;
+ *   [M3]        same page, "Methodik" 3: per-channel plus per-group scaling;
+ *   [Mem]       same page, "Speichereffizienz": 3.0x-3.56x compression, i.e.
+ *               int4 codes plus one fp16 scale per 32 channels.
+ *
+ * Conventions fixed here (the pages leave them open):
+ *   - pairing: z_k = x[2k] + i x[2k+1], k < D/2; one sign per pair (SRFT) or
+ *     per channel (SRHT); forward DFT kernel exp(-2 pi i k m / (D/2)) scaled by
+ *     (D/2)^-1/2; the output Z_m is unpaired to channels 2m (real) and 2m+1
+ *     (imaginary).  SRHT: y = D^-1/2 H_D (s . x), H_D in Sylvester order.
+ *   - signs: bit i of the SplitMix64 stream seeded with the plan seed (bit
+ *     i mod 64 of output i / 64), sign = 1 - 2 bit.
+ *   - group g = output channels [32 g, 32 g + 32); scale = fp16(absmax / 7)
+ *     rounded to nearest even, subnormals kept; code = clamp(rint_even(w /
+ *     scale), -8, 7), 0 where scale == 0; nibble = code + 8, channel 2m in
+ *     the low nibble of byte m.
+ *
+ * Memory: every tensor pointer is a DEVICE pointer owned by the caller.  No
+ * entry point allocates, frees or synchronizes; kernels are enqueued on the
+ * caller's stream (a hipStream_t passed as void*, NULL = the default stream)
+ * and device faults surface at the caller's next synchronization.  fp16 values
+ * are passed as uint16_t bit patterns.  Strides are in elements.
+ *
+ * Errors: every argument check runs on the host before anything is enqueued;
+ * a failing call has no side effects and returns a kvq_status other than
+ * KVQ_OK, with a detail string from kvq_last_error() (per thread).  A launch
+ * failure reported by the HIP runtime returns KVQ_ERR_HIP.  No C++ exception
+ * crosses this interface.
+ *
+ * Concurrency: calls on different streams may run concurrently when their
+ * outputs and workspaces do not overlap.  Inputs must not alias outputs.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = 1,      /* bad value: null pointer, size, stride, range */
+  KVQ_ERR_UNSUPPORTED = 2,  /* valid but not built: D, G or rotation */
+  KVQ_ERR_ALIGN = 3,        /* a pointer or row is not 16-byte aligned */
+  KVQ_ERR_WORKSPACE = 4,    /* workspace missing or too small */
+  KVQ_ERR_HIP = 5           /* the HIP runtime reported a launch error */
+} kvq_status;
+
+typedef enum {
+  KVQ_SRFT = 0,             /* sign-randomized FFT [M1] */
+  KVQ_SRHT = 1,             /* sign-randomized Walsh-Hadamard [abstract] */
+  KVQ_IDENTITY = 2          /* no rotation: exercises the quantizer alone */
+} kvq_rotation;
+
+typedef enum { KVQ_F16 = 0, KVQ_F32 = 1 } kvq_dtype;
+
+typedef struct kvq_plan kvq_plan;   /* opaque, immutable after creation */
+
+/* Version string of the library build. */
+const char* kvq_version(void);
+
+/* Name of a status code; never NULL. */
+const char* kvq_strerror(kvq_status s);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* Create a plan: head dimension D (128 or 256), group size G (32) and the
+ * rotation, with the sign vector drawn from SplitMix64(seed) [M1].  Pure host
+ * work: no GPU call.  *out receives a plan the caller releases with
+ * kvq_plan_destroy. */
+kvq_status kvq_plan_create(int32_t D, int32_t G, kvq_rotation rotation, uint64_t seed,
+                           kvq_plan** out);
+
+/* Release a plan (NULL is a no-op).  Work already enqueued does not use the
+ * plan object: its constants travel with each launch. */
+void kvq_plan_destroy(kvq_plan* plan);
+
+/* Copy the plan's sign vector to host memory: n = D/2 entries for SRFT, D for
+ * SRHT, 0 for IDENTITY; each entry is +1 or -1.  n must equal that count. */
+kvq_status kvq_plan_signs(const kvq_plan* plan, int8_t* host_signs, int64_t n);
+
+/* Read back D, G and the rotation of a plan (any output may be NULL). */
+kvq_status kvq_plan_info(const kvq_plan* plan, int32_t* D, int32_t* G, int32_t* rotation);
+
+/* Encode [M2]: for b < B, h < H, t < T rotate x[b,h,t,:] (fp16, element
+ * (b,h,t,j) at x + b*x_sb + h*x_sh + t*x_st + j; each row 16-byte aligned),
+ * multiply by lambda[b*lambda_sb + h*D + j] (fp32; lambda_sb = 0 shares one
+ * [H,D] table across the batch), quantize per group and write token t0 + t of
+ *   codes  uint8 [B, H, Tcap, D/2]   (dense, 16-byte aligned)
+ *   scales fp16  [B, H, Tcap, D/G]   (dense, 8-byte aligned).
+ * Requires 0 <= t0, t0 + T <= Tcap.  B, H or T of 0 is a no-op. */
+kvq_status kvq_encode(const kvq_plan* plan, const uint16_t* x, int64_t B, int64_t H, int64_t T,
+                      int64_t x_sb, int64_t x_sh, int64_t x_st,
+                      const float* lambda, int64_t lambda_sb,
+                      uint8_t* codes, uint16_t* scales, int64_t Tcap, int64_t t0,
+                      void* stream);
+
+/* Decode (the inverse of kvq_encode up to quantization): for tokens
+ * t0 .. t0+T-1 of codes/scales [B,H,Tcap,...] compute
+ *   x^[j] = (R^T ( (q . scale) / lambda ))[j]
+ * and write it to y (fp16 rounded to nearest even, or fp32) at
+ * y + b*y_sb + h*y_sh + t*y_st + j; fp16 rows must be 16-byte aligned. */
+kvq_status kvq_decode(const kvq_plan* plan, const uint8_t* codes, const uint16_t* scales,
+                      int64_t B, int64_t H, int64_t Tcap, int64_t t0, int64_t T,
+                      const float* lambda, int64_t lambda_sb,
+                      void* y, kvq_dtype y_dtype, int64_t y_sb, int64_t y_sh, int64_t y_st,
+                      void* stream);
+
+/* Rotate only (test hook sharing the encoder's transform): w[b,h,t,:] =
+ * lambda . (R x[b,h,t,:]) in fp32, w dense [B, H, T, D]. */
+kvq_status kvq_rotate(const kvq_plan* plan, const uint16_t* x, int64_t B, int64_t H, int64_t T,
+                      int64_t x_sb, int64_t x_sh, int64_t x_st,
+                      const float* lambda, int64_t lambda_sb, float* w, void* stream);
+
+/* Bytes of device workspace kvq_attn_decode and kvq_attn_decode_f16 need for
+ * this shape (split-K partial results). */
+kvq_status kvq_attn_workspace_size(int32_t D, int64_t B, int64_t Hq, int64_t seq_len,
+                                   size_t* bytes);
+
+/* Decode-step attention over the int4 cache (the read path fused with
+ * attention; the pages time it only end to end [abstract]): for each batch b
+ * and query head h, with kv head g = h / (Hq / Hkv),
+ *   out[b,h,:] = sum_t softmax_t(sm_scale q[b,h,:] . k^[b,g,t,:]) v^[b,g,t,:]
+ * over t < seq_len, where k^ and v^ are the decoded cache rows
+ * (codes/scales [B, Hkv, Tcap, ...] as written by kvq_encode, with lambda_k
+ * and lambda_v [Hkv, D] shared across the batch).  q is fp16 [B, Hq, D]
+ * dense; out is fp16 or fp32 [B, Hq, D] dense.  Scores are taken in the
+ * rotated basis (q . k^ = ((R q) / lambda_k) . (lambda_k R k^)) and the
+ * value average is rotated back once per head.  Requires Hq % Hkv == 0,
+ * 1 <= seq_len <= Tcap, and a workspace of kvq_attn_workspace_size bytes. */
+kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q,
+                           const uint8_t* k_codes, const uint16_t* k_scales, const float* lambda_k,
+                           const uint8_t* v_codes, const uint16_t* v_scales, const float* lambda_v,
+                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Tcap, int64_t seq_len,
+                           float sm_scale, void* out, kvq_dtype out_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same attention over an unquantized fp16 cache k, v [B, Hkv, Tcap, D]
+ * (dense): the fp16 comparator the pages measure the int4 cache against. */
+kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t Tcap, int64_t seq_len,
+                               float sm_scale, void* out, kvq_dtype out_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

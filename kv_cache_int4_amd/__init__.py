@@ -1,0 +1,227 @@
+"""Python binding of libkvq, the MI355X int4 KV-cache quantizer.
+
+Argument marshalling only: every step of encode, decode and attention runs in
+the HIP kernels of ``libkvq.so`` (built in-tree by ``kv_cache_int4_amd.build``).
+PyTorch supplies device memory and the current stream.  If the library is
+missing the import of the entry points raises; there is no fallback.
+
+Method: "When Quantization Is Free: An int4 KV Cache That Outruns fp16 on
+Apple Silicon" (arXiv 2605.05699) -- sign-randomized FFT (or Walsh-Hadamard)
+rotation, per-channel lambda, group-32 abs-max fp16 scale, int4 nibbles.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "KvqError", "Plan", "SRFT", "SRHT", "IDENTITY", "GROUP",
+    "library", "library_path", "encode", "decode", "rotate",
+    "attn_workspace_size", "attn_decode", "attn_decode_f16",
+    "cache_shapes",
+]
+
+SRFT, SRHT, IDENTITY = 0, 1, 2
+GROUP = 32
+_ROT_NAMES = {"srft": SRFT, "srht": SRHT, "identity": IDENTITY}
+_F16, _F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libkvq.so")
+
+
+class KvqError(RuntimeError):
+    """A libkvq call returned an error status."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"kvq status {status}: {detail}")
+
+
+_lib = None
+
+_i32, _i64, _u64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+
+
+def library() -> ctypes.CDLL:
+    """Load libkvq.so (once); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m kv_cache_int4_amd.build`")
+    L = ctypes.CDLL(path)
+    sig = {
+        "kvq_version": (ctypes.c_char_p, []),
+        "kvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "kvq_last_error": (ctypes.c_char_p, []),
+        "kvq_plan_create": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _u64, ctypes.POINTER(_vp)]),
+        "kvq_plan_destroy": (None, [_vp]),
+        "kvq_plan_signs": (ctypes.c_int, [_vp, _vp, _i64]),
+        "kvq_plan_info": (ctypes.c_int, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+        "kvq_encode": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _i64,
+                                      _vp, _vp, _i64, _i64, _vp]),
+        "kvq_decode": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64,
+                                      _vp, ctypes.c_int, _i64, _i64, _i64, _vp]),
+        "kvq_rotate": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+        "kvq_attn_workspace_size": (ctypes.c_int, [_i32, _i64, _i64, _i64, ctypes.POINTER(_sz)]),
+        "kvq_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _i64, _i64, _i64, _i64, _i64, _f32, _vp, ctypes.c_int,
+                                           _vp, _sz, _vp]),
+        "kvq_attn_decode_f16": (ctypes.c_int, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
+                                               _vp, ctypes.c_int, _vp, _sz, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise KvqError(status, library().kvq_last_error().decode())
+
+
+def _stream(t) -> int:
+    import torch
+    if t is None or not t.is_cuda:
+        return 0
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t) -> int:
+    return t.data_ptr() if t is not None else 0
+
+
+class Plan:
+    """Head dimension D, group G, rotation ("srft" | "srht" | "identity") and
+    the seed of the sign vector."""
+
+    def __init__(self, D: int = 128, G: int = GROUP, rotation="srft", seed: int = 0):
+        L = library()
+        rot = _ROT_NAMES[rotation] if isinstance(rotation, str) else int(rotation)
+        h = _vp()
+        _check(L.kvq_plan_create(D, G, rot, seed & ((1 << 64) - 1), ctypes.byref(h)))
+        self._h = h
+        self.D, self.G, self.rotation, self.seed = D, G, rot, seed
+
+    @property
+    def handle(self):
+        return self._h
+
+    def signs(self):
+        import numpy as np
+        n = {SRFT: self.D // 2, SRHT: self.D, IDENTITY: 0}[self.rotation]
+        out = np.zeros(n, dtype=np.int8)
+        _check(library().kvq_plan_signs(self._h, out.ctypes.data if n else None, n))
+        return out
+
+    def info(self):
+        D, G, R = _i32(), _i32(), _i32()
+        _check(library().kvq_plan_info(self._h, ctypes.byref(D), ctypes.byref(G), ctypes.byref(R)))
+        return D.value, G.value, R.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            library().kvq_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 -- interpreter shutdown
+            pass
+
+
+def cache_shapes(B: int, H: int, Tcap: int, D: int, G: int = GROUP):
+    """(codes shape, scales shape) of a dense int4 cache."""
+    return (B, H, Tcap, D // 2), (B, H, Tcap, D // G)
+
+
+def _lam_args(lam, H, D):
+    if lam.dim() == 2:
+        assert tuple(lam.shape) == (H, D)
+        return 0
+    assert lam.dim() == 3 and lam.shape[1:] == (H, D)
+    assert lam.stride(2) == 1 and lam.stride(1) == D
+    return 0 if lam.shape[0] == 1 else lam.stride(0)
+
+
+def _x_args(x, D):
+    assert x.dim() == 4 and x.shape[3] == D and x.stride(3) == 1, "x must be [B, H, T, D] with unit D stride"
+    return x.shape[0], x.shape[1], x.shape[2], x.stride(0), x.stride(1), x.stride(2)
+
+
+def encode(plan: Plan, x, lam, codes, scales, t0: int = 0):
+    """Quantize x [B, H, T, D] (fp16) into tokens t0..t0+T-1 of codes
+    [B, H, Tcap, D/2] (uint8) and scales [B, H, Tcap, D/G] (fp16)."""
+    import torch
+    assert x.dtype == torch.float16 and codes.dtype == torch.uint8 and scales.dtype == torch.float16
+    assert lam.dtype == torch.float32 and lam.is_contiguous()
+    assert codes.is_contiguous() and scales.is_contiguous()
+    B, H, T, sb, sh, st = _x_args(x, plan.D)
+    Tcap = codes.shape[2]
+    _check(library().kvq_encode(plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam), _lam_args(lam, H, plan.D),
+                                _ptr(codes), _ptr(scales), Tcap, t0, _stream(x)))
+
+
+def decode(plan: Plan, codes, scales, lam, y, t0: int = 0):
+    """Dequantize tokens t0..t0+T-1 into y [B, H, T, D] (fp16 or fp32)."""
+    import torch
+    assert codes.is_contiguous() and scales.is_contiguous() and lam.is_contiguous()
+    B, H, Tcap = codes.shape[0], codes.shape[1], codes.shape[2]
+    assert y.dim() == 4 and y.shape[:2] == (B, H) and y.shape[3] == plan.D and y.stride(3) == 1
+    dt = {torch.float16: _F16, torch.float32: _F32}[y.dtype]
+    _check(library().kvq_decode(plan.handle, _ptr(codes), _ptr(scales), B, H, Tcap, t0, y.shape[2],
+                                _ptr(lam), _lam_args(lam, H, plan.D), _ptr(y), dt,
+                                y.stride(0), y.stride(1), y.stride(2), _stream(y)))
+
+
+def rotate(plan: Plan, x, lam, w):
+    """w [B, H, T, D] fp32 = lambda * (R x) (the encoder's transform alone)."""
+    B, H, T, sb, sh, st = _x_args(x, plan.D)
+    assert w.is_contiguous() and tuple(w.shape) == (B, H, T, plan.D)
+    _check(library().kvq_rotate(plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam),
+                                _lam_args(lam, H, plan.D), _ptr(w), _stream(x)))
+
+
+def attn_workspace_size(D: int, B: int, Hq: int, seq_len: int) -> int:
+    n = _sz()
+    _check(library().kvq_attn_workspace_size(D, B, Hq, seq_len, ctypes.byref(n)))
+    return n.value
+
+
+def attn_decode(plan: Plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, seq_len: int,
+                sm_scale: float, out, workspace):
+    """Decode-step attention over the int4 cache: out [B, Hq, D]."""
+    import torch
+    B, Hq, D = q.shape
+    Hkv, Tcap = k_codes.shape[1], k_codes.shape[2]
+    for t in (q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out, workspace):
+        assert t.is_contiguous()
+    dt = {torch.float16: _F16, torch.float32: _F32}[out.dtype]
+    _check(library().kvq_attn_decode(plan.handle, _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(lam_k),
+                                     _ptr(v_codes), _ptr(v_scales), _ptr(lam_v), B, Hq, Hkv, Tcap, seq_len,
+                                     float(sm_scale), _ptr(out), dt, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(q)))
+
+
+def attn_decode_f16(q, k, v, seq_len: int, sm_scale: float, out, workspace):
+    """The same attention over an fp16 cache k, v [B, Hkv, Tcap, D]."""
+    import torch
+    B, Hq, D = q.shape
+    Hkv, Tcap = k.shape[1], k.shape[2]
+    for t in (q, k, v, out, workspace):
+        assert t.is_contiguous()
+    dt = {torch.float16: _F16, torch.float32: _F32}[out.dtype]
+    _check(library().kvq_attn_decode_f16(D, _ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Tcap, seq_len,
+                                         float(sm_scale), _ptr(out), dt, _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(q)))

@@ -1,0 +1,560 @@
+// Encode / rotate / decode kernels of the int4 KV-cache codec (gfx950).
+//
+// Work decomposition.  A wave owns a tile of 16 KiB of fp16 input: 64 head
+// vectors of D=128 (one per lane) or 32 vectors of D=256 (two lanes each).
+// Tiles never cross a (batch, head) row, so the lambda row is wave-uniform.
+// Waves are persistent: each walks the tiles with a stride of the grid; two
+// waves share every SIMD, so one streams its tile in while the other
+// computes.
+//
+// Data movement per tile (encode):
+//   HBM --(coalesced 16-byte loads: 16 consecutive lanes read one 256-byte
+//   row)--> VGPRs --(sign xor, ds_write into a per-lane LDS block with an
+//   XOR swizzle)--> LDS --(each lane reads its own 256-byte block)--> VGPRs
+//   --(fp32 transform, lambda, group abs-max, int4, nibble pack)--> LDS
+//   --(coalesced 16-byte stores)--> HBM codes; scales go straight out with
+//   one 8-byte store per lane.
+// The random signs are applied to the fp16 words in the coalesced layout,
+// where every lane always holds the same 16-byte column of a row, so each
+// lane's four sign masks are fixed for the whole kernel.
+//
+// Decode runs the same path backwards; the fp16 output leaves through the
+// same swizzled LDS blocks and coalesced stores.
+//
+// Method (gist.science explainer of "When Quantization Is Free",
+// "Methodik" 1-2): sign -> FFT over the D/2 complex pairs -> pack ->
+// lambda -> per-group abs-max -> int4 -> two nibbles per byte.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_device.hpp"
+#include "kvq_internal.hpp"
+
+namespace kvq {
+
+namespace {
+
+// One plan-independent description of a codec launch.
+struct CodecArgs {
+  const uint16_t* x;          // encode / rotate input, fp16
+  const uint8_t* codes_in;    // decode input
+  const uint16_t* scales_in;
+  uint8_t* codes;             // encode output
+  uint16_t* scales;
+  void* y;                    // decode output (fp16 or fp32)
+  float* w;                   // rotate output
+  const float* lambda;
+  int64_t H, T, Tcap, t0;
+  int64_t sb, sh, st;         // strides of x (encode, rotate) or y (decode)
+  int64_t lambda_sb;
+  int64_t tiles_per_row, n_tiles;
+  uint64_t signs[4];
+};
+
+template <int D>
+struct Geo {
+  static constexpr int L = D / 128;            // lanes per vector
+  static constexpr int VPT = 64 / L;           // vectors per tile
+  static constexpr int CPR = D / 8;            // 16-byte chunks per fp16 row
+  static constexpr int RPI = 64 / CPR;         // rows per 64-lane load
+  static constexpr int NLD = VPT * CPR / 64;   // loads per lane per tile (16)
+};
+
+// Unitary scale of the rotation, folded into per-group constants.
+template <int D, int ROT>
+__host__ __device__ constexpr float rot_scale() {
+  return ROT == KVQ_ROT_SRFT ? (D == 128 ? 0.125f : 0.0883883476483184405f)
+       : ROT == KVQ_ROT_SRHT ? (D == 128 ? 0.0883883476483184405f : 0.0625f)
+       : 1.0f;
+}
+
+__device__ __forceinline__ uint32_t sign_bit(const uint64_t (&s)[4], int i) {
+  const uint64_t w = i < 64 ? s[0] : i < 128 ? s[1] : i < 192 ? s[2] : s[3];
+  return static_cast<uint32_t>(w >> (i & 63)) & 1u;
+}
+
+// XOR mask for fp16 pair word k (channels 2k, 2k+1) of a row: the random
+// signs, plus a negation of the data the second lane of a D=256 vector owns
+// (it lets the cross-lane radix-2 step use one fused multiply-add).
+template <int D, int ROT>
+__device__ __forceinline__ uint32_t word_mask(const uint64_t (&s)[4], int k) {
+  uint32_t m = 0;
+  if (ROT == KVQ_ROT_SRFT) {
+    m = sign_bit(s, k) ? 0x80008000u : 0u;
+    if (D == 256 && (k & 1)) m ^= 0x80008000u;
+  } else if (ROT == KVQ_ROT_SRHT) {
+    m = (sign_bit(s, 2 * k) << 15) | (sign_bit(s, 2 * k + 1) << 31);
+    if (D == 256 && k >= 64) m ^= 0x80008000u;
+  }
+  return m;
+}
+
+// LDS byte offset of 16-byte chunk j of the 256-byte block owned by lane
+// `blk`: the chunk index is XOR-swizzled with the block so that a lane-
+// parallel read of chunk j by 16 consecutive lanes hits 16 distinct bank
+// groups.
+__device__ __forceinline__ uint32_t blk_off(int blk, int j) {
+  return static_cast<uint32_t>(blk * 256 + ((j ^ (blk & 15)) << 4));
+}
+
+// LDS byte offset of 16-byte chunk q of the 64-byte code row of lane r.
+__device__ __forceinline__ uint32_t code_off(int r, int q) {
+  return static_cast<uint32_t>(r * 64 + ((q ^ ((r >> 2) & 3)) << 4));
+}
+
+struct Tile {
+  int64_t row;      // b * H + h
+  int64_t b, h;
+  int64_t t_start;
+  int nv;           // valid vectors in the tile
+};
+
+template <int D>
+__device__ __forceinline__ Tile tile_info(const CodecArgs& a, int64_t tile) {
+  Tile t;
+  t.row = tile / a.tiles_per_row;
+  t.t_start = (tile - t.row * a.tiles_per_row) * Geo<D>::VPT;
+  t.b = t.row / a.H;
+  t.h = t.row - t.b * a.H;
+  const int64_t left = a.T - t.t_start;
+  t.nv = static_cast<int>(left < Geo<D>::VPT ? left : Geo<D>::VPT);
+  return t;
+}
+
+// Coalesced fp16 row loads of one tile into registers.
+template <int D>
+__device__ __forceinline__ void load_rows(const CodecArgs& a, const Tile& t, int lane,
+                                          uint4 (&buf)[Geo<D>::NLD]) {
+  using G = Geo<D>;
+  const int c = lane % G::CPR;
+  const int r0 = lane / G::CPR;
+  const uint16_t* base = a.x + t.b * a.sb + t.h * a.sh + (t.t_start + r0) * a.st + c * 8;
+#pragma unroll
+  for (int i = 0; i < G::NLD; ++i) {
+    const int v = i * G::RPI + r0;
+    if (v < t.nv) {
+      buf[i] = ld_stream16(base + static_cast<int64_t>(i * G::RPI) * a.st);
+    } else {
+      buf[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Sign-xor the staged words and scatter them into the per-lane LDS blocks.
+template <int D, int ROT>
+__device__ __forceinline__ void stage_rows(uint8_t* lds, int lane, const uint4 (&buf)[Geo<D>::NLD],
+                                           const uint4& mask) {
+  using G = Geo<D>;
+  const int c = lane % G::CPR;
+  const int r0 = lane / G::CPR;
+#pragma unroll
+  for (int i = 0; i < G::NLD; ++i) {
+    const int v = i * G::RPI + r0;
+    uint4 w = buf[i];
+    w.x ^= mask.x; w.y ^= mask.y; w.z ^= mask.z; w.w ^= mask.w;
+    if (D == 128) {
+      *reinterpret_cast<uint4*>(lds + blk_off(v, c)) = w;
+    } else if (ROT != KVQ_ROT_SRFT) {
+      *reinterpret_cast<uint4*>(lds + blk_off(2 * v + (c >> 4), c & 15)) = w;
+    } else {
+      // even pairs to lane 2v, odd pairs to lane 2v+1
+      const uint32_t off = (c & 1) * 8;
+      *reinterpret_cast<uint2*>(lds + blk_off(2 * v, c >> 1) + off) = make_uint2(w.x, w.z);
+      *reinterpret_cast<uint2*>(lds + blk_off(2 * v + 1, c >> 1) + off) = make_uint2(w.y, w.w);
+    }
+  }
+}
+
+// Each lane reads its own block and widens the 64 fp16 pairs to fp32.
+__device__ __forceinline__ void read_block(const uint8_t* lds, int lane, float (&v)[128]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint4 w = *reinterpret_cast<const uint4*>(lds + blk_off(lane, j));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * j + 2 * e] = f16_bits_to_f32(ws[e] & 0xFFFFu);
+      v[8 * j + 2 * e + 1] = f16_bits_to_f32(ws[e] >> 16);
+    }
+  }
+}
+
+// Forward rotation of the lane's 128 values (unnormalized; the scale
+// rot_scale<D, ROT>() is applied by the caller).
+template <int D, int ROT>
+__device__ __forceinline__ void forward_rotation(float (&v)[128], int lane) {
+  if (ROT == KVQ_ROT_SRFT) {
+    fft64<false>(v);
+    if (D == 256) {
+      // radix-2 decimation in time across the lane pair: lane 2v holds the
+      // transform E of the even pairs, lane 2v+1 the (negated) transform O
+      // of the odd pairs; Z_m = E_m + W^m O_m, Z_{m+64} = E_m - W^m O_m.
+      if (lane & 1) {
+#pragma unroll
+        for (int m = 0; m < 64; ++m) twiddle<128, false>(v[2 * rev4(m)], v[2 * rev4(m) + 1], m);
+      }
+      const float sg = (lane & 1) ? 1.f : -1.f;
+#pragma unroll
+      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sg);
+    }
+  } else if (ROT == KVQ_ROT_SRHT) {
+    wht128(v);
+    if (D == 256) {
+      // H_256 [u; v] = [H u + H v; H u - H v]; the second lane holds -H v.
+      const float sg = (lane & 1) ? 1.f : -1.f;
+#pragma unroll
+      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sg);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Encode (MODE 0) and rotate (MODE 1)
+// ---------------------------------------------------------------------------
+template <int D, int ROT, int MODE>
+__global__ void __launch_bounds__(64, 2) encode_kernel(CodecArgs a) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[16384];
+  const int lane = threadIdx.x;
+  constexpr float kScale = rot_scale<D, ROT>();
+
+  // this lane's sign masks: it always stages column c of a row, i.e. the
+  // pair words 4c .. 4c+3
+  const int col = lane % G::CPR;
+  const uint4 mask = make_uint4(word_mask<D, ROT>(a.signs, 4 * col), word_mask<D, ROT>(a.signs, 4 * col + 1),
+                                word_mask<D, ROT>(a.signs, 4 * col + 2), word_mask<D, ROT>(a.signs, 4 * col + 3));
+
+  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    const Tile t = tile_info<D>(a, tile);
+    float v[128];
+    {
+      uint4 buf[G::NLD];
+      load_rows<D>(a, t, lane, buf);
+      stage_rows<D, ROT>(lds, lane, buf, mask);
+    }
+    __syncthreads();
+    read_block(lds, lane, v);
+    __syncthreads();
+
+    forward_rotation<D, ROT>(v, lane);
+
+    const int half = (D == 256) ? (lane & 1) : 0;
+    const float* lam = a.lambda + t.b * a.lambda_sb + t.h * D + half * 128;
+    const int vec = lane / G::L;           // vector index inside the tile
+    const bool valid = vec < t.nv;
+
+    if (MODE == 1) {
+      float* wr = a.w + ((t.row * a.T) + t.t_start + vec) * D + half * 128;
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < 128; j += 4) {
+          float4 o;
+          o.x = v[chan_reg<ROT>(j)] * lam[j] * kScale;
+          o.y = v[chan_reg<ROT>(j + 1)] * lam[j + 1] * kScale;
+          o.z = v[chan_reg<ROT>(j + 2)] * lam[j + 2] * kScale;
+          o.w = v[chan_reg<ROT>(j + 3)] * lam[j + 3] * kScale;
+          *reinterpret_cast<float4*>(wr + j) = o;
+        }
+      }
+    } else {
+      uint32_t cw[16];
+      uint32_t sc[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float amax = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) {
+          const int j = 32 * g + jj;
+          const float wv = v[chan_reg<ROT>(j)] * lam[j];
+          v[chan_reg<ROT>(j)] = wv;
+          amax = fmaxf(amax, fabsf(wv));
+        }
+        // scale = fp16(absmax / 7): the float32 quotient, rounded to nearest
+        // even once more to fp16
+        const float amax_true = amax * kScale;
+        const uint32_t s16 = f32_to_f16_bits(amax_true / 7.0f);
+        sc[g] = s16;
+        const float sf = f16_bits_to_f32(s16);
+        const float r = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t by[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 32 * g + 8 * q + 2 * e;
+            by[e] = pair_byte(quant_bits(v[chan_reg<ROT>(j)], r), quant_bits(v[chan_reg<ROT>(j + 1)], r));
+          }
+          cw[4 * g + q] = pack4(by[0], by[1], by[2], by[3]);
+        }
+      }
+
+      // scales: 8 bytes per lane, contiguous across the tile
+      const int64_t cell = (t.row * a.Tcap + a.t0 + t.t_start);
+      if (valid) {
+        uint2 s2 = make_uint2(sc[0] | (sc[1] << 16), sc[2] | (sc[3] << 16));
+        *reinterpret_cast<uint2*>(a.scales + cell * (D / 32) + lane * 4) = s2;
+      }
+      // codes: through LDS to coalesced 16-byte stores
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<uint4*>(lds + code_off(lane, q)) =
+            make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+      }
+      __syncthreads();
+      uint8_t* cbase = a.codes + cell * (D / 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = i * 64 + lane;
+        const int r = s >> 2;
+        const int q = (s & 3) ^ ((r >> 2) & 3);
+        const uint4 o = *reinterpret_cast<const uint4*>(lds + s * 16);
+        if (r / G::L < t.nv) *reinterpret_cast<uint4*>(cbase + r * 64 + q * 16) = o;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode
+// ---------------------------------------------------------------------------
+template <int D, int ROT, int OUT_F32>
+__global__ void __launch_bounds__(64, 2) decode_kernel(CodecArgs a) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[16384];
+  const int lane = threadIdx.x;
+  constexpr float kScale = rot_scale<D, ROT>();
+  const int col = lane % G::CPR;
+  const uint4 mask = make_uint4(word_mask<D, ROT>(a.signs, 4 * col), word_mask<D, ROT>(a.signs, 4 * col + 1),
+                                word_mask<D, ROT>(a.signs, 4 * col + 2), word_mask<D, ROT>(a.signs, 4 * col + 3));
+
+  auto load_codes = [&](const Tile& tt, uint4 (&cb)[4], uint2& sbuf) {
+    const int64_t cell = tt.row * a.Tcap + a.t0 + tt.t_start;
+    const uint8_t* cbase = a.codes_in + cell * (D / 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = i * 64 + lane;
+      const int r = s >> 2;
+      cb[i] = (r / G::L < tt.nv) ? ld_stream16(cbase + s * 16)
+                                 : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+    }
+    sbuf = (lane / G::L < tt.nv)
+               ? *reinterpret_cast<const uint2*>(a.scales_in + cell * (D / 32) + lane * 4)
+               : make_uint2(0, 0);
+  };
+
+  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    const Tile t = tile_info<D>(a, tile);
+    uint4 cb[4];
+    uint2 sbuf;
+    load_codes(t, cb, sbuf);
+    // stage the code rows: slot s holds chunk (s & 3) of lane (s >> 2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = i * 64 + lane;
+      *reinterpret_cast<uint4*>(lds + code_off(s >> 2, s & 3)) = cb[i];
+    }
+    __syncthreads();
+    uint32_t cw[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = *reinterpret_cast<const uint4*>(lds + code_off(lane, q));
+      cw[4 * q] = w.x; cw[4 * q + 1] = w.y; cw[4 * q + 2] = w.z; cw[4 * q + 3] = w.w;
+    }
+    const uint32_t s16[4] = {sbuf.x & 0xFFFFu, sbuf.x >> 16, sbuf.y & 0xFFFFu, sbuf.y >> 16};
+    __syncthreads();
+
+    const int half = (D == 256) ? (lane & 1) : 0;
+    const float* lam = a.lambda + t.b * a.lambda_sb + t.h * D + half * 128;
+    float v[128];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float sg = f16_bits_to_f32(s16[g]);
+      const float m8 = -8.f * sg;
+#pragma unroll
+      for (int jj = 0; jj < 32; ++jj) {
+        const int j = 32 * g + jj;
+        const uint32_t nib = (cw[j >> 3] >> (4 * (j & 7))) & 15u;
+        // (n - 8) * scale exactly, then divide by lambda (times the unitary
+        // scale of the inverse rotation)
+        const float qs = fmaf(static_cast<float>(nib), sg, m8);
+        v[j] = qs * (kScale * __builtin_amdgcn_rcpf(lam[j]));
+      }
+    }
+
+    // inverse rotation
+    if (ROT == KVQ_ROT_SRFT) {
+      if (D == 256) {
+        // lane 2v: A_m = Z_m + Z_{m+64}; lane 2v+1: -(Z_m - Z_{m+64}) W^-m
+        const float sgn = (lane & 1) ? -1.f : 1.f;
+#pragma unroll
+        for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+        if (lane & 1) {
+#pragma unroll
+          for (int m = 0; m < 64; ++m) twiddle<128, true>(v[2 * m], v[2 * m + 1], m);
+        }
+      }
+      fft64<true>(v);
+    } else if (ROT == KVQ_ROT_SRHT) {
+      if (D == 256) {
+        const float sgn = (lane & 1) ? -1.f : 1.f;
+#pragma unroll
+        for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+      }
+      wht128(v);
+    }
+
+    const int vec = lane / G::L;
+    if (!OUT_F32) {
+      // fp16 words of the lane's 64 pairs, through LDS to coalesced stores
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 4 * j + e;
+          const int p = ROT == KVQ_ROT_SRFT ? rev4(k) : k;
+          wv[e] = pack_f16x2(v[2 * p], v[2 * p + 1]);
+        }
+        *reinterpret_cast<uint4*>(lds + blk_off(lane, j)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
+      __syncthreads();
+      uint16_t* yb = static_cast<uint16_t*>(a.y);
+      const int c = lane % G::CPR;
+      const int r0 = lane / G::CPR;
+#pragma unroll
+      for (int i = 0; i < G::NLD; ++i) {
+        const int vv = i * G::RPI + r0;
+        uint4 w;
+        if (D == 128) {
+          w = *reinterpret_cast<const uint4*>(lds + blk_off(vv, c));
+        } else if (ROT != KVQ_ROT_SRFT) {
+          w = *reinterpret_cast<const uint4*>(lds + blk_off(2 * vv + (c >> 4), c & 15));
+        } else {
+          const uint32_t off = (c & 1) * 8;
+          const uint2 e = *reinterpret_cast<const uint2*>(lds + blk_off(2 * vv, c >> 1) + off);
+          const uint2 o = *reinterpret_cast<const uint2*>(lds + blk_off(2 * vv + 1, c >> 1) + off);
+          w = make_uint4(e.x, o.x, e.y, o.y);
+        }
+        w.x ^= mask.x; w.y ^= mask.y; w.z ^= mask.z; w.w ^= mask.w;
+        if (vv < t.nv) {
+          uint16_t* dst = yb + t.b * a.sb + t.h * a.sh + (t.t_start + vv) * a.st + c * 8;
+          st_stream16(dst, w);
+        }
+      }
+    } else if (vec < t.nv) {
+      // fp32 parity output: each lane writes its own channels
+      float* yr = static_cast<float*>(a.y) + t.b * a.sb + t.h * a.sh + (t.t_start + vec) * a.st;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) {
+        const int p = ROT == KVQ_ROT_SRFT ? rev4(k) : k;
+        int kg, ch;   // global pair index and its first channel
+        if (D == 128) { kg = k; ch = 2 * k; }
+        else if (ROT == KVQ_ROT_SRFT) { kg = 2 * k + (lane & 1); ch = 2 * kg; }
+        else { kg = 64 * (lane & 1) + k; ch = 2 * kg; }
+        const uint32_t m = word_mask<D, ROT>(a.signs, kg);
+        const float lo = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[2 * p]) ^ ((m & 0x8000u) << 16));
+        const float hi = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[2 * p + 1]) ^ (m & 0x80000000u));
+        *reinterpret_cast<float2*>(yr + ch) = make_float2(lo, hi);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+// Persistent grid: enough waves to give every CU eight (two per SIMD), spread
+// so that every wave gets the same number of tiles.
+int64_t persistent_grid(int64_t n_tiles) {
+  const int64_t slots = static_cast<int64_t>(device_cu_count()) * 8;
+  if (n_tiles <= slots) return n_tiles;
+  const int64_t rounds = (n_tiles + slots - 1) / slots;
+  return (n_tiles + rounds - 1) / rounds;
+}
+
+template <int D>
+void fill_common(CodecArgs& a, const CodecDesc& d) {
+  a.H = d.H;
+  a.T = d.T;
+  a.Tcap = d.Tcap;
+  a.t0 = d.t0;
+  a.sb = d.sb;
+  a.sh = d.sh;
+  a.st = d.st;
+  a.lambda = d.lambda;
+  a.lambda_sb = d.lambda_sb;
+  a.tiles_per_row = (d.T + Geo<D>::VPT - 1) / Geo<D>::VPT;
+  a.n_tiles = d.B * d.H * a.tiles_per_row;
+  for (int i = 0; i < 4; ++i) a.signs[i] = d.signs[i];
+}
+
+template <int D, int ROT>
+hipError_t encode_dispatch(const CodecDesc& d, int mode) {
+  CodecArgs a{};
+  fill_common<D>(a, d);
+  a.x = d.x;
+  a.codes = d.codes;
+  a.scales = d.scales;
+  a.w = d.w;
+  if (a.n_tiles == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
+  if (mode == 0) {
+    hipLaunchKernelGGL((encode_kernel<D, ROT, 0>), grid, dim3(64), 0, d.stream, a);
+  } else {
+    hipLaunchKernelGGL((encode_kernel<D, ROT, 1>), grid, dim3(64), 0, d.stream, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int ROT>
+hipError_t decode_dispatch(const CodecDesc& d, bool f32) {
+  CodecArgs a{};
+  fill_common<D>(a, d);
+  a.codes_in = d.codes_in;
+  a.scales_in = d.scales_in;
+  a.y = d.y;
+  if (a.n_tiles == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
+  if (f32) {
+    hipLaunchKernelGGL((decode_kernel<D, ROT, 1>), grid, dim3(64), 0, d.stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<D, ROT, 0>), grid, dim3(64), 0, d.stream, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t encode_rot(const CodecDesc& d, int mode) {
+  switch (d.rotation) {
+    case KVQ_ROT_SRFT: return encode_dispatch<D, KVQ_ROT_SRFT>(d, mode);
+    case KVQ_ROT_SRHT: return encode_dispatch<D, KVQ_ROT_SRHT>(d, mode);
+    default: return encode_dispatch<D, KVQ_ROT_ID>(d, mode);
+  }
+}
+
+template <int D>
+hipError_t decode_rot(const CodecDesc& d, bool f32) {
+  switch (d.rotation) {
+    case KVQ_ROT_SRFT: return decode_dispatch<D, KVQ_ROT_SRFT>(d, f32);
+    case KVQ_ROT_SRHT: return decode_dispatch<D, KVQ_ROT_SRHT>(d, f32);
+    default: return decode_dispatch<D, KVQ_ROT_ID>(d, f32);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_encode(const CodecDesc& d, int mode) {
+  return d.D == 128 ? encode_rot<128>(d, mode) : encode_rot<256>(d, mode);
+}
+
+hipError_t launch_decode(const CodecDesc& d, bool f32) {
+  return d.D == 128 ? decode_rot<128>(d, f32) : decode_rot<256>(d, f32);
+}
+
+}  // namespace kvq

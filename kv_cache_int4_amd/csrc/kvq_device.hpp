@@ -1,0 +1,244 @@
+// Device primitives of the int4 KV-cache codec for CDNA4 (gfx950).
+//
+// One lane owns 128 real values: a whole D=128 head vector, or one half of a
+// D=256 vector (the two halves live in adjacent lanes 2v and 2v+1).  The
+// transforms run entirely in VGPRs with compile-time indices, so every
+// twiddle factor is an instruction literal and nothing touches scratch.
+//
+// Method (paper "When Quantization Is Free", gist.science explainer,
+// "Methodik" 1-2): SRFT(x) = pack(F diag(s) x) with F the unitary DFT over
+// the D/2 complex pairs; the fused kernel then applies the per-channel
+// lambda, the per-group abs-max and int4 rounding, and packs two codes per
+// byte.  The explainer's kernel runs log2(d/2) radix-2 Stockham passes; here
+// the 64-point transform is three radix-4 decimation-in-frequency stages held
+// in registers (the data never leaves the lane between stages), and the
+// 128-point one adds a radix-2 step across a lane pair.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// ---------------------------------------------------------------------------
+// Compile-time twiddle tables: c[e] = cos(2 pi e / N), s[e] = sin(2 pi e / N)
+// evaluated in double by a Taylor series on [-pi, pi] and rounded once to
+// float; quarter turns are exact.
+// ---------------------------------------------------------------------------
+struct TwTable {
+  float c[128];
+  float s[128];
+};
+
+constexpr double kPi = 3.14159265358979323846264338327950288;
+
+constexpr double taylor_sin(double x) {
+  double t = x, s = x;
+  for (int n = 1; n < 30; ++n) {
+    t *= -x * x / ((2.0 * n) * (2.0 * n + 1.0));
+    s += t;
+  }
+  return s;
+}
+
+constexpr double taylor_cos(double x) {
+  double t = 1.0, s = 1.0;
+  for (int n = 1; n < 30; ++n) {
+    t *= -x * x / ((2.0 * n - 1.0) * (2.0 * n));
+    s += t;
+  }
+  return s;
+}
+
+constexpr TwTable make_twiddles(int N) {
+  TwTable t{};
+  for (int e = 0; e < N; ++e) {
+    double x = 2.0 * kPi * e / N;
+    if (x > kPi) x -= 2.0 * kPi;
+    t.c[e] = static_cast<float>(taylor_cos(x));
+    t.s[e] = static_cast<float>(taylor_sin(x));
+    if ((4 * e) % N == 0) {
+      const int q = (4 * e) / N;
+      t.c[e] = q == 0 ? 1.f : (q == 2 ? -1.f : 0.f);
+      t.s[e] = q == 1 ? 1.f : (q == 3 ? -1.f : 0.f);
+    }
+  }
+  return t;
+}
+
+constexpr TwTable kTw128 = make_twiddles(128);
+
+// (re + i im) *= exp(-+ 2 pi i e / N): INV = false takes the forward kernel
+// exp(-2 pi i e / N), INV = true its conjugate.  N divides 128.
+template <int N, bool INV>
+__device__ __forceinline__ void twiddle(float& re, float& im, int e) {
+  e %= N;
+  if (e == 0) return;
+  if (2 * e == N) {
+    re = -re;
+    im = -im;
+    return;
+  }
+  const bool minus_i = (4 * e == N) != INV;     // multiply by -i
+  if (4 * e == N || 4 * e == 3 * N) {
+    const float t = re;
+    if (minus_i) { re = im; im = -t; }
+    else         { re = -im; im = t; }
+    return;
+  }
+  const float c = kTw128.c[e * (128 / N)];
+  const float s = INV ? -kTw128.s[e * (128 / N)] : kTw128.s[e * (128 / N)];
+  // (re + i im)(c - i s) = (re c + im s) + i (im c - re s)
+  const float r2 = fmaf(re, c, im * s);
+  const float i2 = fmaf(im, c, -(re * s));
+  re = r2;
+  im = i2;
+}
+
+// Base-4 digit reversal of a 64-point index: where the decimation-in-
+// frequency transform leaves frequency m.
+__host__ __device__ constexpr int rev4(int m) {
+  return 16 * (m & 3) + 4 * ((m >> 2) & 3) + (m >> 4);
+}
+
+// One radix-4 DIF stage over sub-transforms of length L (v holds 64 complex
+// values as v[2p] + i v[2p+1]).
+template <int L, bool INV>
+__device__ __forceinline__ void dif4_stage(float (&v)[128]) {
+  constexpr int Q = L / 4;
+#pragma unroll
+  for (int base = 0; base < 64; base += L) {
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const int i0 = base + j, i1 = i0 + Q, i2 = i0 + 2 * Q, i3 = i0 + 3 * Q;
+      const float t0r = v[2 * i0] + v[2 * i2], t0i = v[2 * i0 + 1] + v[2 * i2 + 1];
+      const float t1r = v[2 * i0] - v[2 * i2], t1i = v[2 * i0 + 1] - v[2 * i2 + 1];
+      const float t2r = v[2 * i1] + v[2 * i3], t2i = v[2 * i1 + 1] + v[2 * i3 + 1];
+      const float t3r = v[2 * i1] - v[2 * i3], t3i = v[2 * i1 + 1] - v[2 * i3 + 1];
+      v[2 * i0] = t0r + t2r;
+      v[2 * i0 + 1] = t0i + t2i;
+      v[2 * i2] = t0r - t2r;
+      v[2 * i2 + 1] = t0i - t2i;
+      if (!INV) {  // y1 = t1 - i t3, y3 = t1 + i t3
+        v[2 * i1] = t1r + t3i;
+        v[2 * i1 + 1] = t1i - t3r;
+        v[2 * i3] = t1r - t3i;
+        v[2 * i3 + 1] = t1i + t3r;
+      } else {     // y1 = t1 + i t3, y3 = t1 - i t3
+        v[2 * i1] = t1r - t3i;
+        v[2 * i1 + 1] = t1i + t3r;
+        v[2 * i3] = t1r + t3i;
+        v[2 * i3 + 1] = t1i - t3r;
+      }
+      twiddle<L, INV>(v[2 * i1], v[2 * i1 + 1], j);
+      twiddle<L, INV>(v[2 * i2], v[2 * i2 + 1], 2 * j);
+      twiddle<L, INV>(v[2 * i3], v[2 * i3 + 1], 3 * j);
+    }
+  }
+}
+
+// Unnormalized 64-point DFT in registers: input in natural order, output
+// frequency m at position rev4(m).  INV selects the conjugate kernel.
+template <bool INV>
+__device__ __forceinline__ void fft64(float (&v)[128]) {
+  dif4_stage<64, INV>(v);
+  dif4_stage<16, INV>(v);
+  dif4_stage<4, INV>(v);
+}
+
+// Unnormalized Walsh-Hadamard transform of 128 reals in Sylvester (natural)
+// order: H_2n = [[H_n, H_n], [H_n, -H_n]] applied as log2(128) butterfly
+// sweeps.
+__device__ __forceinline__ void wht128(float (&v)[128]) {
+#pragma unroll
+  for (int h = 1; h < 128; h *= 2) {
+#pragma unroll
+    for (int i = 0; i < 128; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+}
+
+// Register holding local channel j (0..127) after the forward transform.
+template <int ROT>
+__host__ __device__ constexpr int chan_reg(int j) {
+  return ROT == 0 ? 2 * rev4(j >> 1) + (j & 1) : j;
+}
+
+// v += sign * (the same register of the partner lane l ^ 1), for every
+// register: the radix-2 step between the two halves of a D=256 vector.
+__device__ __forceinline__ float pair_fma(float own, float sign) {
+  // quad_perm [1,0,3,2]: read the partner lane of each pair
+  const float other = __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, own), 0xB1, 0xF, 0xF, false));
+  return fmaf(other, sign, own);
+}
+
+// Streaming 16-byte global load / store (touched once: nontemporal hint).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void st_stream16(void* p, const uint4& w) {
+  const u32x4_t v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, static_cast<u32x4_t*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Quantizer helpers
+// ---------------------------------------------------------------------------
+
+// fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 under the default
+// rounding mode).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
+// Two fp32 -> one word of two fp16 (round to nearest even), low half first
+// (one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 h = __builtin_convertvector((f2){lo, hi}, h2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// 1.5 * 2^23 + 8: adding it to w*r leaves rint_even(w*r) + 8 in the low
+// mantissa bits (valid while |w*r| < 2^22; larger values are clamped by the
+// integer clamp below).
+constexpr float kMagic = 12582920.0f;
+constexpr int kMagicLo = 0x4B400000;   // bits of 1.5 * 2^23     (code -8)
+constexpr int kMagicHi = 0x4B40000F;   // bits of 1.5 * 2^23 + 15 (code  7)
+
+// Offset nibble of clamp(rint_even(w * r), -8, 7) in the low 4 bits; the
+// upper bits hold the constant 0x4B40000 pattern.
+__device__ __forceinline__ uint32_t quant_bits(float w, float r) {
+  const int b = __builtin_bit_cast(int, fmaf(w, r, kMagic));
+  return static_cast<uint32_t>(min(max(b, kMagicLo), kMagicHi));
+}
+
+// Byte of a channel pair: even channel in the low nibble.
+__device__ __forceinline__ uint32_t pair_byte(uint32_t lo_bits, uint32_t hi_bits) {
+  return lo_bits + (hi_bits << 4);   // low byte = n_even + 16 n_odd, no carry
+}
+
+// Four pair bytes (each in the low byte of its argument) -> one code word.
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+}  // namespace kvq

@@ -1,0 +1,66 @@
+// Internal interface between the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq {
+
+enum { KVQ_ROT_SRFT = 0, KVQ_ROT_SRHT = 1, KVQ_ROT_ID = 2 };
+
+// A validated codec call (encode, rotate or decode).
+struct CodecDesc {
+  int D;
+  int rotation;
+  uint64_t signs[4];          // sign bits, bit i of word i / 64
+  const uint16_t* x;          // encode / rotate input
+  const uint8_t* codes_in;    // decode input
+  const uint16_t* scales_in;
+  uint8_t* codes;             // encode output
+  uint16_t* scales;
+  float* w;                   // rotate output
+  void* y;                    // decode output
+  const float* lambda;
+  int64_t lambda_sb;
+  int64_t B, H, T, Tcap, t0;
+  int64_t sb, sh, st;
+  hipStream_t stream;
+};
+
+// A validated decode-step attention call.
+struct AttnDesc {
+  int D;
+  int rotation;
+  uint64_t signs[4];
+  bool int4;                  // int4 cache (true) or fp16 cache (false)
+  const uint16_t* q;
+  const uint8_t* k_codes;
+  const uint16_t* k_scales;
+  const float* lambda_k;
+  const uint8_t* v_codes;
+  const uint16_t* v_scales;
+  const float* lambda_v;
+  const uint16_t* k16;
+  const uint16_t* v16;
+  int64_t B, Hq, Hkv, Tcap, seq_len;
+  float sm_scale;
+  void* out;
+  bool out_f32;
+  void* workspace;
+  hipStream_t stream;
+};
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// mode 0 = encode (codes + scales), mode 1 = rotate (fp32 w)
+hipError_t launch_encode(const CodecDesc& d, int mode);
+hipError_t launch_decode(const CodecDesc& d, bool f32);
+
+// Split-K geometry of the attention kernels.
+int64_t attn_num_splits(int64_t B, int64_t Hkv, int64_t seq_len);
+size_t attn_workspace_bytes(int D, int64_t B, int64_t Hq, int64_t seq_len);
+hipError_t launch_attention(const AttnDesc& d);
+
+}  // namespace kvq

@@ -31,7 +31,7 @@ import torch
 
 __all__ = [
     "Config", "CONFIGS", "gen", "gaussian_outliers", "channel_spread",
-    "student_t3", "lognormal_lambda", "queries",
+    "student_t3", "lognormal_lambda", "queries", "prefix_inputs", "decode_inputs",
 ]
 
 
@@ -168,3 +168,24 @@ def prefix_inputs(cfg: Config, device="cpu", T: int | None = None):
         xs.append(x)
         lams.append(lognormal_lambda((cfg.H, cfg.D), cfg.lambda_seed, device, 0.3, layer, kv))
     return torch.stack(xs), torch.stack(lams)
+
+
+def decode_inputs(B: int, Hkv: int, Hq: int, Tcap: int, D: int, seed: int, device="cpu"):
+    """Inputs of a decode step: fp16 K and V [B, Hkv, Tcap, D] with the
+    channel-spread law of one layer (per-head channel statistics and outlier
+    channels shared across the batch, independent values per sequence),
+    lambda_K and lambda_V [Hkv, D], and queries q [B, Hq, D]."""
+    out = []
+    for kv in (0, 1):
+        g = gen(device, seed, 0, kv)
+        std = torch.exp(0.5 * _normal((Hkv, D), g, device))
+        keep = _outlier_mask(Hkv, D, n_outliers(D), g, device)
+        std = std * (keep + (1.0 - keep) * 30.0)
+        x = torch.empty((B, Hkv, Tcap, D), device=device, dtype=torch.float16)
+        for b in range(B):          # per sequence, to bound the fp32 temporaries
+            x[b] = (_normal((Hkv, Tcap, D), g, device) * std[:, None, :]).to(torch.float16)
+        out.append(x)
+    lam_k = lognormal_lambda((Hkv, D), seed + 100, device, 0.3, 0, 0)
+    lam_v = lognormal_lambda((Hkv, D), seed + 100, device, 0.3, 0, 1)
+    q = queries(B, Hq, D, seed, device)
+    return out[0], out[1], lam_k, lam_v, q

@@ -1,0 +1,129 @@
+"""Comparison of GPU results with the CPU oracle, by the parity protocol.
+
+Codes and scales must be bit-exact except where the oracle's float64 value
+sits within 1e-4 of a rounding boundary:
+  * a scale may differ only where a/7 lies within 1e-4 (relative) of an fp16
+    rounding midpoint;
+  * a code may differ only where w/scale lies within 1e-4 (in code units) of
+    a half-integer; in a group whose scale differs, the GPU codes are checked
+    against the oracle's w re-quantized with the GPU's scale.
+The mismatch fraction (codes + scales, per element) is reported and must stay
+below 1e-5; on samples too small to resolve 1e-5 at most one boundary
+mismatch is tolerated.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+BOUNDARY = 1e-4
+FRACTION = 1e-5
+
+
+def requantize(w64: np.ndarray, scales16: np.ndarray, G: int = O.GROUP) -> np.ndarray:
+    """Oracle codes of w with the given fp16 scales (the same float32 decision
+    as the oracle's quantizer)."""
+    w32 = np.asarray(w64, dtype=np.float64).astype(np.float32)
+    D = w32.shape[-1]
+    s = np.repeat(np.asarray(scales16, dtype=np.float16).astype(np.float32), G, axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = w32 / s
+    q = np.where(s == 0, np.float32(0), np.clip(np.rint(r), -8, 7))
+    return q.astype(np.int8)
+
+
+def compare_codes(codes_gpu, scales_gpu, x16, lam, rotation, signs, G: int = O.GROUP):
+    """Check GPU codes/scales of vectors x16 [N, D] against the oracle.
+
+    Returns a report dict; raises AssertionError on any mismatch that is not a
+    boundary case or when the mismatch fraction is too large."""
+    codes_ref, scales_ref, w = O.encode(x16, lam, rotation, signs, G)
+    codes_gpu = np.asarray(codes_gpu).reshape(codes_ref.shape)
+    scales_gpu = np.asarray(scales_gpu).reshape(scales_ref.shape)
+    N, D = w.shape[0], w.shape[-1]
+    n_el = N * D
+    sg = scales_gpu.view(np.uint16)
+    sr = scales_ref.view(np.uint16)
+    code_dist_ref, scale_dist = O.boundary_distances(w, scales_ref, G)
+
+    scale_bad = sg != sr
+    n_scale_bad = int(scale_bad.sum())
+    if n_scale_bad:
+        assert np.all(scale_dist[scale_bad] <= BOUNDARY), (
+            f"{n_scale_bad} scale mismatches, max boundary distance {scale_dist[scale_bad].max():.3e}")
+
+    qg = O.unpack_nibbles(codes_gpu)
+    qr = O.unpack_nibbles(codes_ref)
+    # groups with a GPU-specific scale: re-quantize with that scale
+    q_expect = qr.copy()
+    code_dist = code_dist_ref
+    if n_scale_bad:
+        q_alt = requantize(w, scales_gpu, G)
+        bad_full = np.repeat(scale_bad, G, axis=-1)
+        q_expect = np.where(bad_full, q_alt, qr)
+        cd_alt, _ = O.boundary_distances(w, scales_gpu, G)
+        code_dist = np.where(bad_full, cd_alt, code_dist_ref)
+    code_bad = qg != q_expect
+    n_code_bad = int(code_bad.sum())
+    if n_code_bad:
+        assert np.all(code_dist[code_bad] <= BOUNDARY), (
+            f"{n_code_bad} code mismatches, max boundary distance {code_dist[code_bad].max():.3e}")
+    frac = (n_code_bad + n_scale_bad) / max(n_el, 1)
+    if n_el * FRACTION >= 1:
+        assert frac < FRACTION, f"mismatch fraction {frac:.3e} >= {FRACTION}"
+    else:
+        assert n_code_bad + n_scale_bad <= 1, f"{n_code_bad + n_scale_bad} boundary mismatches in {n_el} elements"
+    return {
+        "vectors": N, "elements": n_el,
+        "code_mismatch": n_code_bad, "scale_mismatch": n_scale_bad,
+        "code_mismatch_frac": n_code_bad / max(n_el, 1),
+        "scale_mismatch_frac_per_group": n_scale_bad / max(N * (D // G), 1),
+        "mismatch_frac": frac,
+        "w": w,
+    }
+
+
+def compare_rotation(w_gpu, x16, lam, rotation, signs, rel: float = 1e-5):
+    """Rotated fp32 values: per vector max|w_gpu - w_ref| <= rel * max|w_ref|."""
+    w_ref = O.rotate(x16, lam, rotation, signs)
+    w_gpu = np.asarray(w_gpu, dtype=np.float64).reshape(w_ref.shape)
+    err = np.max(np.abs(w_gpu - w_ref), axis=-1)
+    scale = np.max(np.abs(w_ref), axis=-1)
+    worst = float(np.max(err / np.maximum(scale, 1e-30)))
+    assert np.all(err <= rel * scale), f"rotation relative error {worst:.3e} > {rel}"
+    return worst
+
+
+def ulp16(x: np.ndarray) -> np.ndarray:
+    """Spacing of fp16 numbers at |x| (subnormal spacing near zero)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+def compare_decode(y_gpu, codes, scales, lam, rotation, signs, G: int = O.GROUP, atol: float = 1e-3):
+    """Decoded values of the same codes: fp32 within atol absolute; fp16
+    within half an fp16 ulp of the oracle value plus atol."""
+    ref = O.decode(codes, scales, lam, rotation, signs, G)
+    y = np.asarray(y_gpu)
+    yg = y.astype(np.float64).reshape(ref.shape)
+    err = np.abs(yg - ref)
+    if y.dtype == np.float16:
+        bound = 0.5 * ulp16(ref) + atol
+        assert np.all(err <= bound), f"fp16 decode error {np.max(err - bound):.3e} over bound"
+        not_rne = int(np.sum(y.reshape(ref.shape) != ref.astype(np.float16)))
+        return {"max_err": float(err.max()), "not_rne": not_rne}
+    assert np.all(err <= atol), f"decode max error {err.max():.3e} > {atol}"
+    return {"max_err": float(err.max())}
+
+
+def compare_attention(o_gpu, o_ref, rel: float = 2e-3):
+    """Per (b, h): ||o_gpu - o_ref||_inf <= rel * ||o_ref||_inf."""
+    o = np.asarray(o_gpu, dtype=np.float64).reshape(o_ref.shape)
+    err = np.max(np.abs(o - o_ref), axis=-1)
+    scale = np.max(np.abs(o_ref), axis=-1)
+    worst = float(np.max(err / np.maximum(scale, 1e-30)))
+    assert np.all(err <= rel * scale), f"attention relative error {worst:.3e} > {rel}"
+    return worst

@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library is loaded on the CPU: every symbol the header declares must be
+exported, plans must reproduce the oracle's sign vectors, and every argument
+check must fail on the host, with its documented status and no GPU call
+(nothing here ever reaches a kernel launch).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import kv_cache_int4_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP = range(6)
+A = 0x10000        # a 16-byte aligned fake device address (never dereferenced)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    L = K.library()
+    syms = declared_symbols()
+    assert len(syms) >= 13
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in kvq.h but not exported"
+
+
+def test_library_is_built_for_gfx950():
+    with open(K.library_path(), "rb") as f:
+        blob = f.read()
+    assert b"gfx950" in blob
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("rot", [O.SRFT, O.SRHT, O.IDENTITY])
+@pytest.mark.parametrize("seed", [0, 1, 1004, 2**63 + 12345])
+def test_plan_signs_match_oracle(D, rot, seed):
+    p = K.Plan(D, 32, rot, seed)
+    assert np.array_equal(p.signs(), O.plan_signs(D, rot, seed))
+    assert p.info() == (D, 32, rot)
+
+
+def test_plan_create_rejects():
+    L = K.library()
+    h = ctypes.c_void_p()
+    assert L.kvq_plan_create(100, 32, 0, 0, ctypes.byref(h)) == UNSUPPORTED
+    assert b"D=100" in L.kvq_last_error()
+    assert L.kvq_plan_create(128, 16, 0, 0, ctypes.byref(h)) == UNSUPPORTED
+    assert L.kvq_plan_create(128, 32, 7, 0, ctypes.byref(h)) == INVALID
+    assert L.kvq_plan_create(128, 32, 0, 0, None) == INVALID
+    assert L.kvq_plan_signs(None, None, 0) == INVALID
+    assert L.kvq_strerror(WORKSPACE) == b"workspace missing or too small"
+    L.kvq_plan_destroy(None)
+
+
+def _encode(plan, x=A, B=1, H=2, T=4, sb=1024, sh=512, st=128, lam=A, lsb=0, codes=A, scales=A,
+            Tcap=8, t0=0):
+    return K.library().kvq_encode(plan.handle if plan else None, x, B, H, T, sb, sh, st, lam, lsb,
+                                  codes, scales, Tcap, t0, None)
+
+
+def test_encode_validation():
+    p = K.Plan(128, 32, "srft", 1)
+    assert _encode(None) == INVALID
+    assert _encode(p, Tcap=3) == INVALID                 # t0 + T > Tcap
+    assert _encode(p, t0=5) == INVALID
+    assert _encode(p, B=-1) == INVALID
+    assert _encode(p, x=None) == INVALID
+    assert _encode(p, lam=None) == INVALID
+    assert _encode(p, codes=None) == INVALID
+    assert _encode(p, x=A + 2) == ALIGN
+    assert _encode(p, st=130) == ALIGN                   # rows not 16-byte aligned
+    assert _encode(p, st=-128) == INVALID
+    assert _encode(p, codes=A + 8) == ALIGN
+    assert _encode(p, scales=A + 2) == ALIGN
+    assert _encode(p, lam=A + 1) == ALIGN
+    assert _encode(p, lsb=-1) == INVALID
+    assert _encode(p, B=1 << 40, H=1 << 20) == INVALID  # overflowing shape
+    # zero work is a no-op that touches nothing (NULL pointers allowed)
+    assert _encode(p, T=0, x=None, lam=None, codes=None, scales=None) == OK
+    assert K.library().kvq_last_error() == b""
+
+
+def test_decode_and_rotate_validation():
+    L = K.library()
+    p = K.Plan(256, 32, "srht", 2)
+    h = p.handle
+    # codes, scales, B, H, Tcap, t0, T, lam, lsb, y, dtype, y strides
+    assert L.kvq_decode(h, A, A, 1, 1, 8, 6, 4, A, 0, A, 0, 2048, 2048, 256, None) == INVALID
+    assert L.kvq_decode(h, A, A, 1, 1, 8, 0, 4, A, 0, A, 2, 2048, 2048, 256, None) == INVALID
+    assert L.kvq_decode(h, A, A, 1, 1, 8, 0, 4, A, 0, A + 8, 0, 2048, 2048, 256, None) == ALIGN
+    assert L.kvq_decode(h, A, A, 1, 1, 8, 0, 4, A, 0, A, 0, 2048, 2048, 260, None) == ALIGN
+    assert L.kvq_decode(h, A, A, 1, 1, 8, 0, 4, A, 0, A, 1, 2048, 2048, 257, None) == ALIGN
+    assert L.kvq_decode(h, None, A, 1, 1, 8, 0, 4, A, 0, A, 0, 2048, 2048, 256, None) == INVALID
+    assert L.kvq_decode(h, A, A, 1, 1, 8, 0, 0, A, 0, A, 0, 2048, 2048, 256, None) == OK
+    assert L.kvq_rotate(h, A, 1, 1, 4, 1024, 1024, 256, A, 0, None, None) == INVALID
+    assert L.kvq_rotate(h, A, 1, 1, 4, 1024, 1024, 256, A, 0, A + 4, None) == ALIGN
+    assert L.kvq_rotate(None, A, 1, 1, 4, 1024, 1024, 256, A, 0, A, None) == INVALID
+
+
+def test_attention_validation():
+    L = K.library()
+    p = K.Plan(128, 32, "srft", 3)
+    h = p.handle
+    need = K.attn_workspace_size(128, 64, 8, 32769)
+    assert need > 64 * 8 * 128 * 4
+    args = dict(q=A, kc=A, ks=A, lk=A, vc=A, vs=A, lv=A, B=64, Hq=8, Hkv=2, Tcap=33024, L=32769,
+                sm=0.088, out=A, dt=0, ws=A, wsb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.kvq_attn_decode(h, a["q"], a["kc"], a["ks"], a["lk"], a["vc"], a["vs"], a["lv"], a["B"],
+                                 a["Hq"], a["Hkv"], a["Tcap"], a["L"], a["sm"], a["out"], a["dt"], a["ws"],
+                                 a["wsb"], None)
+
+    assert call(Hq=6, Hkv=4) == INVALID               # Hq % Hkv
+    assert call(L=0) == INVALID
+    assert call(L=40000) == INVALID                   # seq_len > Tcap
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(kc=A + 4) == ALIGN
+    assert call(ks=A + 2) == ALIGN
+    assert call(q=None) == INVALID
+    assert call(vc=None) == INVALID
+    assert call(dt=5) == INVALID
+    assert call(B=0) == OK                            # nothing to do
+    p256 = K.Plan(256, 32, "srft", 3)
+    assert L.kvq_attn_decode(p256.handle, A, A, A, A, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need,
+                             None) == UNSUPPORTED
+    assert L.kvq_attn_decode_f16(256, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need, None) == UNSUPPORTED
+    assert L.kvq_attn_decode_f16(128, A, A, A, 1, 3, 2, 8, 4, 0.1, A, 0, A, need, None) == INVALID
+    assert L.kvq_attn_decode_f16(128, A, None, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need, None) == INVALID
+
+
+def test_workspace_size_monotone():
+    a = K.attn_workspace_size(128, 2, 8, 100)
+    b = K.attn_workspace_size(128, 2, 8, 100000)
+    assert 0 < a < b
+    with pytest.raises(K.KvqError):
+        K.attn_workspace_size(64, 2, 8, 100)

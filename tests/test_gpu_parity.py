@@ -1,0 +1,349 @@
+"""GPU parity: libkvq (through the C ABI) against the CPU oracle on the same
+seeded inputs.
+
+Bars (per spec tolerances): rotated fp32 within 1e-5 relative per
+vector; codes and scales bit-exact except within 1e-4 of a rounding boundary
+with the mismatch fraction below 1e-5; decoded values within 1e-3 absolute
+(fp32) or half an fp16 ulp plus 1e-3 (fp16); attention within 2e-3 relative
+per (batch, head).  Output buffers carry canary bytes around the written
+region to catch stray writes.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import kv_cache_int4_amd as K
+from kv_cache_int4_amd import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+ROTS = {"srft": O.SRFT, "srht": O.SRHT, "identity": O.IDENTITY}
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    K.library()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def np16(t):
+    return t.detach().cpu().numpy()
+
+
+def lam_per_vector(lam, B, H, T):
+    """lambda [B,H,D] or [H,D] -> [B*H*T, D] for the oracle."""
+    l = lam.detach().cpu().numpy().astype(np.float32)
+    if l.ndim == 2:
+        l = np.broadcast_to(l[None], (B,) + l.shape)
+    return np.repeat(l[:, :, None, :], T, axis=2).reshape(-1, l.shape[-1])
+
+
+def gpu_encode(plan, x, lam, Tcap=None, t0=0):
+    """Encode on the GPU into a cache pre-filled with canary values; return
+    the device buffers and the written slice, and assert that every token
+    outside [t0, t0 + T) still holds its canary."""
+    B, H, T, D = x.shape
+    Tcap = T + t0 if Tcap is None else Tcap
+    codes = torch.full((B, H, Tcap, D // 2), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((B, H, Tcap, D // 32), 1234.0, dtype=torch.float16, device="cuda")
+    K.encode(plan, x, lam, codes, scales, t0)
+    torch.cuda.synchronize()
+    c, s = codes.cpu(), scales.cpu()
+    if t0 > 0:
+        assert bool((c[:, :, :t0] == 0x5A).all()) and bool((s[:, :, :t0] == 1234.0).all())
+    if t0 + T < Tcap:
+        assert bool((c[:, :, t0 + T:] == 0x5A).all()) and bool((s[:, :, t0 + T:] == 1234.0).all())
+    return codes, scales, c[:, :, t0:t0 + T].numpy(), s[:, :, t0:t0 + T].numpy()
+
+
+def check_encode(name, plan, rot, x, lam, Tcap=None, t0=0):
+    B, H, T, D = x.shape
+    say(f"[encode] {name} D={D} rot={rot} B={B} H={H} T={T} t0={t0}")
+    xd = x.cuda() if not x.is_cuda else x
+    codes_d, scales_d, c, s = gpu_encode(plan, xd, lam.cuda(), Tcap, t0)
+    signs = O.plan_signs(D, ROTS[rot], plan.seed)
+    xs = np16(x).reshape(-1, D)
+    lv = lam_per_vector(lam, B, H, T)
+    rep = P.compare_codes(c.reshape(-1, D // 2), s.reshape(-1, D // 32), xs, lv, ROTS[rot], signs)
+    say(f"   codes ok: code mismatches {rep['code_mismatch']}, scale mismatches {rep['scale_mismatch']}, "
+        f"fraction {rep['mismatch_frac']:.2e}")
+    return codes_d, scales_d, c, s, rep
+
+
+# ----------------------------------------------------------------- encode --
+
+@pytest.mark.parametrize("rot", ["srft", "srht", "identity"])
+def test_small_roundtrip_all_rotations(rot):
+    cfg = W.CONFIGS["small"]
+    x, lam = W.prefix_inputs(cfg)
+    plan = K.Plan(cfg.D, 32, rot, cfg.sign_seed)
+    codes_d, scales_d, c, s, rep = check_encode("small", plan, rot, x, lam)
+    signs = O.plan_signs(cfg.D, ROTS[rot], plan.seed)
+    B, H, T, D = x.shape
+    lv = lam_per_vector(lam, B, H, T)
+    # rotation alone
+    w = torch.empty((B, H, T, D), dtype=torch.float32, device="cuda")
+    K.rotate(plan, x.cuda(), lam.cuda(), w)
+    worst = P.compare_rotation(np16(w).reshape(-1, D), np16(x).reshape(-1, D), lv, ROTS[rot], signs)
+    say(f"   rotation rel err {worst:.2e}")
+    # decode fp32 and fp16 of the same codes
+    for dt in (torch.float32, torch.float16):
+        y = torch.empty((B, H, T, D), dtype=dt, device="cuda")
+        K.decode(plan, codes_d, scales_d, lam.cuda(), y)
+        torch.cuda.synchronize()
+        r = P.compare_decode(np16(y).reshape(-1, D), c.reshape(-1, D // 2), s.reshape(-1, D // 32), lv,
+                             ROTS[rot], signs)
+        say(f"   decode {dt}: {r}")
+    # round trip within the quantization bound (orthogonality)
+    y = torch.empty((B, H, T, D), dtype=torch.float32, device="cuda")
+    K.decode(plan, codes_d, scales_d, lam.cuda(), y)
+    sig = np.repeat(s.reshape(-1, D // 32).astype(np.float64), 32, axis=-1)
+    bound = np.linalg.norm(sig / (2 * lv.astype(np.float64)), axis=-1)
+    err = np.linalg.norm(np16(y).reshape(-1, D).astype(np.float64) - np16(x).reshape(-1, D), axis=-1)
+    normal = (sig >= 2.0 ** -14).all(axis=-1)
+    assert np.all((err <= bound * (1 + 1e-4) + 1e-4)[normal])
+
+
+def test_qwen_prefix_full_srft():
+    """Qwen2.5-1.5B-shaped prefix (28 layers x {K,V} x 2 heads x 4096 tokens,
+    D=128): every vector checked."""
+    cfg = W.CONFIGS["qwen"]
+    x, lam = W.prefix_inputs(cfg)
+    plan = K.Plan(cfg.D, 32, "srft", cfg.sign_seed)
+    _, _, _, _, rep = check_encode("qwen-full", plan, "srft", x, lam)
+    assert rep["elements"] == cfg.vectors * cfg.D
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+def test_gemma_prefix_full(rot):
+    """Gemma-3-1B-shaped prefix (26 layers x {K,V} x 1 head x 4096 tokens,
+    D=256), SRFT and SRHT: every vector checked, decode included."""
+    cfg = W.CONFIGS["gemma"]
+    x, lam = W.prefix_inputs(cfg)
+    plan = K.Plan(cfg.D, 32, rot, cfg.sign_seed)
+    codes_d, scales_d, c, s, rep = check_encode("gemma-full", plan, rot, x, lam)
+    B, H, T, D = x.shape
+    signs = O.plan_signs(D, ROTS[rot], plan.seed)
+    lv = lam_per_vector(lam, B, H, T)
+    y = torch.empty((B, H, T, D), dtype=torch.float16, device="cuda")
+    K.decode(plan, codes_d, scales_d, lam.cuda(), y)
+    torch.cuda.synchronize()
+    r = P.compare_decode(np16(y).reshape(-1, D), c.reshape(-1, D // 2), s.reshape(-1, D // 32), lv,
+                         ROTS[rot], signs)
+    say(f"   decode fp16: {r}")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("rot", ["srft", "srht", "identity"])
+@pytest.mark.parametrize("T", [1, 63, 65, 130])
+def test_ragged_tokens_offsets_strides(D, rot, T):
+    """Ragged tails, a write offset inside a larger cache, strided input rows
+    and a lambda table shared across the batch."""
+    g = W.gen("cpu", 77, D, T)
+    B, H = 3, 2
+    base = torch.randn((B, H, T + 5, D + 24), generator=g).to(torch.float16) * 3
+    x = base[:, :, 2:2 + T, 8:8 + D]            # strides (H*(T+5)*(D+24), ...), row stride D+24
+    lam = torch.exp(0.3 * torch.randn((H, D), generator=g))
+    plan = K.Plan(D, 32, rot, 4242)
+    codes_d, scales_d, c, s, _ = check_encode("ragged", plan, rot, x, lam, Tcap=T + 40, t0=17)
+    signs = O.plan_signs(D, ROTS[rot], plan.seed)
+    lv = lam_per_vector(lam, B, H, T)
+    # decode the written tokens into a strided fp16 output and fp32
+    out = torch.full((B, H, T + 3, D + 8), 7.0, dtype=torch.float16, device="cuda")
+    y = out[:, :, 1:1 + T, :D]
+    K.decode(plan, codes_d, scales_d, lam.cuda(), y, t0=17)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    assert bool((o[:, :, 0] == 7.0).all()) and bool((o[:, :, 1 + T:] == 7.0).all())
+    assert bool((o[:, :, :, D:] == 7.0).all())
+    P.compare_decode(np16(y).reshape(-1, D), c.reshape(-1, D // 2), s.reshape(-1, D // 32), lv,
+                     ROTS[rot], signs)
+    y32 = torch.empty((B, H, T, D), dtype=torch.float32, device="cuda")
+    K.decode(plan, codes_d, scales_d, lam.cuda(), y32, t0=17)
+    torch.cuda.synchronize()
+    P.compare_decode(np16(y32).reshape(-1, D), c.reshape(-1, D // 2), s.reshape(-1, D // 32), lv,
+                     ROTS[rot], signs)
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_quantizer_special_groups(D):
+    """Identity rotation: exact grid values, half-even ties with power-of-two
+    scales, all-zero groups and subnormal-scale groups (clamp to -8)."""
+    rng = np.random.default_rng(5)
+    N = 64
+    x = np.zeros((N, D), dtype=np.float16)
+    lam = np.ones((N, D), dtype=np.float32)
+    for n in range(N):
+        for g in range(D // 32):
+            kind = (n + g) % 4
+            sl = slice(32 * g, 32 * g + 32)
+            if kind == 0:       # exact grid with sigma = 0.5
+                k = rng.integers(-7, 8, 32)
+                k[0] = 7
+                x[n, sl] = (k * 0.5).astype(np.float16)
+            elif kind == 1:     # ties with sigma = 1
+                x[n, sl] = np.array([7, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5] * 4, dtype=np.float16)
+            elif kind == 2:     # all zero
+                pass
+            else:               # subnormal scale: multiples of 2^-24
+                m = rng.integers(-10, 11, 32)
+                m[0] = 10
+                x[n, sl] = (m * 2.0 ** -24).astype(np.float16)
+    xt = torch.from_numpy(x).reshape(1, 1, N, D)
+    lt = torch.ones((1, D), dtype=torch.float32)
+    plan = K.Plan(D, 32, "identity", 0)
+    _, _, c, s, rep = check_encode("special", plan, "identity", xt, lt)
+    codes_ref, scales_ref, _ = O.encode(x, lam, O.IDENTITY, O.plan_signs(D, O.IDENTITY, 0))
+    assert np.array_equal(s.reshape(N, -1).view(np.uint16), scales_ref.view(np.uint16))
+    assert np.array_equal(c.reshape(N, -1), codes_ref)
+    assert (O.unpack_nibbles(codes_ref) == -8).any()
+
+
+def test_empty_calls_are_noops():
+    plan = K.Plan(128, 32, "srft", 1)
+    x = torch.zeros((2, 2, 0, 128), dtype=torch.float16, device="cuda")
+    lam = torch.ones((2, 128), device="cuda")
+    codes = torch.full((2, 2, 8, 64), 3, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((2, 2, 8, 4), dtype=torch.float16, device="cuda")
+    K.encode(plan, x, lam, codes, scales, 4)
+    torch.cuda.synchronize()
+    assert bool((codes == 3).all())
+
+
+def test_mistral_bulk_sampled():
+    """Mistral-7B-shaped bulk calls at full per-call size (B=16, H=8,
+    T=8192, D=128, Student-t(3) values): two calls (layer 0 K and V) encoded
+    and decoded on the GPU, 32768 seeded sample vectors checked against the
+    oracle."""
+    cfg = W.CONFIGS["mistral"]
+    plan = K.Plan(cfg.D, 32, "srft", cfg.sign_seed)
+    signs = O.plan_signs(cfg.D, O.SRFT, plan.seed)
+    rng = np.random.default_rng(0)
+    for kv in (0, 1):
+        say(f"[mistral] call layer 0 kv {kv}")
+        x = W.student_t3(cfg.H, cfg.T, cfg.D, cfg.data_seed, "cuda", 0, kv).unsqueeze(0).expand(
+            cfg.B, -1, -1, -1).contiguous()
+        # batch rows differ: perturb deterministically per batch row
+        x = (x.float() * (1.0 + 0.01 * torch.arange(cfg.B, device="cuda").view(-1, 1, 1, 1))).half()
+        lam = W.lognormal_lambda((cfg.H, cfg.D), cfg.lambda_seed, "cuda", 0.3, 0, kv)
+        codes = torch.empty((cfg.B, cfg.H, cfg.T, cfg.D // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((cfg.B, cfg.H, cfg.T, cfg.D // 32), dtype=torch.float16, device="cuda")
+        K.encode(plan, x, lam, codes, scales)
+        y = torch.empty_like(x)
+        K.decode(plan, codes, scales, lam, y)
+        torch.cuda.synchronize()
+        idx = rng.choice(cfg.B * cfg.H * cfg.T, 32768, replace=False)
+        xs = x.reshape(-1, cfg.D)[torch.from_numpy(idx).cuda()].cpu().numpy()
+        cs = codes.reshape(-1, cfg.D // 2)[torch.from_numpy(idx).cuda()].cpu().numpy()
+        ss = scales.reshape(-1, cfg.D // 32)[torch.from_numpy(idx).cuda()].cpu().numpy()
+        ys = y.reshape(-1, cfg.D)[torch.from_numpy(idx).cuda()].cpu().numpy()
+        heads = (idx // cfg.T) % cfg.H
+        lv = lam.cpu().numpy()[heads]
+        rep = P.compare_codes(cs, ss, xs, lv, O.SRFT, signs)
+        say(f"   codes: {rep['code_mismatch']} / {rep['scale_mismatch']} mismatches")
+        P.compare_decode(ys, cs, ss, lv, O.SRFT, signs)
+
+
+# -------------------------------------------------------------- attention --
+
+def build_cache(plan, B, Hkv, Hq, T, Tcap, D, seed):
+    """Decode-step inputs on the GPU and their int4 caches (tokens 0..T-1
+    encoded with kvq_encode)."""
+    k16, v16, lam_k, lam_v, q = W.decode_inputs(B, Hkv, Hq, Tcap, D, seed, "cuda")
+    kc = torch.empty((B, Hkv, Tcap, D // 2), dtype=torch.uint8, device="cuda")
+    ksc = torch.empty((B, Hkv, Tcap, D // 32), dtype=torch.float16, device="cuda")
+    vc = torch.empty_like(kc)
+    vsc = torch.empty_like(ksc)
+    K.encode(plan, k16[:, :, :T], lam_k, kc, ksc, 0)
+    K.encode(plan, v16[:, :, :T], lam_v, vc, vsc, 0)
+    return k16, v16, lam_k, lam_v, q, kc, ksc, vc, vsc
+
+
+def run_attn(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, out_dtype=torch.float32):
+    B, Hq, D = q.shape
+    ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=out_dtype, device="cuda")
+    K.attn_decode(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, out, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht", "identity"])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (2, 1), (16, 2)])
+@pytest.mark.parametrize("L", [1, 17, 300, 2051])
+def test_attention_small(rot, Hq, Hkv, L):
+    D, B = 128, 2
+    plan = K.Plan(D, 32, rot, 31)
+    Tcap = L + 9
+    say(f"[attn] rot={rot} Hq={Hq} Hkv={Hkv} L={L}")
+    k16, v16, lam_k, lam_v, q, kc, ksc, vc, vsc = build_cache(plan, B, Hkv, Hq, L, Tcap, D, 11)
+    sm = 1 / math.sqrt(D)
+    signs = O.plan_signs(D, ROTS[rot], plan.seed)
+    ref = O.attention_int4(np16(q), kc.cpu().numpy(), ksc.cpu().numpy(), lam_k.cpu().numpy(),
+                           vc.cpu().numpy(), vsc.cpu().numpy(), lam_v.cpu().numpy(), L, sm, ROTS[rot], signs)
+    for dt in (torch.float32, torch.float16):
+        out = run_attn(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, dt)
+        worst = P.compare_attention(np16(out), ref)
+        say(f"   int4 {dt}: rel err {worst:.2e}")
+    # fp16 comparator over the unquantized cache
+    ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    K.attn_decode_f16(q, k16, v16, L, sm, out, ws)
+    torch.cuda.synchronize()
+    ref16 = O.attention_f16(np16(q), k16.cpu().numpy(), v16.cpu().numpy(), L, sm)
+    worst = P.compare_attention(np16(out), ref16)
+    say(f"   fp16 comparator: rel err {worst:.2e}")
+
+
+def test_attention_decode_step_full_size():
+    """The decode step at full size: batch 64, Hq 8 / Hkv 2, D=128, 32768
+    cached tokens plus one appended with kvq_encode (T=1, t0=32768), then
+    attention over 32769 tokens; 8 seeded (b, kv head) pairs checked against
+    the oracle (all their query heads)."""
+    cfg = W.CONFIGS["decode"]
+    B, Hkv, Hq, D = cfg.B, cfg.H, 8, cfg.D
+    T0 = cfg.T
+    L = T0 + 1
+    Tcap = T0 + 256
+    plan = K.Plan(D, 32, "srft", cfg.sign_seed)
+    say("[attn-full] building caches")
+    k16, v16, lam_k, lam_v, q, kc, ksc, vc, vsc = build_cache(plan, B, Hkv, Hq, T0, Tcap, D, cfg.data_seed)
+    # append one token per sequence
+    K.encode(plan, k16[:, :, T0:T0 + 1], lam_k, kc, ksc, T0)
+    K.encode(plan, v16[:, :, T0:T0 + 1], lam_v, vc, vsc, T0)
+    sm = 1 / math.sqrt(D)
+    say("[attn-full] int4 attention")
+    out = run_attn(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, torch.float16)
+    ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device="cuda")
+    out16 = torch.empty((B, Hq, D), dtype=torch.float16, device="cuda")
+    say("[attn-full] fp16 comparator")
+    K.attn_decode_f16(q, k16, v16, L, sm, out16, ws)
+    torch.cuda.synchronize()
+    signs = O.plan_signs(D, O.SRFT, plan.seed)
+    rng = np.random.default_rng(4)
+    pairs = [(int(b), int(g)) for b, g in zip(rng.choice(B, 8, replace=False), rng.integers(0, Hkv, 8))]
+    rep = Hq // Hkv
+    for b, g in pairs:
+        sl = slice(b, b + 1)
+        kcs = kc[sl, g:g + 1, :L].cpu().numpy()
+        kss = ksc[sl, g:g + 1, :L].cpu().numpy()
+        vcs = vc[sl, g:g + 1, :L].cpu().numpy()
+        vss = vsc[sl, g:g + 1, :L].cpu().numpy()
+        qs = np16(q[sl, g * rep:(g + 1) * rep])
+        ref = O.attention_int4(qs, kcs, kss, lam_k[g:g + 1].cpu().numpy(), vcs, vss,
+                               lam_v[g:g + 1].cpu().numpy(), L, sm, O.SRFT, signs)
+        w1 = P.compare_attention(np16(out[sl, g * rep:(g + 1) * rep]).astype(np.float64), ref)
+        ref16 = O.attention_f16(qs, k16[sl, g:g + 1].cpu().numpy(), v16[sl, g:g + 1].cpu().numpy(), L, sm)
+        w2 = P.compare_attention(np16(out16[sl, g * rep:(g + 1) * rep]).astype(np.float64), ref16)
+        say(f"   (b={b}, g={g}): int4 rel {w1:.2e}, fp16 rel {w2:.2e}")
