@@ -1,29 +1,37 @@
 // Decode-step attention over the int4 cache (and the fp16-cache comparator).
 //
 // Three launches per step on the caller's stream:
-//   1. qrot:    q~ = sm_scale * log2(e) * (R q) / lambda_K for every (b, h):
-//               scores can then be taken directly against the rotated,
-//               lambda-scaled cache, since q . k^ = (R q) . (R k^) and the
-//               cache stores lambda * R k (one lane per query vector, the
-//               same in-register FFT as the codec).
+//   1. qrot:    q~ = sm_scale * log2(e) * (R q) / lambda_K for every query
+//               vector (one lane each, the codec's in-register transform).
+//               Scores can then be taken directly against the stored codes:
+//               the cache holds lambda * R k, and q . k^ = (R q) . (R k^).
+//               For the int4 cache q~ is written as three int8 limbs per
+//               32-channel group, q~ ~= s (Q1 + Q2/256 + Q3/65536) with
+//               s = max|q~| / 127 (about 23 bits); for the fp16 cache as
+//               fp16 hi + lo halves.
 //   2. split:   one wave per (b, kv head, group of <= 4 query heads, context
-//               split) streams its slice of the cache 16 tokens at a time:
-//                 QK: v_mfma_f32_16x16x32_f16 with the 16 tokens as rows and
-//                     the query heads as columns, one MFMA per 32-channel
-//                     group (the group's fp16 scale is applied to the MFMA
-//                     result); q~ is split into fp16 hi + lo halves so the
-//                     product keeps ~22 bits;
-//                 softmax: online, base 2, with the running maximum moved
-//                     only when a score exceeds it by more than 2^8 (the
-//                     common rescale factor cancels in the final division);
-//                 PV: v_mfma_f32_16x16x16f16 with rows = (channel group,
-//                     head) pairs, so each row's weights p * scale_V carry
-//                     the value scale of one group and the int4 values enter
-//                     the MFMA exactly as small integers.
+//               split) streams its slice of the cache 32 tokens at a time:
+//                 QK (int4): v_mfma_i32_16x16x64_i8, rows = 16 tokens,
+//                   columns = (channel group, head) pairs, so every lane
+//                   holds useful scores.  The codes enter as unsigned
+//                   nibbles (n = q + 8, one AND and one shift per word); the
+//                   -8 offset is the accumulator's initial value, and the
+//                   group scale multiplies the exact integer result.
+//                 QK (fp16): v_mfma_f32_16x16x32_f16 on the fp16 keys.
+//                 softmax: online, base 2, exact running maximum.
+//                 PV: v_mfma_f32_16x16x32_f16.  For the int4 cache the rows
+//                   are again (channel group, head) pairs: a row's weights
+//                   p * scale_V carry the value scale of one group and the
+//                   codes enter as exact small fp16 integers (n - 8, built
+//                   from the nibble with a biased exponent).  The weights are
+//                   split into fp16 hi + lo halves (two MFMAs), which keeps
+//                   ~22 bits: one fp16 rounding of p costs up to ~5e-3
+//                   relative error through cancellation across tokens.
 //               It writes the partial (max, sum, 128 weighted values) of
 //               every head to the workspace.
 //   3. combine: merges the splits (log-sum-exp), divides by lambda_V and
-//               applies the inverse rotation once per output vector.
+//               applies the inverse rotation across the 64 lanes of a wave
+//               (radix-2 steps with cross-lane shuffles).
 //
 // Method: the read side of the paper's fused quantizer ("When Quantization
 // Is Free", abstract; gist.science explainer, "Methodik" 1-2) fused into the
@@ -38,13 +46,25 @@ namespace kvq {
 
 namespace {
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kHeadsPerWave = 4;
-constexpr int kTok = 16;              // tokens per inner step
+constexpr int kBlk = 32;              // tokens per inner step
+constexpr int kQRec = 512;            // bytes of one rotated-query record
+
+// Record layout (int4 cache): three int8 limbs per channel,
+// q~ ~= s (Q1 + Q2 / 256 + Q3 / 65536): [0,128) Q1, [128,256) Q2,
+// [256,384) Q3, [384,400) s[4] f32, [400,448) sums of Q1, Q2, Q3 per group
+// (i32[3][4]).  Record layout (fp16 cache): [0,256) hi fp16[128],
+// [256,512) lo fp16[128].
+constexpr int kRecS = 384;
+constexpr int kRecSum = 400;
+
+__constant__ TwTable kTw64Const = make_twiddles(64);
 
 struct AttnArgs {
   const uint16_t* q;
@@ -56,7 +76,7 @@ struct AttnArgs {
   const float* lambda_v;
   const uint16_t* k16;
   const uint16_t* v16;
-  float* qt;          // [B*Hq][128] rotated, scaled queries
+  uint8_t* qrec;      // [B*Hq] records
   float* part_acc;    // [B*Hq][S][128]
   float* part_ml;     // [B*Hq][S][2]
   void* out;
@@ -67,81 +87,322 @@ struct AttnArgs {
   uint64_t signs[4];
 };
 
+__device__ __forceinline__ uint32_t sign_bit(const uint64_t (&s)[4], int i) {
+  const uint64_t w = i < 64 ? s[0] : i < 128 ? s[1] : i < 192 ? s[2] : s[3];
+  return static_cast<uint32_t>(w >> (i & 63)) & 1u;
+}
+
 // ---------------------------------------------------------------------------
 // 1. query rotation
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+__device__ __forceinline__ int bitrev6(int x) {
+  return static_cast<int>(__builtin_bitreverse32(static_cast<uint32_t>(x)) >> 26);
+}
+
+// One wave per query vector.  Lane l owns channels 2l, 2l+1.
 template <int ROT>
 __global__ void __launch_bounds__(64) attn_qrot_kernel(AttnArgs a, int int4) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x;
-  if (idx >= a.B * a.Hq) return;
+  const int lane = threadIdx.x;
+  const int64_t idx = blockIdx.x;          // b * Hq + h
   const int64_t h = idx % a.Hq;
   const int64_t g = h / (a.Hq / a.Hkv);
   const uint16_t* qr = a.q + idx * 128;
-  float v[128];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint4 w = *reinterpret_cast<const uint4*>(qr + 8 * j);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k = 4 * j + e;   // pair index
-      uint32_t m = 0;
-      if (int4 && ROT == KVQ_ROT_SRFT) {
-        m = ((a.signs[k >> 6] >> (k & 63)) & 1) ? 0x80008000u : 0u;
-      } else if (int4 && ROT == KVQ_ROT_SRHT) {
-        const int i0 = 2 * k, i1 = 2 * k + 1;
-        m = (static_cast<uint32_t>((a.signs[i0 >> 6] >> (i0 & 63)) & 1) << 15) |
-            (static_cast<uint32_t>((a.signs[i1 >> 6] >> (i1 & 63)) & 1) << 31);
-      }
-      const uint32_t x = ws[e] ^ m;
-      v[2 * k] = f16_bits_to_f32(x & 0xFFFFu);
-      v[2 * k + 1] = f16_bits_to_f32(x >> 16);
-    }
-  }
-  float* out = a.qt + idx * 128;
+  uint8_t* rec = a.qrec + idx * kQRec;
   if (!int4) {
     const float s = a.sm_scale * kLog2e;
-#pragma unroll
-    for (int j = 0; j < 128; j += 4)
-      *reinterpret_cast<float4*>(out + j) = make_float4(v[j] * s, v[j + 1] * s, v[j + 2] * s, v[j + 3] * s);
+    const uint32_t w = reinterpret_cast<const uint32_t*>(qr)[lane];
+    const float x0 = f16_bits_to_f32(w & 0xFFFFu) * s, x1 = f16_bits_to_f32(w >> 16) * s;
+    const uint32_t hw = pack_f16x2(x0, x1);
+    reinterpret_cast<uint32_t*>(rec)[lane] = hw;
+    reinterpret_cast<uint32_t*>(rec + 256)[lane] =
+        pack_f16x2(x0 - f16_bits_to_f32(hw & 0xFFFFu), x1 - f16_bits_to_f32(hw >> 16));
     return;
   }
+  float y0, y1;       // rotated channels 2 lane, 2 lane + 1 (unnormalized)
   float c = 1.f;
   if (ROT == KVQ_ROT_SRFT) {
-    fft64<false>(v);
-    c = 0.125f;
-  } else if (ROT == KVQ_ROT_SRHT) {
-    wht128(v);
-    c = 0.0883883476483184405f;
-  }
-  const float s = a.sm_scale * kLog2e * c;
-  const float* lk = a.lambda_k + g * 128;
+    // forward 64-point DFT across lanes, radix-2 decimation in time: lane l
+    // starts with pair bitrev(l) (signed) and ends with frequency l
+    const int k = bitrev6(lane);
+    const uint32_t w = reinterpret_cast<const uint32_t*>(qr)[k] ^ (sign_bit(a.signs, k) ? 0x80008000u : 0u);
+    float re = f16_bits_to_f32(w & 0xFFFFu), im = f16_bits_to_f32(w >> 16);
 #pragma unroll
-  for (int j = 0; j < 128; j += 4) {
-    float4 o;
-    o.x = v[chan_reg<ROT>(j)] * s / lk[j];
-    o.y = v[chan_reg<ROT>(j + 1)] * s / lk[j + 1];
-    o.z = v[chan_reg<ROT>(j + 2)] * s / lk[j + 2];
-    o.w = v[chan_reg<ROT>(j + 3)] * s / lk[j + 3];
-    *reinterpret_cast<float4*>(out + j) = o;
+    for (int hh = 1; hh <= 32; hh <<= 1) {
+      const float pr = shfl_xor(re, hh), pi = shfl_xor(im, hh);
+      const bool upper = lane & hh;
+      // t = W^j * (the upper element), W = exp(-2 pi i / (2 hh))
+      const float ur = upper ? re : pr, ui = upper ? im : pi;
+      const int e = (lane & (hh - 1)) * (32 / hh);
+      const float cw = kTw64Const.c[e], sw = kTw64Const.s[e];
+      const float tr = ur * cw + ui * sw, ti = ui * cw - ur * sw;
+      const float br = upper ? pr : re, bi = upper ? pi : im;
+      re = upper ? br - tr : br + tr;
+      im = upper ? bi - ti : bi + ti;
+    }
+    y0 = re;
+    y1 = im;
+    c = 0.125f;
+  } else {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(qr)[lane];
+    uint32_t m = 0;
+    if (ROT == KVQ_ROT_SRHT) m = (sign_bit(a.signs, 2 * lane) << 15) | (sign_bit(a.signs, 2 * lane + 1) << 31);
+    y0 = f16_bits_to_f32((w ^ m) & 0xFFFFu);
+    y1 = f16_bits_to_f32((w ^ m) >> 16);
+    if (ROT == KVQ_ROT_SRHT) {
+      const float t0 = y0 + y1, t1 = y0 - y1;
+      y0 = t0;
+      y1 = t1;
+#pragma unroll
+      for (int hh = 1; hh <= 32; hh <<= 1) {
+        const float p0 = shfl_xor(y0, hh), p1 = shfl_xor(y1, hh);
+        if (lane & hh) { y0 = p0 - y0; y1 = p1 - y1; }
+        else { y0 += p0; y1 += p1; }
+      }
+      c = 0.0883883476483184405f;
+    }
   }
+  const float sc = a.sm_scale * kLog2e * c;
+  const float* lk = a.lambda_k + g * 128;
+  const float q0 = y0 * sc / lk[2 * lane], q1 = y1 * sc / lk[2 * lane + 1];
+  // group = 16 lanes: abs max, three int8 limbs
+  float amax = fmaxf(fabsf(q0), fabsf(q1));
+#pragma unroll
+  for (int m = 1; m <= 8; m <<= 1) amax = fmaxf(amax, shfl_xor(amax, m));
+  const float inv = amax > 0.f ? 127.f / amax : 0.f;
+  const float t[2] = {q0 * inv, q1 * inv};
+  int li[3][2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    // |t| <= 127; each residual is at most half a unit of its limb
+    float r1 = rintf(t[e]);
+    const float u = (t[e] - r1) * 256.f;
+    float r2 = rintf(u);
+    const float r3 = fminf(fmaxf(rintf((u - r2) * 256.f), -128.f), 127.f);
+    if (r2 > 127.f) {          // +128 is no int8: carry into the first limb
+      r2 -= 256.f;
+      r1 += 1.f;
+    }
+    li[0][e] = static_cast<int>(r1);
+    li[1][e] = static_cast<int>(r2);
+    li[2][e] = static_cast<int>(r3);
+  }
+  const int grp = lane >> 4;
+#pragma unroll
+  for (int limb = 0; limb < 3; ++limb) {
+    reinterpret_cast<uint16_t*>(rec + 128 * limb)[lane] =
+        static_cast<uint16_t>((li[limb][0] & 0xFF) | ((li[limb][1] & 0xFF) << 8));
+    float sum = static_cast<float>(li[limb][0] + li[limb][1]);
+#pragma unroll
+    for (int m = 1; m <= 8; m <<= 1) sum += shfl_xor(sum, m);
+    if ((lane & 15) == 0) reinterpret_cast<int*>(rec + kRecSum)[4 * limb + grp] = static_cast<int>(sum);
+  }
+  if ((lane & 15) == 0) reinterpret_cast<float*>(rec + kRecS)[grp] = amax > 0.f ? amax / 127.f : 0.f;
 }
 
 // ---------------------------------------------------------------------------
 // 2. split-K streaming kernel
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float shfl_xor(float x, int mask) {
-  return __shfl_xor(x, mask, 64);
+// x + (x of lane (l + n) mod 16 within the row): DPP row_ror
+template <int N>
+__device__ __forceinline__ float add_row_ror(float x) {
+  const float r = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + N, 0xF, 0xF, true));
+  return x + r;
 }
 
-// fp16 pair (lo, hi) = (q_a - 8, q_b - 8) from two offset nibbles sitting in
-// bits 0..3 and 16..19 of x (the other bits zero): 0x6400 | n is the fp16
-// value 1024 + n, exactly.
-__device__ __forceinline__ uint32_t nib_pair_to_f16x2(uint32_t x) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 v = __builtin_bit_cast(h2, x | 0x64006400u);
-  const h2 r = v - (h2){(_Float16)1032.0f, (_Float16)1032.0f};
-  return __builtin_bit_cast(uint32_t, r);
+// Cache loads of one 32-token block (sub-blocks sb = 0, 1 of 16 tokens).
+template <bool INT4>
+struct Blk {
+  uint4 k[2];            // int4: 16 code bytes of token 16 sb + n16, group kq
+  uint4 kf[2][4];        // fp16: 8 channels of each group for that token
+  uint32_t v[2][4];      // int4: code dword n16 of token 16 sb + 4 kq + i
+  uint4 vf[2][4];        // fp16: channels 8 n16 .. 8 n16 + 7 of that token
+  uint16_t ks[2][4];     // int4: key scale of token 16 sb + 4 kq + i, group n16 / 4
+  uint16_t vs[2][4];     // int4: value scale of the same token, group n16 / 4
+};
+
+// Row-relative bases of one (batch, kv head): every offset below is 32-bit.
+struct Rows {
+  const uint8_t* kc;     // int4 codes of token 0
+  const uint16_t* ksc;
+  const uint8_t* vc;
+  const uint16_t* vsc;
+  const uint16_t* k16;   // fp16 cache
+  const uint16_t* v16;
+};
+
+// Token index actually read: in the last (tail) block of a split the
+// positions past the end re-read its last token; their scores are masked.
+template <bool TAIL>
+__device__ __forceinline__ uint32_t tok(uint32_t t, uint32_t t_last) {
+  return TAIL ? min(t, t_last) : t;
+}
+
+// Loads at a wave-uniform base plus an unsigned 32-bit lane offset (the
+// SGPR-base form of the global load instructions).
+template <typename T>
+__device__ __forceinline__ T ld(const void* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(static_cast<const uint8_t*>(base) + off);
+}
+
+template <bool INT4, bool TAIL>
+__device__ __forceinline__ void load_blk(const Rows& r, uint32_t t0, uint32_t t_last, uint32_t n16, uint32_t kq,
+                                         Blk<INT4>& o) {
+  const uint32_t grp = n16 >> 2;
+#pragma unroll
+  for (uint32_t sb = 0; sb < 2; ++sb) {
+    const uint32_t tk = tok<TAIL>(t0 + 16 * sb + n16, t_last);
+    if (INT4) {
+      o.k[sb] = ld<uint4>(r.kc, (tk << 6) + (kq << 4));
+    } else {
+#pragma unroll
+      for (uint32_t gq = 0; gq < 4; ++gq) o.kf[sb][gq] = ld<uint4>(r.k16, (tk << 8) + 64 * gq + 16 * kq);
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) {
+      const uint32_t t = tok<TAIL>(t0 + 16 * sb + 4 * kq + i, t_last);
+      if (INT4) {
+        o.v[sb][i] = ld<uint32_t>(r.vc, (t << 6) + (n16 << 2));
+        o.ks[sb][i] = ld<uint16_t>(r.ksc, (t << 3) + (grp << 1));
+        o.vs[sb][i] = ld<uint16_t>(r.vsc, (t << 3) + (grp << 1));
+      } else {
+        o.vf[sb][i] = ld<uint4>(r.v16, (t << 8) + (n16 << 4));
+      }
+    }
+  }
+}
+
+// Per-wave streaming state.
+template <bool INT4>
+struct State {
+  int4_t qb[3][2];           // int4 QK right operand: [limb][k-step]
+  int4_t corr[3];            // int4 accumulator start: -8 * sum(Q) per limb
+  float sfac;                // int4: s / 256 of column (group, head)
+  half8_t qh[4], ql[4];      // fp16 QK right operand: hi / lo
+  float4_t acc[8];           // PV accumulators, MFMA c <-> channel 8 n16 + c
+  float m_run;               // running max of this lane's head
+  float l_part;              // this lane's share of the running sum
+};
+
+template <bool INT4, bool TAIL>
+__device__ __forceinline__ void process_blk(State<INT4>& st, const Blk<INT4>& cur, uint32_t t0, uint32_t t_end,
+                                            uint32_t kq) {
+  // ---- scores: lane holds tokens t0 + 16 sb + 4 kq + i of its head ----
+  float sc[2][4];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    if (INT4) {
+      const uint4 w = cur.k[sb];
+      // unsigned nibbles as int8: k-step 0 = even channels, 1 = odd channels
+      const int4_t a0 = (int4_t){static_cast<int>(w.x & 0x0F0F0F0Fu), static_cast<int>(w.y & 0x0F0F0F0Fu),
+                                 static_cast<int>(w.z & 0x0F0F0F0Fu), static_cast<int>(w.w & 0x0F0F0F0Fu)};
+      const int4_t a1 = (int4_t){static_cast<int>((w.x >> 4) & 0x0F0F0F0Fu),
+                                 static_cast<int>((w.y >> 4) & 0x0F0F0F0Fu),
+                                 static_cast<int>((w.z >> 4) & 0x0F0F0F0Fu),
+                                 static_cast<int>((w.w >> 4) & 0x0F0F0F0Fu)};
+      int4_t c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[0][0], st.corr[0], 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[0][1], c1, 0, 0, 0);
+      int4_t c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[1][0], st.corr[1], 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[1][1], c2, 0, 0, 0);
+      int4_t c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[2][0], st.corr[2], 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[2][1], c3, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // 256 c1 + c2 is exact in int32; the third limb joins in fp32
+        const float f = fmaf(static_cast<float>(c1[i] * 256 + c2[i]), 256.f, static_cast<float>(c3[i])) * st.sfac;
+        float x = f * f16_bits_to_f32(cur.ks[sb][i]);
+        x = add_row_ror<8>(x);     // + group (g + 2) mod 4
+        x = add_row_ror<4>(x);     // + groups (g + 1), (g + 3)
+        sc[sb][i] = x;
+      }
+    } else {
+      float4_t c = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const half8_t ka = __builtin_bit_cast(half8_t, cur.kf[sb][grp]);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, st.qh[grp], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, st.ql[grp], c, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[sb][i] = c[i];
+    }
+    if (TAIL) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (t0 + 16 * sb + 4 * kq + i >= t_end) sc[sb][i] = -INFINITY;
+    }
+  }
+
+  // ---- online softmax (base 2, exact running max) ----
+  float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  bm = fmaxf(bm, shfl_xor(bm, 16));
+  bm = fmaxf(bm, shfl_xor(bm, 32));
+  if (__builtin_amdgcn_ballot_w64(bm > st.m_run) != 0) {
+    const float m_new = fmaxf(st.m_run, bm);
+    const float alpha = (st.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+    st.l_part *= alpha;
+    st.m_run = m_new;
+    // PV rows (block kq, head i) scale by the factor of head i (lane i)
+    float al[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      al[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st.acc[c][i] *= al[i];
+    }
+  }
+
+  // ---- PV left operand: p (times the value scale of group n16 / 4) ----
+  half8_t pa_hi, pa_lo;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(sc[sb][i] - st.m_run);
+      st.l_part += p;
+      const float w = INT4 ? p * f16_bits_to_f32(cur.vs[sb][i]) : p;
+      const _Float16 hi = static_cast<_Float16>(w);
+      pa_hi[4 * sb + i] = hi;
+      pa_lo[4 * sb + i] = static_cast<_Float16>(w - static_cast<float>(hi));
+    }
+  }
+
+  // ---- PV: MFMA c takes channel 8 n16 + c; k slot 4 sb + i <-> token.
+  // A nibble masked under the exponent of 1024 is the fp16 number 1024 + n
+  // (low nibble) or 1024 + 16 n (high nibble); one packed subtraction makes
+  // it n - 8 or 16 (n - 8), exact normal fp16 values.  (Products of two fp16
+  // subnormals, which a nibble masked in place would be, do not keep their
+  // full value in the matrix unit's fp32 sums.) ----
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t hv[4];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        if (INT4) {
+          const int by = c >> 1;
+          const uint32_t sel = 0x0c000c00u | (static_cast<uint32_t>(4 + by) << 16) | static_cast<uint32_t>(by);
+          const uint32_t x = __builtin_amdgcn_perm(cur.v[sb][2 * pr + 1], cur.v[sb][2 * pr], sel);
+          const uint32_t biased = (x & ((c & 1) ? 0x00F000F0u : 0x000F000Fu)) | 0x64006400u;
+          const half2_t off = (c & 1) ? (half2_t){static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)}
+                                         : (half2_t){static_cast<_Float16>(-1032.f), static_cast<_Float16>(-1032.f)};
+          hv[2 * sb + pr] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, biased) + off);
+        } else {
+          const uint32_t w0 = (&cur.vf[sb][2 * pr].x)[c >> 1];
+          const uint32_t w1 = (&cur.vf[sb][2 * pr + 1].x)[c >> 1];
+          hv[2 * sb + pr] = __builtin_amdgcn_perm(w1, w0, (c & 1) ? 0x07060302u : 0x05040100u);
+        }
+      }
+    }
+    const half8_t vb = __builtin_bit_cast(half8_t, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb, st.acc[c], 0, 0, 0);
+    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_lo, vb, st.acc[c], 0, 0, 0);
+  }
 }
 
 template <bool INT4>
@@ -161,285 +422,255 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
   const int64_t hq0 = g * rep + hc * kHeadsPerWave;
   const int nh = static_cast<int>(rep - hc * kHeadsPerWave < kHeadsPerWave ? rep - hc * kHeadsPerWave
                                                                           : kHeadsPerWave);
-  const int64_t t_begin = s * a.chunk;
-  int64_t t_end = t_begin + a.chunk;
-  if (t_end > a.seq_len) t_end = a.seq_len;
+  const uint32_t t_begin = static_cast<uint32_t>(s * a.chunk);
+  const uint32_t t_end = static_cast<uint32_t>(min(s * a.chunk + a.chunk, a.seq_len));
+  const int64_t cell0 = (b * a.Hkv + g) * a.Tcap;
+  Rows rows;
+  rows.kc = a.k_codes + cell0 * 64;
+  rows.ksc = a.k_scales + cell0 * 4;
+  rows.vc = a.v_codes + cell0 * 64;
+  rows.vsc = a.v_scales + cell0 * 4;
+  rows.k16 = a.k16 + cell0 * 128;
+  rows.v16 = a.v16 + cell0 * 128;
 
-  // QK right operand: q~ of head n16 (zero for padding columns), channels
-  // 32 grp + 8 kq + {0, 4, 1, 5, 2, 6, 3, 7} in the eight k slots -- the
-  // order in which the key nibbles are unpacked below.
-  half8_t qb_hi[4], qb_lo[4];
-  {
-    const float* qrow = a.qt + (b * a.Hq + hq0 + (n16 < nh ? n16 : 0)) * 128;
+  // The head whose scores this lane holds: int4 columns are (group, head)
+  // pairs with head = n16 & 3; fp16 columns are heads.
+  const int my_head = INT4 ? (n16 & 3) : n16;
+  const bool head_ok = my_head < nh;
+  const uint8_t* rec = a.qrec + (b * a.Hq + hq0 + (head_ok ? my_head : 0)) * kQRec;
+
+  State<INT4> st;
+  if (INT4) {
+    const int grp = n16 >> 2;
+    const bool live = head_ok && grp == kq;
+#pragma unroll
+    for (int limb = 0; limb < 3; ++limb) {
+      uint32_t d[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        d[e] = live ? reinterpret_cast<const uint32_t*>(rec + 128 * limb + 32 * kq)[e] : 0u;
+      // k slot j of k-step ks <-> channel 32 kq + 2 j + ks
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t sel = ks ? 0x07050301u : 0x06040200u;
+        st.qb[limb][ks] = (int4_t){static_cast<int>(__builtin_amdgcn_perm(d[1], d[0], sel)),
+                                   static_cast<int>(__builtin_amdgcn_perm(d[3], d[2], sel)),
+                                   static_cast<int>(__builtin_amdgcn_perm(d[5], d[4], sel)),
+                                   static_cast<int>(__builtin_amdgcn_perm(d[7], d[6], sel))};
+      }
+      const int sum = head_ok ? reinterpret_cast<const int*>(rec + kRecSum)[4 * limb + grp] : 0;
+      st.corr[limb] = (int4_t){-8 * sum, -8 * sum, -8 * sum, -8 * sum};
+    }
+    st.sfac = head_ok ? reinterpret_cast<const float*>(rec + kRecS)[grp] * (1.f / 65536.f) : 0.f;
+  } else {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int ch = 32 * grp + 8 * kq + p + 4 * e;
-          const float x = (n16 < nh) ? qrow[ch] : 0.f;
-          const _Float16 hi = static_cast<_Float16>(x);
-          const _Float16 lo = static_cast<_Float16>(x - static_cast<float>(hi));
-          qb_hi[grp][2 * p + e] = hi;
-          qb_lo[grp][2 * p + e] = lo;
-        }
-      }
+      const uint4 h = head_ok ? *reinterpret_cast<const uint4*>(rec + 2 * (32 * grp + 8 * kq)) : make_uint4(0, 0, 0, 0);
+      const uint4 l = head_ok ? *reinterpret_cast<const uint4*>(rec + 256 + 2 * (32 * grp + 8 * kq))
+                              : make_uint4(0, 0, 0, 0);
+      st.qh[grp] = __builtin_bit_cast(half8_t, h);
+      st.ql[grp] = __builtin_bit_cast(half8_t, l);
     }
   }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) st.acc[c] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.f;
 
-  float4_t acc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max of head n16 (same in its 4 lanes)
-  float l_part = 0.f;        // this lane's share of the running sum
-
-  const int64_t row_kv = b * a.Hkv + g;
-  // useful PV rows: int4 rows are (channel group, head) = (n16 / 4, n16 % 4);
-  // fp16 rows are heads.
-  const int pv_head = INT4 ? (n16 & 3) : n16;
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTok) {
-    // ---- keys: A operand (token n16, k slice kq of each group) ----
-    const int64_t tk = t0 + n16;
-    const bool kvalid = tk < t_end;
-    half8_t ka[4];
-    if (INT4) {
-      const uint32_t* krow = reinterpret_cast<const uint32_t*>(a.k_codes + (row_kv * a.Tcap + tk) * 64);
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const uint32_t w = kvalid ? krow[4 * grp + kq] : 0x88888888u;
-        // slots (2p, 2p+1) = nibbles (p, p + 4)
-        uint32_t h2[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) h2[p] = nib_pair_to_f16x2((w >> (4 * p)) & 0x000F000Fu);
-        ka[grp] = __builtin_bit_cast(half8_t, make_uint4(h2[0], h2[1], h2[2], h2[3]));
-      }
-    } else {
-      const uint16_t* krow = a.k16 + (row_kv * a.Tcap + tk) * 128;
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        uint4 w = kvalid ? *reinterpret_cast<const uint4*>(krow + 32 * grp + 8 * kq) : make_uint4(0, 0, 0, 0);
-        // reorder the 8 channels to slots {0, 4, 1, 5, 2, 6, 3, 7}
-        const uint32_t c01 = w.x, c23 = w.y, c45 = w.z, c67 = w.w;
-        const uint32_t s0 = __builtin_amdgcn_perm(c45, c01, 0x05040100u);  // (c0, c4)
-        const uint32_t s1 = __builtin_amdgcn_perm(c45, c01, 0x07060302u);  // (c1, c5)
-        const uint32_t s2 = __builtin_amdgcn_perm(c67, c23, 0x05040100u);  // (c2, c6)
-        const uint32_t s3 = __builtin_amdgcn_perm(c67, c23, 0x07060302u);  // (c3, c7)
-        ka[grp] = __builtin_bit_cast(half8_t, make_uint4(s0, s1, s2, s3));
-      }
+  // 32-token blocks; the block that reaches t_end is a tail
+  const uint32_t t_last = t_end - 1;
+  const int n_full = static_cast<int>((t_end - t_begin) / kBlk);   // blocks entirely inside
+  uint32_t t0 = t_begin;
+  if (INT4) {
+    // ping-pong: the next block streams in while this one is processed
+    Blk<INT4> b0, b1;
+    if (n_full > 0) load_blk<INT4, false>(rows, t0, t_last, n16, kq, b0);
+    for (int i = 0; i < n_full; i += 2) {
+      // b0 holds block i
+      if (i + 1 < n_full) load_blk<INT4, false>(rows, t0 + kBlk, t_last, n16, kq, b1);
+      else if (t0 + kBlk < t_end) load_blk<INT4, true>(rows, t0 + kBlk, t_last, n16, kq, b1);
+      process_blk<INT4, false>(st, b0, t0, t_end, kq);
+      t0 += kBlk;
+      if (i + 1 >= n_full) break;
+      // b1 holds block i + 1
+      if (i + 2 < n_full) load_blk<INT4, false>(rows, t0 + kBlk, t_last, n16, kq, b0);
+      else if (t0 + kBlk < t_end) load_blk<INT4, true>(rows, t0 + kBlk, t_last, n16, kq, b0);
+      process_blk<INT4, false>(st, b1, t0, t_end, kq);
+      t0 += kBlk;
     }
-
-    // ---- scores: C[token 4 kq + i][head n16] ----
-    float sc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (INT4) {
-      // key scales of this lane's four output tokens
-      uint2 ks[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = t0 + 4 * kq + i;
-        ks[i] = (t < t_end) ? *reinterpret_cast<const uint2*>(a.k_scales + (row_kv * a.Tcap + t) * 4)
-                            : make_uint2(0, 0);
-      }
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        float4_t c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[grp], qb_hi[grp], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[grp], qb_lo[grp], c, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t sw = (grp < 2 ? ks[i].x : ks[i].y) >> (16 * (grp & 1));
-          sc[i] = fmaf(f16_bits_to_f32(sw & 0xFFFFu), c[i], sc[i]);
-        }
-      }
-    } else {
-      float4_t c = (float4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[grp], qb_hi[grp], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[grp], qb_lo[grp], c, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = c[i];
+    if (t0 < t_end) {
+      // the partial block: already in b1 (odd n_full) or b0 (even n_full > 0),
+      // or not loaded yet (n_full == 0)
+      if (n_full == 0) load_blk<INT4, true>(rows, t0, t_last, n16, kq, b0);
+      if (n_full & 1) process_blk<INT4, true>(st, b1, t0, t_end, kq);
+      else process_blk<INT4, true>(st, b0, t0, t_end, kq);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (t0 + 4 * kq + i >= t_end) sc[i] = -INFINITY;
-
-    // ---- online softmax (base 2) ----
-    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    bm = fmaxf(bm, shfl_xor(bm, 16));
-    bm = fmaxf(bm, shfl_xor(bm, 32));
-    const bool grow = bm > m_run + 8.f;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = fmaxf(m_run, bm);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      l_part *= alpha;
-      m_run = m_new;
-      // rescale the PV accumulator rows of every head
-      float al[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) al[h] = __shfl(alpha, h, 64);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[c][i] *= INT4 ? al[i] : (kq == 0 ? al[i] : 1.f);
-      }
+  } else {
+    // the fp16 tile is four times larger: one buffer, occupancy hides latency
+    for (int i = 0; i < n_full; ++i, t0 += kBlk) {
+      Blk<INT4> bb;
+      load_blk<INT4, false>(rows, t0, t_last, n16, kq, bb);
+      process_blk<INT4, false>(st, bb, t0, t_end, kq);
     }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = exp2f(sc[i] - m_run);
-      l_part += p[i];
-    }
-
-    // ---- PV left operand: rows (group, head) for int4, heads for fp16 ----
-    half4_t pa;
-    if (INT4) {
-      const int src = (lane & ~15) | pv_head;     // lane holding head pv_head
-      const int grp = n16 >> 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pi = __shfl(p[i], src, 64);
-        const int64_t t = t0 + 4 * kq + i;
-        float sv = 0.f;
-        if (t < t_end) sv = f16_bits_to_f32(a.v_scales[(row_kv * a.Tcap + t) * 4 + grp]);
-        pa[i] = static_cast<_Float16>(pi * sv);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pa[i] = static_cast<_Float16>(p[i]);
-    }
-
-    // ---- values: lane (n16, kq) reads 8 channels 8 n16 .. 8 n16 + 7 of
-    // tokens 4 kq .. 4 kq + 3; MFMA c takes channel 8 n16 + c ----
-    if (INT4) {
-      uint32_t vw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = t0 + 4 * kq + i;
-        vw[i] = (t < t_end) ? reinterpret_cast<const uint32_t*>(a.v_codes + (row_kv * a.Tcap + t) * 64)[n16]
-                            : 0x88888888u;
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int by = c >> 1;
-        const uint32_t sel = 0x0c000c00u | (static_cast<uint32_t>(4 + by) << 16) | static_cast<uint32_t>(by);
-        uint32_t x01 = __builtin_amdgcn_perm(vw[1], vw[0], sel);
-        uint32_t x23 = __builtin_amdgcn_perm(vw[3], vw[2], sel);
-        if (c & 1) { x01 >>= 4; x23 >>= 4; }
-        const uint32_t h01 = nib_pair_to_f16x2(x01 & 0x000F000Fu);
-        const uint32_t h23 = nib_pair_to_f16x2(x23 & 0x000F000Fu);
-        const half4_t vb = __builtin_bit_cast(half4_t, make_uint2(h01, h23));
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, acc[c], 0, 0, 0);
-      }
-    } else {
-      uint4 vr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = t0 + 4 * kq + i;
-        vr[i] = (t < t_end) ? *reinterpret_cast<const uint4*>(a.v16 + (row_kv * a.Tcap + t) * 128 + 8 * n16)
-                            : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t w0 = (&vr[0].x)[c >> 1], w1 = (&vr[1].x)[c >> 1];
-        const uint32_t w2 = (&vr[2].x)[c >> 1], w3 = (&vr[3].x)[c >> 1];
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t h01 = __builtin_amdgcn_perm(w1, w0, sel);
-        const uint32_t h23 = __builtin_amdgcn_perm(w3, w2, sel);
-        const half4_t vb = __builtin_bit_cast(half4_t, make_uint2(h01, h23));
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, acc[c], 0, 0, 0);
-      }
+    if (t0 < t_end) {
+      Blk<INT4> bb;
+      load_blk<INT4, true>(rows, t0, t_last, n16, kq, bb);
+      process_blk<INT4, true>(st, bb, t0, t_end, kq);
     }
   }
 
   // ---- partial results ----
+  float l_part = st.l_part;
   l_part += shfl_xor(l_part, 16);
   l_part += shfl_xor(l_part, 32);
-  const int64_t ws_base = (b * a.Hq + hq0);
-  if (kq == 0 && n16 < nh) {
+  const int64_t ws_base = b * a.Hq + hq0;
+  if (kq == 0 && n16 < nh) {      // lane n16 = head (group 0 column for int4)
     float* ml = a.part_ml + ((ws_base + n16) * a.S + s) * 2;
-    ml[0] = m_run;
+    ml[0] = st.m_run;
     ml[1] = l_part;
   }
-  // acc[c][i]: row (int4: group kq, head i; fp16: head 4 kq + i), channel 8 n16 + c
+  // acc[c][i]: row block kq (int4: value group kq; fp16: heads 4 kq ..),
+  // head i, channel 8 n16 + c
   const bool useful = INT4 ? (kq == (n16 >> 2)) : (kq == 0);
   if (useful) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i < nh) {
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          v[c] = st.acc[c][i];
+          if (INT4 && (c & 1)) v[c] *= 0.0625f;
+        }
         float* dst = a.part_acc + ((ws_base + i) * a.S + s) * 128 + 8 * n16;
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. combine splits, inverse rotation
+// 3. combine splits, inverse rotation across the wave
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += shfl_xor(x, m);
+  return x;
+}
+
 template <int ROT, int OUT_F32>
 __global__ void __launch_bounds__(64) attn_combine_kernel(AttnArgs a, int int4) {
-  __shared__ float sh[128];
   const int lane = threadIdx.x;
   const int64_t bh = blockIdx.x;
   const int64_t h = bh % a.Hq;
   const int64_t g = h / (a.Hq / a.Hkv);
   const float* ml = a.part_ml + bh * a.S * 2;
-  float m = -INFINITY;
-  for (int64_t s = 0; s < a.S; ++s) m = fmaxf(m, ml[2 * s]);
-  float l = 0.f, x0 = 0.f, x1 = 0.f;
-  for (int64_t s = 0; s < a.S; ++s) {
-    const float ms = ml[2 * s];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - m);
-    l = fmaf(wgt, ml[2 * s + 1], l);
-    const float2 v = *reinterpret_cast<const float2*>(a.part_acc + (bh * a.S + s) * 128 + 2 * lane);
-    x0 = fmaf(wgt, v.x, x0);
-    x1 = fmaf(wgt, v.y, x1);
-  }
-  const float inv = 1.f / l;
-  sh[2 * lane] = x0 * inv;
-  sh[2 * lane + 1] = x1 * inv;
-  __syncthreads();
-  if (lane != 0) return;
+  const float* acc = a.part_acc + bh * a.S * 128 + 2 * lane;
 
-  float v[128];
-  if (int4) {
-    float c = 1.f;
-    if (ROT == KVQ_ROT_SRFT) c = 0.125f;
-    else if (ROT == KVQ_ROT_SRHT) c = 0.0883883476483184405f;
-    const float* lv = a.lambda_v + g * 128;
+  // split maxima and sums, 64 splits per pass (one per lane)
+  float m = -INFINITY;
+  for (int64_t s0 = 0; s0 < a.S; s0 += 64)
+    if (s0 + lane < a.S) m = fmaxf(m, ml[2 * (s0 + lane)]);
+  m = wave_max(m);
+  float l = 0.f, x0 = 0.f, x1 = 0.f;
+  for (int64_t s0 = 0; s0 < a.S; s0 += 64) {
+    const int64_t sl = s0 + lane;
+    const float ms = sl < a.S ? ml[2 * sl] : -INFINITY;
+    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m);
+    if (sl < a.S) l = fmaf(w, ml[2 * sl + 1], l);
+    const int n = static_cast<int>(a.S - s0 < 64 ? a.S - s0 : 64);
+    int j = 0;
+    for (; j + 8 <= n; j += 8) {
+      float2 v[8];
 #pragma unroll
-    for (int j = 0; j < 128; ++j) v[j] = sh[j] * c / lv[j];
-    if (ROT == KVQ_ROT_SRFT) fft64<true>(v);
-    else if (ROT == KVQ_ROT_SRHT) wht128(v);
-  } else {
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float2*>(acc + (s0 + j + u) * 128);
 #pragma unroll
-    for (int j = 0; j < 128; ++j) v[j] = sh[j];
+      for (int u = 0; u < 8; ++u) {
+        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+        x0 = fmaf(wu, v[u].x, x0);
+        x1 = fmaf(wu, v[u].y, x1);
+      }
+    }
+    for (; j < n; ++j) {
+      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+      const float2 v = *reinterpret_cast<const float2*>(acc + (s0 + j) * 128);
+      x0 = fmaf(wu, v.x, x0);
+      x1 = fmaf(wu, v.y, x1);
+    }
   }
+  l = wave_sum(l);
+  const float inv = 1.f / l;
+  x0 *= inv;
+  x1 *= inv;
+
+  int k = lane;              // pair index this lane writes
+  uint32_t neg0 = 0, neg1 = 0;
+  if (int4) {
+    const float* lv = a.lambda_v + g * 128;
+    if (ROT == KVQ_ROT_SRFT) {
+      // Z_lane = (x0 + i x1) / lambda, unitary inverse 64-point DFT across
+      // lanes: radix-2 decimation in frequency, output bit-reversed
+      float re = x0 * (0.125f / lv[2 * lane]);
+      float im = x1 * (0.125f / lv[2 * lane + 1]);
 #pragma unroll
-  for (int k = 0; k < 64; ++k) {
-    const int p = (int4 && ROT == KVQ_ROT_SRFT) ? rev4(k) : k;
-    float lo = v[2 * p], hi = v[2 * p + 1];
-    if (int4 && ROT == KVQ_ROT_SRFT) {
-      if ((a.signs[k >> 6] >> (k & 63)) & 1) { lo = -lo; hi = -hi; }
-    } else if (int4 && ROT == KVQ_ROT_SRHT) {
-      const int i0 = 2 * k, i1 = 2 * k + 1;
-      if ((a.signs[i0 >> 6] >> (i0 & 63)) & 1) lo = -lo;
-      if ((a.signs[i1 >> 6] >> (i1 & 63)) & 1) hi = -hi;
-    }
-    if (OUT_F32) {
-      *reinterpret_cast<float2*>(static_cast<float*>(a.out) + bh * 128 + 2 * k) = make_float2(lo, hi);
+      for (int hh = 32; hh >= 1; hh >>= 1) {
+        const float pr = shfl_xor(re, hh), pi = shfl_xor(im, hh);
+        if (lane & hh) {
+          const float dr = pr - re, di = pi - im;
+          const int e = (lane & (hh - 1)) * (32 / hh);   // exp(+2 pi i e / 64)
+          const float cw = kTw64Const.c[e], sw = kTw64Const.s[e];
+          re = dr * cw - di * sw;
+          im = dr * sw + di * cw;
+        } else {
+          re += pr;
+          im += pi;
+        }
+      }
+      k = bitrev6(lane);
+      x0 = re;
+      x1 = im;
+      neg0 = neg1 = sign_bit(a.signs, k);
+    } else if (ROT == KVQ_ROT_SRHT) {
+      // H_128 on channels 2 lane + e: the stride-1 step inside the lane,
+      // strides 2 .. 64 across lanes
+      float y0 = x0 * (0.0883883476483184405f / lv[2 * lane]);
+      float y1 = x1 * (0.0883883476483184405f / lv[2 * lane + 1]);
+      const float t0 = y0 + y1, t1 = y0 - y1;
+      y0 = t0;
+      y1 = t1;
+#pragma unroll
+      for (int hh = 1; hh <= 32; hh <<= 1) {
+        const float p0 = shfl_xor(y0, hh), p1 = shfl_xor(y1, hh);
+        if (lane & hh) { y0 = p0 - y0; y1 = p1 - y1; }
+        else { y0 += p0; y1 += p1; }
+      }
+      x0 = y0;
+      x1 = y1;
+      neg0 = sign_bit(a.signs, 2 * lane);
+      neg1 = sign_bit(a.signs, 2 * lane + 1);
     } else {
-      static_cast<uint32_t*>(a.out)[bh * 64 + k] = pack_f16x2(lo, hi);
+      x0 /= lv[2 * lane];
+      x1 /= lv[2 * lane + 1];
     }
+  }
+  if (neg0) x0 = -x0;
+  if (neg1) x1 = -x1;
+  if (OUT_F32) {
+    *reinterpret_cast<float2*>(static_cast<float*>(a.out) + bh * 128 + 2 * k) = make_float2(x0, x1);
+  } else {
+    static_cast<uint32_t*>(a.out)[bh * 64 + k] = pack_f16x2(x0, x1);
   }
 }
 
-// Split count: about two waves per CU slot across the whole grid, at least
-// 256 tokens per split.
+// Split count: about 16 waves per CU across the grid, at least 256 tokens
+// per split.
 void split_geometry(int64_t B, int64_t Hq, int64_t Hkv, int64_t seq_len, int64_t& S, int64_t& chunk,
                     int64_t& n_hchunks, int cus) {
   const int64_t rep = Hq / Hkv;
@@ -451,14 +682,14 @@ void split_geometry(int64_t B, int64_t Hq, int64_t Hkv, int64_t seq_len, int64_t
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   chunk = (seq_len + s - 1) / s;
-  chunk = (chunk + kTok - 1) / kTok * kTok;
+  chunk = (chunk + kBlk - 1) / kBlk * kBlk;
   S = (seq_len + chunk - 1) / chunk;
 }
 
 template <int ROT>
 hipError_t run_attention(const AttnDesc& d, AttnArgs& a) {
   const int int4 = d.int4 ? 1 : 0;
-  const unsigned nq = static_cast<unsigned>((d.B * d.Hq + 63) / 64);
+  const unsigned nq = static_cast<unsigned>(d.B * d.Hq);
   hipLaunchKernelGGL((attn_qrot_kernel<ROT>), dim3(nq), dim3(64), 0, d.stream, a, int4);
   const unsigned nsplit = static_cast<unsigned>(d.B * d.Hkv * a.n_hchunks * a.S);
   if (d.int4) {
@@ -475,9 +706,9 @@ hipError_t run_attention(const AttnDesc& d, AttnArgs& a) {
   return hipGetLastError();
 }
 
-// Workspace layout (bytes, 256-aligned sections): qt [B*Hq*128] f32,
-// part_ml [B*Hq*S*2] f32, part_acc [B*Hq*S*128] f32.
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int64_t max_splits(int64_t seq_len) { return (seq_len + 255) / 256 > 0 ? (seq_len + 255) / 256 : 1; }
 
 }  // namespace
 
@@ -487,12 +718,14 @@ int64_t attn_num_splits(int64_t B, int64_t Hkv, int64_t seq_len) {
   return S;
 }
 
+// Workspace layout (256-aligned sections): query records [B*Hq][512 B],
+// (max, sum) [B*Hq][S][2] f32, partial sums [B*Hq][S][128] f32, sized for
+// the largest split count any shape with this seq_len can use.
 size_t attn_workspace_bytes(int D, int64_t B, int64_t Hq, int64_t seq_len) {
   (void)D;
-  // sized for the largest split count any Hkv could produce (Hkv = 1)
-  const int64_t S = (seq_len + 255) / 256 > 0 ? (seq_len + 255) / 256 : 1;
+  const int64_t S = max_splits(seq_len);
   const size_t rows = static_cast<size_t>(B * Hq);
-  return align256(rows * 128 * 4) + align256(rows * S * 2 * 4) + align256(rows * S * 128 * 4);
+  return align256(rows * kQRec) + align256(rows * S * 2 * 4) + align256(rows * S * 128 * 4);
 }
 
 hipError_t launch_attention(const AttnDesc& d) {
@@ -515,13 +748,13 @@ hipError_t launch_attention(const AttnDesc& d) {
   a.sm_scale = d.sm_scale;
   for (int i = 0; i < 4; ++i) a.signs[i] = d.signs[i];
   split_geometry(d.B, d.Hq, d.Hkv, d.seq_len, a.S, a.chunk, a.n_hchunks, device_cu_count());
-  const int64_t max_s = (d.seq_len + 255) / 256 > 0 ? (d.seq_len + 255) / 256 : 1;
-  if (a.S > max_s) return hipErrorInvalidValue;
+  const int64_t ms = max_splits(d.seq_len);
+  if (a.S > ms) return hipErrorInvalidValue;
   const size_t rows = static_cast<size_t>(d.B * d.Hq);
   uint8_t* ws = static_cast<uint8_t*>(d.workspace);
-  a.qt = reinterpret_cast<float*>(ws);
-  a.part_ml = reinterpret_cast<float*>(ws + align256(rows * 128 * 4));
-  a.part_acc = reinterpret_cast<float*>(ws + align256(rows * 128 * 4) + align256(rows * max_s * 2 * 4));
+  a.qrec = ws;
+  a.part_ml = reinterpret_cast<float*>(ws + align256(rows * kQRec));
+  a.part_acc = reinterpret_cast<float*>(ws + align256(rows * kQRec) + align256(rows * ms * 2 * 4));
   switch (d.int4 ? d.rotation : KVQ_ROT_ID) {
     case KVQ_ROT_SRFT: return run_attention<KVQ_ROT_SRFT>(d, a);
     case KVQ_ROT_SRHT: return run_attention<KVQ_ROT_SRHT>(d, a);

@@ -8,8 +8,10 @@ sits within 1e-4 of a rounding boundary:
     a half-integer; in a group whose scale differs, the GPU codes are checked
     against the oracle's w re-quantized with the GPU's scale.
 The mismatch fraction (codes + scales, per element) is reported and must stay
-below 1e-5; on samples too small to resolve 1e-5 at most one boundary
-mismatch is tolerated.
+below 1e-5 on every sample of at least 10^6 elements.  Smaller samples cannot
+resolve a rate of 1e-5 (the expected count is below 10); there every
+mismatch must still be a boundary case and the count may not exceed
+max(1, 3e-5 * elements), three times the expected count at the bar.
 """
 
 from __future__ import annotations
@@ -71,10 +73,12 @@ def compare_codes(codes_gpu, scales_gpu, x16, lam, rotation, signs, G: int = O.G
         assert np.all(code_dist[code_bad] <= BOUNDARY), (
             f"{n_code_bad} code mismatches, max boundary distance {code_dist[code_bad].max():.3e}")
     frac = (n_code_bad + n_scale_bad) / max(n_el, 1)
-    if n_el * FRACTION >= 1:
+    if n_el >= 1_000_000:
         assert frac < FRACTION, f"mismatch fraction {frac:.3e} >= {FRACTION}"
     else:
-        assert n_code_bad + n_scale_bad <= 1, f"{n_code_bad + n_scale_bad} boundary mismatches in {n_el} elements"
+        allowed = max(1, int(3 * FRACTION * n_el))
+        assert n_code_bad + n_scale_bad <= allowed, (
+            f"{n_code_bad + n_scale_bad} boundary mismatches in {n_el} elements (allowed {allowed})")
     return {
         "vectors": N, "elements": n_el,
         "code_mismatch": n_code_bad, "scale_mismatch": n_scale_bad,
