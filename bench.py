@@ -32,6 +32,32 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes of this
+# bench, scaled by what the same counters read for a 512 MiB copy (FETCH_SIZE
+# reads half the bytes fetched, WRITE_SIZE all bytes written).  Valid only for
+# the kernel sources they were taken on (sha256 prefix of the listed files);
+# reported as null once those change.
+TRAFFIC = {
+    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "22555fa1dfde4b8f",
+             "bytes": (111.0 + 296095.1 + 4210.5) * 2 * 1024 + (224.0 + 8709.2 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "ab208ef2cf33cb9d",
+               "bytes": 57703.3 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "ab208ef2cf33cb9d",
+               "bytes": 18287.5 * 2 * 1024 + 118299.2 * 1024},
+}
+
+
+def measured_traffic(which: str):
+    """Counter-measured HBM bytes of one launch, or None if the kernel's
+    sources changed since the counters were taken."""
+    import hashlib
+    t = TRAFFIC[which]
+    h = hashlib.sha256()
+    for f in t["files"]:
+        with open(os.path.join(ROOT, "kv_cache_int4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return round(t["bytes"]) if h.hexdigest()[:16] == t["sha256"] else None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -40,7 +66,75 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=4, help="prefix batches rotated over")
+    ap.add_argument("--profile-marks", action="store_true",
+                    help="bracket the timed steps with marker kernels and add a calibration copy "
+                         "of known size, for --trace-summary of a rocprofv3 run")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarize a rocprofv3 kernel_trace.csv or counter_collection.csv written "
+                         "by a --profile-marks run, then exit")
     return ap.parse_args()
+
+
+CALIB_BYTES = 512 << 20      # calibration copy: 512 MiB read + 512 MiB written
+MARK_CYCLES = 1000           # marker kernel length (torch.cuda._sleep)
+
+
+def trace_summary(path: str) -> str:
+    """Per-kernel rows of the dispatches between the two marker kernels of a
+    --profile-marks run, as a Markdown table.
+
+    A kernel trace gives calls and durations (us) per (kernel, grid); a
+    counter collection gives the mean per dispatch of each counter (FETCH_SIZE
+    and WRITE_SIZE are KiB), and for the calibration copy the ratio of the
+    counter to the bytes it moves."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    if not rows:
+        return "(empty)"
+    key = "Dispatch_Id" if "Dispatch_Id" in rows[0] else "Correlation_Id"
+    rows.sort(key=lambda r: int(r[key]))
+    marks = [i for i, r in enumerate(rows) if "sleep" in r["Kernel_Name"] or "spin" in r["Kernel_Name"]]
+    if len(marks) < 2:
+        raise SystemExit(f"{path}: fewer than two marker dispatches")
+    lo, hi = marks[0], marks[-1]
+    gk = "Grid_Size" if "Grid_Size" in rows[0] else "Grid_Size_X"
+    window = rows[lo + 1:hi]
+    # the calibration copy is the last kernel before the closing marker
+    calib_id = max(int(r[key]) for r in window)
+
+    def short(r):
+        if int(r[key]) == calib_id:
+            return "calibration copy (512 MiB)"
+        n = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+        n = n[5:] if n.startswith("void ") else n
+        return n.split("(")[0].replace("kvq::", "")
+
+    out = []
+    if "Counter_Name" in rows[0]:
+        acc = {}
+        for r in window:
+            k = (short(r), int(r[gk]), r["Counter_Name"])
+            d = acc.setdefault(k, {})
+            d.setdefault(int(r[key]), 0.0)
+            d[int(r[key])] += float(r["Counter_Value"])
+        out.append("| kernel | grid | counter | dispatches | mean per dispatch | calibration ratio |")
+        out.append("|---|---|---|---|---|---|")
+        for (name, grid, ctr), d in sorted(acc.items()):
+            mean = sum(d.values()) / len(d)
+            ratio = ""
+            if name.startswith("calibration") and ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                ratio = f"{mean * 1024 / CALIB_BYTES:.4f}"
+            out.append(f"| {name} | {grid} | {ctr} | {len(d)} | {mean:.1f} | {ratio} |")
+    else:
+        acc = {}
+        for r in window:
+            k = (short(r), int(r[gk]))
+            acc.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        out.append("| kernel | grid (work-items) | calls | avg us | min us | max us |")
+        out.append("|---|---|---|---|---|---|")
+        for (name, grid), v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"| {name} | {grid} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return "\n".join(out)
 
 
 def cpu_baseline(n_vec: int = 458752):
@@ -79,6 +173,9 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the int4 KV-cache path is per-GPU work with no collectives", file=sys.stderr)
@@ -154,6 +251,9 @@ def main():
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    if args.profile_marks:
+        torch.cuda._sleep(MARK_CYCLES)
+        torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(i, events[i])
@@ -179,6 +279,15 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     f16_us = e0.elapsed_time(e1) / n16 * 1e3
+    if args.profile_marks:
+        src = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(MARK_CYCLES)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- algorithmic bytes ----
     enc_bytes = n_vec * (2 * D + D // 2 + 2 * (D // 32))          # 328 B / vector
@@ -196,15 +305,17 @@ def main():
     dom = max(shares, key=shares.get)
     if dom == "attn":
         rl = {"kernel": "kvq_attn_decode (qrot + split-K stream + combine)", "bytes": attn_bytes,
-              "seconds": ms["attn"] / 1e3}
+              "seconds": ms["attn"] / 1e3, "traffic": measured_traffic("attn")}
     elif dom == "encode":
-        rl = {"kernel": "kvq_encode", "bytes": enc_bytes, "seconds": enc_s}
+        rl = {"kernel": "kvq_encode", "bytes": enc_bytes, "seconds": enc_s,
+              "traffic": measured_traffic("encode")}
     else:
-        rl = {"kernel": "kvq_decode", "bytes": enc_bytes, "seconds": dec_s}
+        rl = {"kernel": "kvq_decode", "bytes": enc_bytes, "seconds": dec_s,
+              "traffic": measured_traffic("decode")}
     achieved = rl["bytes"] / rl["seconds"] / 1e9
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": rl["traffic"],
         "kernel": rl["kernel"], "algorithmic_bytes_per_launch": rl["bytes"],
         "avg_launch_us": round(rl["seconds"] * 1e6, 2),
     }
