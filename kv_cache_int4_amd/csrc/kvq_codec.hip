@@ -68,7 +68,7 @@ __host__ __device__ constexpr float rot_scale() {
        : 1.0f;
 }
 
-__device__ __forceinline__ uint32_t sign_bit(const uint64_t (&s)[4], int i) {
+__host__ __device__ __forceinline__ uint32_t sign_bit(const uint64_t (&s)[4], int i) {
   const uint64_t w = i < 64 ? s[0] : i < 128 ? s[1] : i < 192 ? s[2] : s[3];
   return static_cast<uint32_t>(w >> (i & 63)) & 1u;
 }
@@ -77,7 +77,7 @@ __device__ __forceinline__ uint32_t sign_bit(const uint64_t (&s)[4], int i) {
 // signs, plus a negation of the data the second lane of a D=256 vector owns
 // (it lets the cross-lane radix-2 step use one fused multiply-add).
 template <int D, int ROT>
-__device__ __forceinline__ uint32_t word_mask(const uint64_t (&s)[4], int k) {
+__host__ __device__ __forceinline__ uint32_t word_mask(const uint64_t (&s)[4], int k) {
   uint32_t m = 0;
   if (ROT == KVQ_ROT_SRFT) {
     m = sign_bit(s, k) ? 0x80008000u : 0u;
@@ -316,6 +316,277 @@ __global__ void __launch_bounds__(64, 2) encode_kernel(CodecArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// D = 128 encode: one vector per lane, tiles of 64 vectors (16 KiB) brought
+// into LDS by direct global->LDS loads, one tile ahead of the compute.
+// ---------------------------------------------------------------------------
+
+// fp16 + fp16 -> fp32 (or -) with both conversions folded into one
+// v_fma_mix_f32: (+-b_half) * 1.0 + a_half.  SELA / SELB pick the low (0)
+// or high (1) half of each packed word.
+#define KVQ_MIX(NAME, SELA, SELB, NEG)                                                     \
+  __device__ __forceinline__ float NAME(uint32_t a, uint32_t b) {                          \
+    float r;                                                                               \
+    asm("v_fma_mix_f32 %0, " NEG "%1, 1.0, %2 op_sel:[" #SELB ",0," #SELA "] op_sel_hi:[1,0,1]" \
+        : "=v"(r) : "v"(b), "v"(a));                                                       \
+    return r;                                                                              \
+  }
+KVQ_MIX(mix_add_ll, 0, 0, "")
+KVQ_MIX(mix_sub_ll, 0, 0, "-")
+KVQ_MIX(mix_add_hh, 1, 1, "")
+KVQ_MIX(mix_sub_hh, 1, 1, "-")
+KVQ_MIX(mix_add_lh, 0, 1, "")
+KVQ_MIX(mix_sub_lh, 0, 1, "-")
+#undef KVQ_MIX
+
+// Slot i*64 + lane of the LDS tile (16 bytes) receives row 4i + lane/16,
+// chunk (lane%16) ^ (row%16): exactly where blk_off puts it, so the per-lane
+// row reads below are free of bank conflicts.  The lane's byte offset inside
+// a group of four rows depends only on i % 4 (off4, fixed per call); the rest
+// of the address is wave-uniform, so the loads take the scalar-base form.
+// Rows past the tile's end are not loaded (their lanes compute on stale data
+// and store nothing).
+__device__ __forceinline__ void dma_tile128(const CodecArgs& a, const Tile& t, uint8_t* lds, int lane,
+                                            const uint32_t (&off4)[4]) {
+  const char* base = reinterpret_cast<const char*>(a.x + t.b * a.sb + t.h * a.sh + t.t_start * a.st);
+  const int64_t step = 8 * a.st;        // bytes of four rows
+  if (t.nv == 64) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_global_load_lds(base + i * step + off4[i & 3], lds + 1024 * i, 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (4 * i + (lane >> 4) < t.nv)
+        __builtin_amdgcn_global_load_lds(base + i * step + off4[i & 3], lds + 1024 * i, 16, 0, 0);
+  }
+}
+
+// First radix-4 DIF stage of the 64-point transform, straight from the
+// packed fp16 pairs p[k] = (re, im) of z_k.
+__device__ __forceinline__ void dif4_first_packed(const uint32_t (&p)[64], float (&v)[128]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t a = p[j], b = p[j + 16], c = p[j + 32], d = p[j + 48];
+    const float t0r = mix_add_ll(a, c), t0i = mix_add_hh(a, c);
+    const float t1r = mix_sub_ll(a, c), t1i = mix_sub_hh(a, c);
+    const float t2r = mix_add_ll(b, d), t2i = mix_add_hh(b, d);
+    const float t3r = mix_sub_ll(b, d), t3i = mix_sub_hh(b, d);
+    const int i0 = j, i1 = j + 16, i2 = j + 32, i3 = j + 48;
+    v[2 * i0] = t0r + t2r;
+    v[2 * i0 + 1] = t0i + t2i;
+    v[2 * i2] = t0r - t2r;
+    v[2 * i2 + 1] = t0i - t2i;
+    v[2 * i1] = t1r + t3i;
+    v[2 * i1 + 1] = t1i - t3r;
+    v[2 * i3] = t1r - t3i;
+    v[2 * i3 + 1] = t1i + t3r;
+    twiddle<64, false>(v[2 * i1], v[2 * i1 + 1], j);
+    twiddle<64, false>(v[2 * i2], v[2 * i2 + 1], 2 * j);
+    twiddle<64, false>(v[2 * i3], v[2 * i3 + 1], 3 * j);
+  }
+}
+
+// Forward rotation of one packed fp16 vector (signs already applied):
+// result in v with channel j at chan_reg<ROT>(j), unnormalized.
+template <int ROT>
+__device__ __forceinline__ void rotate_packed(const uint32_t (&p)[64], float (&v)[128]) {
+  if (ROT == KVQ_ROT_SRFT) {
+    dif4_first_packed(p, v);
+    dif4_stage<16, false>(v);
+    dif4_stage<4, false>(v);
+  } else if (ROT == KVQ_ROT_SRHT) {
+    // stride-1 butterflies inside each packed word, then the rest
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+      v[2 * k] = mix_add_lh(p[k], p[k]);
+      v[2 * k + 1] = mix_sub_lh(p[k], p[k]);
+    }
+#pragma unroll
+    for (int h = 2; h < 128; h *= 2) {
+#pragma unroll
+      for (int i = 0; i < 128; i += 2 * h) {
+#pragma unroll
+        for (int j = i; j < i + h; ++j) {
+          const float x0 = v[j], x1 = v[j + h];
+          v[j] = x0 + x1;
+          v[j + h] = x0 - x1;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+      v[2 * k] = f16_bits_to_f32(p[k] & 0xFFFFu);
+      v[2 * k + 1] = f16_bits_to_f32(p[k] >> 16);
+    }
+  }
+}
+
+// Codes of one group of 32 channels (16 pair bytes -> 4 words) from w and
+// r = 1 / scale.  Without CLAMP the magic-number rounding alone gives the
+// code: with a normal fp16 scale |w r| <= 7 (1 + 2^-11) (1 + 2^-23) < 7.5.
+template <int ROT, bool CLAMP>
+__device__ __forceinline__ void quant_group(const float (&v)[128], int g, float r, uint32_t* cw) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t by[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 32 * g + 8 * q + 2 * e;
+      uint32_t lo, hi;
+      if (CLAMP) {
+        lo = quant_bits(v[chan_reg<ROT>(j)], r);
+        hi = quant_bits(v[chan_reg<ROT>(j + 1)], r);
+      } else {
+        lo = __builtin_bit_cast(uint32_t, fmaf(v[chan_reg<ROT>(j)], r, kMagic));
+        hi = __builtin_bit_cast(uint32_t, fmaf(v[chan_reg<ROT>(j + 1)], r, kMagic));
+      }
+      by[e] = pair_byte(lo, hi);
+    }
+    cw[q] = pack4(by[0], by[1], by[2], by[3]);
+  }
+}
+
+// LDS of the D=128 kernels: the 16 KiB tile, two lambda rows (the current
+// tile's and the prefetched one's) and the 64 sign masks.
+constexpr int kLdsTile = 16384;
+constexpr int kLdsLam = kLdsTile;            // 2 x 512 B
+constexpr int kLdsMask = kLdsTile + 1024;    // 256 B
+constexpr int kLds128 = kLdsTile + 1024 + 256;
+
+// Sign mask of complex pair k (one fp16 word pair) of a D=128 vector.
+template <int ROT>
+__device__ __forceinline__ uint32_t pair_mask128(const CodecArgs& a, int k) {
+  if (ROT == KVQ_ROT_SRFT) return ((a.signs[0] >> k) & 1u) ? 0x80008000u : 0u;
+  if (ROT == KVQ_ROT_SRHT) {
+    const uint64_t w = k < 32 ? a.signs[0] : a.signs[1];
+    const int i = (2 * k) & 63;
+    return (static_cast<uint32_t>((w >> i) & 1u) << 15) | (static_cast<uint32_t>((w >> (i + 1)) & 1u) << 31);
+  }
+  return 0u;
+}
+
+// The lambda row of a tile (512 B) into LDS: lanes 0..31, 16 bytes each.
+__device__ __forceinline__ void dma_lambda128(const CodecArgs& a, const Tile& t, uint8_t* dst, int lane) {
+  if (lane < 32)
+    __builtin_amdgcn_global_load_lds(a.lambda + t.b * a.lambda_sb + t.h * 128 + 4 * lane, dst, 16, 0, 0);
+}
+
+template <int ROT, int MODE>
+__global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds128];
+  const int lane = threadIdx.x;
+  constexpr float kScale = rot_scale<128, ROT>();
+
+  reinterpret_cast<uint32_t*>(lds + kLdsMask)[lane] = pair_mask128<ROT>(a, lane);
+  uint32_t off4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    off4[i] = static_cast<uint32_t>((lane >> 4) * 2 * a.st + 16 * ((lane & 15) ^ (r & 15)));
+  }
+  int64_t tile = blockIdx.x;
+  if (tile < a.n_tiles) {
+    const Tile t = tile_info<128>(a, tile);
+    dma_tile128(a, t, lds, lane, off4);
+    dma_lambda128(a, t, lds + kLdsLam, lane);
+  }
+  __syncthreads();
+  for (int it = 0; tile < a.n_tiles; tile += gridDim.x, ++it) {
+    const Tile t = tile_info<128>(a, tile);
+    const uint4* masks = reinterpret_cast<const uint4*>(lds + kLdsMask);
+    uint32_t p[64];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint4 w = *reinterpret_cast<const uint4*>(lds + blk_off(lane, j));
+      const uint4 m = masks[j];
+      p[4 * j] = w.x ^ m.x;
+      p[4 * j + 1] = w.y ^ m.y;
+      p[4 * j + 2] = w.z ^ m.z;
+      p[4 * j + 3] = w.w ^ m.w;
+    }
+    // the tile is in registers: the buffer takes the next one
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int64_t nxt = tile + gridDim.x;
+    if (nxt < a.n_tiles) {
+      const Tile tn = tile_info<128>(a, nxt);
+      dma_tile128(a, tn, lds, lane, off4);
+      dma_lambda128(a, tn, lds + kLdsLam + 512 * ((it + 1) & 1), lane);
+    }
+
+    float v[128];
+    rotate_packed<ROT>(p, v);
+    // keep the lambda reads below the transform (they would hold 128
+    // registers across it)
+    asm volatile("" ::: "memory");
+
+    const float4* lam4 = reinterpret_cast<const float4*>(lds + kLdsLam + 512 * (it & 1));
+    const bool valid = lane < t.nv;
+
+    if (MODE == 1) {
+      float* wr = a.w + ((t.row * a.T) + t.t_start + lane) * 128;
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < 128; j += 4) {
+          const float4 l4 = lam4[j / 4];
+          float4 o;
+          o.x = v[chan_reg<ROT>(j)] * l4.x * kScale;
+          o.y = v[chan_reg<ROT>(j + 1)] * l4.y * kScale;
+          o.z = v[chan_reg<ROT>(j + 2)] * l4.z * kScale;
+          o.w = v[chan_reg<ROT>(j + 3)] * l4.w * kScale;
+          *reinterpret_cast<float4*>(wr + j) = o;
+        }
+      }
+    } else {
+      float r[4];
+      uint32_t sc[4];
+      bool tiny = false;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float amax = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 32; jj += 4) {
+          const int j = 32 * g + jj;
+          const float4 l4 = lam4[j / 4];
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float wv = v[chan_reg<ROT>(j + e)] * lv[e];
+            v[chan_reg<ROT>(j + e)] = wv;
+            amax = fmaxf(amax, fabsf(wv));
+          }
+        }
+        // scale = fp16(absmax / 7): the float32 quotient rounded to nearest
+        // even once more to fp16
+        sc[g] = f32_to_f16_bits((amax * kScale) / 7.0f);
+        const float sf = f16_bits_to_f32(sc[g]);
+        r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
+        tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);    // fp16-subnormal scale
+      }
+      uint32_t cw[16];
+      if (__builtin_amdgcn_ballot_w64(tiny && valid) == 0) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) quant_group<ROT, false>(v, g, r[g], cw + 4 * g);
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) quant_group<ROT, true>(v, g, r[g], cw + 4 * g);
+      }
+      if (valid) {
+        const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;   // wave-uniform
+        char* sbase = reinterpret_cast<char*>(a.scales + cell0 * 4);
+        char* cbase = reinterpret_cast<char*>(a.codes + cell0 * 64);
+        *reinterpret_cast<uint2*>(sbase + static_cast<uint32_t>(lane * 8)) =
+            make_uint2(sc[0] | (sc[1] << 16), sc[2] | (sc[3] << 16));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint4*>(cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) =
+              make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Decode
 // ---------------------------------------------------------------------------
 template <int D, int ROT, int OUT_F32>
@@ -504,7 +775,13 @@ hipError_t encode_dispatch(const CodecDesc& d, int mode) {
   a.w = d.w;
   if (a.n_tiles == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
-  if (mode == 0) {
+  if (D == 128) {
+    if (mode == 0) {
+      hipLaunchKernelGGL((encode128_kernel<ROT, 0>), grid, dim3(64), 0, d.stream, a);
+    } else {
+      hipLaunchKernelGGL((encode128_kernel<ROT, 1>), grid, dim3(64), 0, d.stream, a);
+    }
+  } else if (mode == 0) {
     hipLaunchKernelGGL((encode_kernel<D, ROT, 0>), grid, dim3(64), 0, d.stream, a);
   } else {
     hipLaunchKernelGGL((encode_kernel<D, ROT, 1>), grid, dim3(64), 0, d.stream, a);
