@@ -587,6 +587,150 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// D = 128 decode to fp16: codes, scales and the lambda row of the next tile
+// arrive in LDS by direct loads while the current tile computes; the fp16
+// rows leave through an 8 KiB LDS stage, one half-row (64 channels) at a time.
+// ---------------------------------------------------------------------------
+constexpr int kDecCodes = 0;             // 4 KiB: 64 code rows of 64 B, swizzled
+constexpr int kDecScales = 4096;         // 512 B
+constexpr int kDecLam = 4608;            // 512 B
+constexpr int kDecRl = 5120;             // 512 B: unitary scale / lambda
+constexpr int kDecOut = 5632;            // 8 KiB: half rows of 128 B
+constexpr int kLdsDec128 = kDecOut + 8192;
+
+__device__ __forceinline__ void dma_codes128(const CodecArgs& a, const Tile& t, uint8_t* lds, int lane) {
+  const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;
+  const char* cb = reinterpret_cast<const char*>(a.codes_in + cell0 * 64);
+  const char* sb = reinterpret_cast<const char*>(a.scales_in + cell0 * 4);
+  // slot 64 i + lane holds chunk q of vector v, at code_off(v, q)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = 16 * i + (lane >> 2);
+    const int q = (lane & 3) ^ ((v >> 2) & 3);
+    if (v < t.nv)
+      __builtin_amdgcn_global_load_lds(cb + static_cast<uint32_t>(64 * v + 16 * q), lds + kDecCodes + 1024 * i, 16, 0, 0);
+  }
+  // scales: one dword (two scales) per lane and instruction
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (32 * i + (lane >> 1) < t.nv)
+      __builtin_amdgcn_global_load_lds(sb + static_cast<uint32_t>(256 * i + 4 * lane), lds + kDecScales + 256 * i, 4, 0, 0);
+  }
+  if (lane < 32)
+    __builtin_amdgcn_global_load_lds(a.lambda + t.b * a.lambda_sb + t.h * 128 + 4 * lane, lds + kDecLam, 16, 0, 0);
+}
+
+template <int ROT>
+__global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsDec128];
+  const int lane = threadIdx.x;
+  constexpr float kScale = rot_scale<128, ROT>();
+  uint32_t magic;   // fp16 pair (1024, 1024): a register operand for v_and_or
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+  // sign masks of the 16-byte output chunk this lane stores in each half
+  uint4 mk[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int k = 32 * hf + 4 * (lane & 7);
+    mk[hf] = make_uint4(pair_mask128<ROT>(a, k), pair_mask128<ROT>(a, k + 1), pair_mask128<ROT>(a, k + 2),
+                        pair_mask128<ROT>(a, k + 3));
+  }
+  const uint32_t out_lane = static_cast<uint32_t>((lane >> 3) * 2 * a.st + 16 * (lane & 7));
+  const int64_t out_step = 16 * a.st;     // bytes of eight rows
+
+  int64_t tile = blockIdx.x;
+  if (tile < a.n_tiles) dma_codes128(a, tile_info<128>(a, tile), lds, lane);
+  __syncthreads();
+  for (; tile < a.n_tiles; tile += gridDim.x) {
+    const Tile t = tile_info<128>(a, tile);
+    uint32_t cw[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = *reinterpret_cast<const uint4*>(lds + kDecCodes + code_off(lane, q));
+      cw[4 * q] = w.x; cw[4 * q + 1] = w.y; cw[4 * q + 2] = w.z; cw[4 * q + 3] = w.w;
+    }
+    const uint2 s2 = *reinterpret_cast<const uint2*>(lds + kDecScales + 8 * lane);
+    const float l0 = reinterpret_cast<const float*>(lds + kDecLam)[lane];
+    const float l1 = reinterpret_cast<const float*>(lds + kDecLam)[lane + 64];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int64_t nxt = tile + gridDim.x;
+    if (nxt < a.n_tiles) dma_codes128(a, tile_info<128>(a, nxt), lds, lane);
+    reinterpret_cast<float*>(lds + kDecRl)[lane] = kScale * __builtin_amdgcn_rcpf(l0);
+    reinterpret_cast<float*>(lds + kDecRl)[lane + 64] = kScale * __builtin_amdgcn_rcpf(l1);
+    __syncthreads();
+
+    // (n - 8) * scale exactly: the nibble under the exponent of 1024 is the
+    // fp16 number 1024 + n (low nibble of a byte) or 1024 + 16 n (high
+    // nibble); one fma_mix removes the bias.  Then * (unitary scale / lambda).
+    const float4* rl4 = reinterpret_cast<const float4*>(lds + kDecRl);
+    const uint32_t s16[4] = {s2.x & 0xFFFFu, s2.x >> 16, s2.y & 0xFFFFu, s2.y >> 16};
+    float v[128];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // one group's 1/lambda reads at a time (hoisted, they would hold 128
+      // registers)
+      asm volatile("" ::: "memory");
+      const float sg = f16_bits_to_f32(s16[g]);
+      const float m_lo = -1032.f * sg;
+      const float sg16 = sg * 0.0625f;
+      const float m_hi = -72.f * sg;       // -1152 * sg / 16
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t x = cw[4 * g + k], y = x >> 8;
+        const h2_t h0 = __builtin_bit_cast(h2_t, (x & 0x000F000Fu) | magic);   // channels 0, 4
+        const h2_t h1 = __builtin_bit_cast(h2_t, (x & 0x00F000F0u) | magic);   // channels 1, 5
+        const h2_t h2 = __builtin_bit_cast(h2_t, (y & 0x000F000Fu) | magic);   // channels 2, 6
+        const h2_t h3 = __builtin_bit_cast(h2_t, (y & 0x00F000F0u) | magic);   // channels 3, 7
+        const int j = 32 * g + 8 * k;
+        const float4 ra = rl4[j / 4], rb = rl4[j / 4 + 1];
+        v[j] = fmaf(static_cast<float>(h0[0]), sg, m_lo) * ra.x;
+        v[j + 1] = fmaf(static_cast<float>(h1[0]), sg16, m_hi) * ra.y;
+        v[j + 2] = fmaf(static_cast<float>(h2[0]), sg, m_lo) * ra.z;
+        v[j + 3] = fmaf(static_cast<float>(h3[0]), sg16, m_hi) * ra.w;
+        v[j + 4] = fmaf(static_cast<float>(h0[1]), sg, m_lo) * rb.x;
+        v[j + 5] = fmaf(static_cast<float>(h1[1]), sg16, m_hi) * rb.y;
+        v[j + 6] = fmaf(static_cast<float>(h2[1]), sg, m_lo) * rb.z;
+        v[j + 7] = fmaf(static_cast<float>(h3[1]), sg16, m_hi) * rb.w;
+      }
+    }
+
+    if (ROT == KVQ_ROT_SRFT) fft64<true>(v);
+    else if (ROT == KVQ_ROT_SRHT) wht128(v);
+
+    const char* ybase = reinterpret_cast<const char*>(static_cast<uint16_t*>(a.y) + t.b * a.sb + t.h * a.sh +
+                                                      t.t_start * a.st);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      // the lane's 32 pairs of this half: chunk c (pairs 4c..4c+3) of row
+      // `lane` at lane*128 + ((c ^ ((lane >> 1) & 7)) << 4)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 32 * hf + 4 * c + e;
+          const int pp = ROT == KVQ_ROT_SRFT ? rev4(k) : k;
+          wv[e] = pack_f16x2(v[2 * pp], v[2 * pp + 1]);
+        }
+        *reinterpret_cast<uint4*>(lds + kDecOut + lane * 128 + ((c ^ ((lane >> 1) & 7)) << 4)) =
+            make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        uint4 w = *reinterpret_cast<const uint4*>(lds + kDecOut + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+        w.x ^= mk[hf].x; w.y ^= mk[hf].y; w.z ^= mk[hf].z; w.w ^= mk[hf].w;
+        if (r < t.nv) st_stream16(const_cast<char*>(ybase) + i * out_step + hf * 128 + out_lane, w);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Decode
 // ---------------------------------------------------------------------------
 template <int D, int ROT, int OUT_F32>
@@ -798,7 +942,9 @@ hipError_t decode_dispatch(const CodecDesc& d, bool f32) {
   a.y = d.y;
   if (a.n_tiles == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
-  if (f32) {
+  if (D == 128 && !f32) {
+    hipLaunchKernelGGL((decode128_kernel<ROT>), grid, dim3(64), 0, d.stream, a);
+  } else if (f32) {
     hipLaunchKernelGGL((decode_kernel<D, ROT, 1>), grid, dim3(64), 0, d.stream, a);
   } else {
     hipLaunchKernelGGL((decode_kernel<D, ROT, 0>), grid, dim3(64), 0, d.stream, a);
