@@ -447,12 +447,10 @@ __device__ __forceinline__ void quant_group(const float (&v)[128], int g, float 
   }
 }
 
-// LDS of the D=128 kernels: the 16 KiB tile, two lambda rows (the current
-// tile's and the prefetched one's) and the 64 sign masks.
-constexpr int kLdsTile = 16384;
-constexpr int kLdsLam = kLdsTile;            // 2 x 512 B
-constexpr int kLdsMask = kLdsTile + 1024;    // 256 B
-constexpr int kLds128 = kLdsTile + 1024 + 256;
+constexpr int kLdsTile = 16384;              // LDS tile of the D=128 encoder
+
+// Read-only data for scalar loads (the constant address space).
+typedef __attribute__((address_space(4))) const float cfloat;
 
 // Sign mask of complex pair k (one fp16 word pair) of a D=128 vector.
 template <int ROT>
@@ -466,19 +464,16 @@ __device__ __forceinline__ uint32_t pair_mask128(const CodecArgs& a, int k) {
   return 0u;
 }
 
-// The lambda row of a tile (512 B) into LDS: lanes 0..31, 16 bytes each.
-__device__ __forceinline__ void dma_lambda128(const CodecArgs& a, const Tile& t, uint8_t* dst, int lane) {
-  if (lane < 32)
-    __builtin_amdgcn_global_load_lds(a.lambda + t.b * a.lambda_sb + t.h * 128 + 4 * lane, dst, 16, 0, 0);
-}
-
 template <int ROT, int MODE>
 __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds128];
+  // two LDS objects, so that reads of the masks need not wait for the
+  // direct loads into the tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
+  __shared__ __attribute__((aligned(16))) uint32_t mask_lds[64];
   const int lane = threadIdx.x;
   constexpr float kScale = rot_scale<128, ROT>();
 
-  reinterpret_cast<uint32_t*>(lds + kLdsMask)[lane] = pair_mask128<ROT>(a, lane);
+  mask_lds[lane] = pair_mask128<ROT>(a, lane);
   uint32_t off4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -489,12 +484,22 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
   if (tile < a.n_tiles) {
     const Tile t = tile_info<128>(a, tile);
     dma_tile128(a, t, lds, lane, off4);
-    dma_lambda128(a, t, lds + kLdsLam, lane);
   }
   __syncthreads();
-  for (int it = 0; tile < a.n_tiles; tile += gridDim.x, ++it) {
+  // codes and scales of the previous tile, stored only after the next tile's
+  // loads are on their way (so that the wait for those loads at the top of
+  // the loop never waits on fresh stores)
+  uint4 pend_c[4] = {};
+  uint2 pend_s = {};
+  bool pend_valid = false;
+  char* pend_cbase = nullptr;
+  char* pend_sbase = nullptr;
+  for (; tile < a.n_tiles; tile += gridDim.x) {
     const Tile t = tile_info<128>(a, tile);
-    const uint4* masks = reinterpret_cast<const uint4*>(lds + kLdsMask);
+    // the tile's direct loads have landed in LDS (everything issued after
+    // them is a store of the tile before, a transform ago)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint4* masks = reinterpret_cast<const uint4*>(mask_lds);
     uint32_t p[64];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -508,19 +513,20 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
     // the tile is in registers: the buffer takes the next one
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t nxt = tile + gridDim.x;
-    if (nxt < a.n_tiles) {
-      const Tile tn = tile_info<128>(a, nxt);
-      dma_tile128(a, tn, lds, lane, off4);
-      dma_lambda128(a, tn, lds + kLdsLam + 512 * ((it + 1) & 1), lane);
+    if (nxt < a.n_tiles) dma_tile128(a, tile_info<128>(a, nxt), lds, lane, off4);
+    if (MODE == 0 && pend_valid) {
+      *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint4*>(pend_cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) = pend_c[q];
     }
 
     float v[128];
     rotate_packed<ROT>(p, v);
-    // keep the lambda reads below the transform (they would hold 128
-    // registers across it)
+    // lambda of the row: scalar loads (read-only for the kernel), one group
+    // at a time so that they stay out of the transform's register budget
     asm volatile("" ::: "memory");
-
-    const float4* lam4 = reinterpret_cast<const float4*>(lds + kLdsLam + 512 * (it & 1));
+    const cfloat* lam = (const cfloat*)(a.lambda + t.b * a.lambda_sb + t.h * 128);
     const bool valid = lane < t.nv;
 
     if (MODE == 1) {
@@ -528,12 +534,11 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
       if (valid) {
 #pragma unroll
         for (int j = 0; j < 128; j += 4) {
-          const float4 l4 = lam4[j / 4];
           float4 o;
-          o.x = v[chan_reg<ROT>(j)] * l4.x * kScale;
-          o.y = v[chan_reg<ROT>(j + 1)] * l4.y * kScale;
-          o.z = v[chan_reg<ROT>(j + 2)] * l4.z * kScale;
-          o.w = v[chan_reg<ROT>(j + 3)] * l4.w * kScale;
+          o.x = v[chan_reg<ROT>(j)] * lam[j] * kScale;
+          o.y = v[chan_reg<ROT>(j + 1)] * lam[j + 1] * kScale;
+          o.z = v[chan_reg<ROT>(j + 2)] * lam[j + 2] * kScale;
+          o.w = v[chan_reg<ROT>(j + 3)] * lam[j + 3] * kScale;
           *reinterpret_cast<float4*>(wr + j) = o;
         }
       }
@@ -543,18 +548,14 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
       bool tiny = false;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        asm volatile("" ::: "memory");
         float amax = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 32; jj += 4) {
+        for (int jj = 0; jj < 32; ++jj) {
           const int j = 32 * g + jj;
-          const float4 l4 = lam4[j / 4];
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float wv = v[chan_reg<ROT>(j + e)] * lv[e];
-            v[chan_reg<ROT>(j + e)] = wv;
-            amax = fmaxf(amax, fabsf(wv));
-          }
+          const float wv = v[chan_reg<ROT>(j)] * lam[j];
+          v[chan_reg<ROT>(j)] = wv;
+          amax = fmaxf(amax, fabsf(wv));
         }
         // scale = fp16(absmax / 7): the float32 quotient rounded to nearest
         // even once more to fp16
@@ -571,32 +572,39 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) quant_group<ROT, true>(v, g, r[g], cw + 4 * g);
       }
-      if (valid) {
-        const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;   // wave-uniform
-        char* sbase = reinterpret_cast<char*>(a.scales + cell0 * 4);
-        char* cbase = reinterpret_cast<char*>(a.codes + cell0 * 64);
-        *reinterpret_cast<uint2*>(sbase + static_cast<uint32_t>(lane * 8)) =
-            make_uint2(sc[0] | (sc[1] << 16), sc[2] | (sc[3] << 16));
+      const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;   // wave-uniform
+      pend_sbase = reinterpret_cast<char*>(a.scales + cell0 * 4);
+      pend_cbase = reinterpret_cast<char*>(a.codes + cell0 * 64);
+      pend_s = make_uint2(sc[0] | (sc[1] << 16), sc[2] | (sc[3] << 16));
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<uint4*>(cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) =
-              make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
-      }
+      for (int q = 0; q < 4; ++q) pend_c[q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+      pend_valid = valid;
     }
+  }
+  if (MODE == 0 && pend_valid) {
+    *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(pend_cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) = pend_c[q];
   }
 }
 
 // ---------------------------------------------------------------------------
 // D = 128 decode to fp16: codes, scales and the lambda row of the next tile
 // arrive in LDS by direct loads while the current tile computes; the fp16
-// rows leave through an 8 KiB LDS stage, one half-row (64 channels) at a time.
+// rows leave through a 9 KiB LDS stage, one half-row (64 channels) at a time.
 // ---------------------------------------------------------------------------
+// Direct-load targets (one LDS object) ...
 constexpr int kDecCodes = 0;             // 4 KiB: 64 code rows of 64 B, swizzled
 constexpr int kDecScales = 4096;         // 512 B
 constexpr int kDecLam = 4608;            // 512 B
-constexpr int kDecRl = 5120;             // 512 B: unitary scale / lambda
-constexpr int kDecOut = 5632;            // 8 KiB: half rows of 128 B
-constexpr int kLdsDec128 = kDecOut + 8192;
+constexpr int kLdsDecIn = 5120;
+// ... and the LDS the compute phase uses (another object, so that its reads
+// need not wait for the direct loads in flight)
+constexpr int kDecRl = 0;                // 512 B: unitary scale / lambda
+constexpr int kDecOut = 512;             // 9 KiB: half rows of 128 B at a 144 B pitch
+constexpr int kDecPitch = 144;           // 16 B of padding: conflict-free both ways
+constexpr int kLdsDecWork = kDecOut + 64 * kDecPitch;
 
 __device__ __forceinline__ void dma_codes128(const CodecArgs& a, const Tile& t, uint8_t* lds, int lane) {
   const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;
@@ -620,23 +628,22 @@ __device__ __forceinline__ void dma_codes128(const CodecArgs& a, const Tile& t, 
     __builtin_amdgcn_global_load_lds(a.lambda + t.b * a.lambda_sb + t.h * 128 + 4 * lane, lds + kDecLam, 16, 0, 0);
 }
 
+// The kernels of this file run one wave per workgroup, and a wave's LDS
+// operations complete in order: lanes see each other's LDS writes once the
+// wave's own LDS counter drains.  (A workgroup barrier would also wait for
+// the vector-memory counter, i.e. for the next tile's direct loads.)
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 template <int ROT>
 __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
   typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsDec128];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsDecIn];
+  __shared__ __attribute__((aligned(16))) uint8_t work[kLdsDecWork];
   const int lane = threadIdx.x;
   constexpr float kScale = rot_scale<128, ROT>();
   uint32_t magic;   // fp16 pair (1024, 1024): a register operand for v_and_or
   asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-  // sign masks of the 16-byte output chunk this lane stores in each half
-  uint4 mk[2];
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int k = 32 * hf + 4 * (lane & 7);
-    mk[hf] = make_uint4(pair_mask128<ROT>(a, k), pair_mask128<ROT>(a, k + 1), pair_mask128<ROT>(a, k + 2),
-                        pair_mask128<ROT>(a, k + 3));
-  }
   const uint32_t out_lane = static_cast<uint32_t>((lane >> 3) * 2 * a.st + 16 * (lane & 7));
   const int64_t out_step = 16 * a.st;     // bytes of eight rows
 
@@ -657,14 +664,14 @@ __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t nxt = tile + gridDim.x;
     if (nxt < a.n_tiles) dma_codes128(a, tile_info<128>(a, nxt), lds, lane);
-    reinterpret_cast<float*>(lds + kDecRl)[lane] = kScale * __builtin_amdgcn_rcpf(l0);
-    reinterpret_cast<float*>(lds + kDecRl)[lane + 64] = kScale * __builtin_amdgcn_rcpf(l1);
-    __syncthreads();
+    reinterpret_cast<float*>(work + kDecRl)[lane] = kScale * __builtin_amdgcn_rcpf(l0);
+    reinterpret_cast<float*>(work + kDecRl)[lane + 64] = kScale * __builtin_amdgcn_rcpf(l1);
+    lds_sync();
 
     // (n - 8) * scale exactly: the nibble under the exponent of 1024 is the
     // fp16 number 1024 + n (low nibble of a byte) or 1024 + 16 n (high
     // nibble); one fma_mix removes the bias.  Then * (unitary scale / lambda).
-    const float4* rl4 = reinterpret_cast<const float4*>(lds + kDecRl);
+    const float4* rl4 = reinterpret_cast<const float4*>(work + kDecRl);
     const uint32_t s16[4] = {s2.x & 0xFFFFu, s2.x >> 16, s2.y & 0xFFFFu, s2.y >> 16};
     float v[128];
 #pragma unroll
@@ -698,13 +705,18 @@ __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
 
     if (ROT == KVQ_ROT_SRFT) fft64<true>(v);
     else if (ROT == KVQ_ROT_SRHT) wht128(v);
+    // the next tile's direct loads (the only vector-memory operations issued
+    // since the last stores) have had the dequantization and the transform
+    // to land; waiting here rather than at the top of the loop keeps this
+    // tile's stores out of the wait
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     const char* ybase = reinterpret_cast<const char*>(static_cast<uint16_t*>(a.y) + t.b * a.sb + t.h * a.sh +
                                                       t.t_start * a.st);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       // the lane's 32 pairs of this half: chunk c (pairs 4c..4c+3) of row
-      // `lane` at lane*128 + ((c ^ ((lane >> 1) & 7)) << 4)
+      // `lane` at lane * 144 + 16 c
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         uint32_t wv[4];
@@ -714,18 +726,21 @@ __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
           const int pp = ROT == KVQ_ROT_SRFT ? rev4(k) : k;
           wv[e] = pack_f16x2(v[2 * pp], v[2 * pp + 1]);
         }
-        *reinterpret_cast<uint4*>(lds + kDecOut + lane * 128 + ((c ^ ((lane >> 1) & 7)) << 4)) =
-            make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        *reinterpret_cast<uint4*>(work + kDecOut + lane * kDecPitch + 16 * c) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
-      __syncthreads();
+      lds_sync();
+      // signs of the 16-byte chunk this lane stores (pairs 32 hf + 4 (lane % 8) ..)
+      const int k0 = 32 * hf + 4 * (lane & 7);
+      const uint4 mk = make_uint4(pair_mask128<ROT>(a, k0), pair_mask128<ROT>(a, k0 + 1),
+                                  pair_mask128<ROT>(a, k0 + 2), pair_mask128<ROT>(a, k0 + 3));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 8 * i + (lane >> 3), c = lane & 7;
-        uint4 w = *reinterpret_cast<const uint4*>(lds + kDecOut + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-        w.x ^= mk[hf].x; w.y ^= mk[hf].y; w.z ^= mk[hf].z; w.w ^= mk[hf].w;
+        uint4 w = *reinterpret_cast<const uint4*>(work + kDecOut + r * kDecPitch + 16 * c);
+        w.x ^= mk.x; w.y ^= mk.y; w.z ^= mk.z; w.w ^= mk.w;
         if (r < t.nv) st_stream16(const_cast<char*>(ybase) + i * out_step + hf * 128 + out_lane, w);
       }
-      __syncthreads();
+      lds_sync();
     }
   }
 }
