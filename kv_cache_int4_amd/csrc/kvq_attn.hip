@@ -405,6 +405,189 @@ __device__ __forceinline__ void process_blk(State<INT4>& st, const Blk<INT4>& cu
   }
 }
 
+// ---- int4 cache: block loads at wave-uniform bases ----
+// Lane (n16, kq), n16 = 4 g + h: QK column (value/key group g, head h); its
+// scores are those of tokens 16 sb + 4 kq + i (i < 4).
+struct Blk4 {
+  uint4 k[2];          // 16 code bytes of token 16 sb + n16, channels 32 kq ..
+  uint32_t v[2][4];    // code dword n16 of token 16 sb + 4 kq + i
+  uint32_t ks[2];      // key scale (fp16) of token 16 sb + 4 kq + h, group g
+  uint32_t vs[2];      // value scale of the same token and group
+};
+
+// Lane byte offsets of a full block's loads, from the block's first token.
+struct Off4 {
+  uint32_t k, v, s;
+};
+
+__device__ __forceinline__ Off4 lane_offsets4(uint32_t n16, uint32_t kq) {
+  Off4 o;
+  o.k = (n16 << 6) + (kq << 4);
+  o.v = (kq << 8) + (n16 << 2);
+  o.s = ((4 * kq + (n16 & 3)) << 3) + ((n16 >> 2) << 1);
+  return o;
+}
+
+// *(T*)(base + off + imm): base wave-uniform, off a 32-bit lane offset, imm a
+// constant the load instruction carries.
+template <typename T>
+__device__ __forceinline__ T ldi(const uint8_t* base, uint32_t off, int imm) {
+  return *reinterpret_cast<const T*>(base + off + imm);
+}
+
+// Loads of the block starting at token t0.  In a tail block the positions
+// past t_last re-read token t_last (their scores are masked).
+template <bool TAIL>
+__device__ __forceinline__ void load4(const Rows& r, uint32_t t0, uint32_t t_last, const Off4& o, uint32_t n16,
+                                      uint32_t kq, Blk4& b) {
+  const uint8_t* kc = r.kc + static_cast<size_t>(t0) * 64;
+  const uint8_t* vc = r.vc + static_cast<size_t>(t0) * 64;
+  const uint8_t* ksc = reinterpret_cast<const uint8_t*>(r.ksc) + static_cast<size_t>(t0) * 8;
+  const uint8_t* vsc = reinterpret_cast<const uint8_t*>(r.vsc) + static_cast<size_t>(t0) * 8;
+  if (!TAIL) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      b.k[sb] = ldi<uint4>(kc, o.k, 1024 * sb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b.v[sb][i] = ldi<uint32_t>(vc, o.v, 64 * (16 * sb + i));
+      b.ks[sb] = ldi<uint16_t>(ksc, o.s, 128 * sb);
+      b.vs[sb] = ldi<uint16_t>(vsc, o.s, 128 * sb);
+    }
+  } else {
+    const uint32_t last = t_last - t0;
+#pragma unroll
+    for (uint32_t sb = 0; sb < 2; ++sb) {
+      const uint32_t tk = min(16 * sb + n16, last);
+      b.k[sb] = ldi<uint4>(kc, (tk << 6) + (kq << 4), 0);
+#pragma unroll
+      for (uint32_t i = 0; i < 4; ++i) {
+        const uint32_t t = min(16 * sb + 4 * kq + i, last);
+        b.v[sb][i] = ldi<uint32_t>(vc, (t << 6) + (n16 << 2), 0);
+      }
+      const uint32_t ts = min(16 * sb + 4 * kq + (n16 & 3), last);
+      b.ks[sb] = ldi<uint16_t>(ksc, (ts << 3) + ((n16 >> 2) << 1), 0);
+      b.vs[sb] = ldi<uint16_t>(vsc, (ts << 3) + ((n16 >> 2) << 1), 0);
+    }
+  }
+}
+
+// x of lane 4 (l / 4) + I: the value of quad position I, to every lane of
+// the quad (DPP quad_perm [I, I, I, I]).
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), I * 0x55, 0xF, 0xF, true));
+}
+
+template <bool TAIL>
+__device__ __forceinline__ void process4(State<true>& st, const Blk4& cur, uint32_t t0, uint32_t t_end, uint32_t kq,
+                                         uint32_t mag_lo, uint32_t mag_hi) {
+  // ---- scores ----
+  float sc[2][4];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const uint4 w = cur.k[sb];
+    // unsigned nibbles as int8: k-step 0 = even channels, 1 = odd channels
+    const int4_t a0 = (int4_t){static_cast<int>(w.x & 0x0F0F0F0Fu), static_cast<int>(w.y & 0x0F0F0F0Fu),
+                               static_cast<int>(w.z & 0x0F0F0F0Fu), static_cast<int>(w.w & 0x0F0F0F0Fu)};
+    const int4_t a1 = (int4_t){static_cast<int>((w.x >> 4) & 0x0F0F0F0Fu), static_cast<int>((w.y >> 4) & 0x0F0F0F0Fu),
+                               static_cast<int>((w.z >> 4) & 0x0F0F0F0Fu), static_cast<int>((w.w >> 4) & 0x0F0F0F0Fu)};
+    int4_t c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[0][0], st.corr[0], 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[0][1], c1, 0, 0, 0);
+    int4_t c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[1][0], st.corr[1], 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[1][1], c2, 0, 0, 0);
+    int4_t c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[2][0], st.corr[2], 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[2][1], c3, 0, 0, 0);
+    // key scale of token i: loaded by quad position i (same group, head i)
+    const float ksf = f16_bits_to_f32(cur.ks[sb]);
+    const float ks4[4] = {quad_bcast<0>(ksf), quad_bcast<1>(ksf), quad_bcast<2>(ksf), quad_bcast<3>(ksf)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // 256 c1 + c2 is exact in int32; the third limb joins in fp32; sfac is
+      // this column's query scale
+      float x = fmaf(static_cast<float>(c1[i] * 256 + c2[i]), 256.f, static_cast<float>(c3[i])) * st.sfac * ks4[i];
+      x = add_row_ror<8>(x);     // + group (g + 2) mod 4
+      x = add_row_ror<4>(x);     // + groups (g + 1), (g + 3)
+      sc[sb][i] = x;
+    }
+    if (TAIL) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (t0 + 16 * sb + 4 * kq + i >= t_end) sc[sb][i] = -INFINITY;
+    }
+  }
+
+  // ---- online softmax (base 2, exact running max) ----
+  float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  bm = fmaxf(bm, shfl_xor(bm, 16));
+  bm = fmaxf(bm, shfl_xor(bm, 32));
+  if (__builtin_amdgcn_ballot_w64(bm > st.m_run) != 0) {
+    const float m_new = fmaxf(st.m_run, bm);
+    const float alpha = (st.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+    st.l_part *= alpha;
+    st.m_run = m_new;
+    // PV rows (value group kq, head i) scale by the factor of head i (lane i)
+    float al[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      al[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st.acc[c][i] *= al[i];
+    }
+  }
+
+  // ---- PV left operand: p times the value scale of group g, hi + lo ----
+  half8_t pa_hi, pa_lo;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    const float vsf = f16_bits_to_f32(cur.vs[sb]);
+    const float vs4[4] = {quad_bcast<0>(vsf), quad_bcast<1>(vsf), quad_bcast<2>(vsf), quad_bcast<3>(vsf)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(sc[sb][i] - st.m_run);
+      st.l_part += p;
+      const float w = p * vs4[i];
+      const _Float16 hi = static_cast<_Float16>(w);
+      pa_hi[4 * sb + i] = hi;
+      pa_lo[4 * sb + i] = static_cast<_Float16>(w - static_cast<float>(hi));
+    }
+  }
+
+  // ---- PV: MFMA c takes channel 8 n16 + c; k slot 4 sb + i <-> token.
+  // A nibble masked under a biased exponent is an exact fp16 number: the
+  // low nibble under 1024 (unit in bit 0) gives 1024 + n, the high nibble
+  // under 64 (unit in bit 4) gives 64 + n; one packed subtraction leaves
+  // n - 8.  (Products of two fp16 subnormals, which a nibble masked in place
+  // would be, do not keep their full value in the matrix unit's fp32 sums.)
+  const half2_t off_lo = {static_cast<_Float16>(-1032.f), static_cast<_Float16>(-1032.f)};
+  const half2_t off_hi = {static_cast<_Float16>(-72.f), static_cast<_Float16>(-72.f)};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t hv[4];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const int by = c >> 1;
+        const uint32_t sel = 0x0c000c00u | (static_cast<uint32_t>(4 + by) << 16) | static_cast<uint32_t>(by);
+        const uint32_t x = __builtin_amdgcn_perm(cur.v[sb][2 * pr + 1], cur.v[sb][2 * pr], sel);
+        const uint32_t biased = (c & 1) ? ((x & 0x00F000F0u) | mag_hi) : ((x & 0x000F000Fu) | mag_lo);
+        hv[2 * sb + pr] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, biased) + ((c & 1) ? off_hi : off_lo));
+      }
+    }
+    const half8_t vb = __builtin_bit_cast(half8_t, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb, st.acc[c], 0, 0, 0);
+    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_lo, vb, st.acc[c], 0, 0, 0);
+  }
+}
+
+// Waves per CU the split geometry targets: the int4 kernel holds two waves
+// per SIMD (up to 256 registers), the fp16 one four.
+constexpr int kWavesPerCuInt4 = 16;
+constexpr int kWavesPerCuF16 = 16;
+
 template <bool INT4>
 __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
   const int lane = threadIdx.x;
@@ -482,28 +665,47 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
   const int n_full = static_cast<int>((t_end - t_begin) / kBlk);   // blocks entirely inside
   uint32_t t0 = t_begin;
   if (INT4) {
-    // ping-pong: the next block streams in while this one is processed
-    Blk<INT4> b0, b1;
-    if (n_full > 0) load_blk<INT4, false>(rows, t0, t_last, n16, kq, b0);
-    for (int i = 0; i < n_full; i += 2) {
-      // b0 holds block i
-      if (i + 1 < n_full) load_blk<INT4, false>(rows, t0 + kBlk, t_last, n16, kq, b1);
-      else if (t0 + kBlk < t_end) load_blk<INT4, true>(rows, t0 + kBlk, t_last, n16, kq, b1);
-      process_blk<INT4, false>(st, b0, t0, t_end, kq);
-      t0 += kBlk;
-      if (i + 1 >= n_full) break;
-      // b1 holds block i + 1
-      if (i + 2 < n_full) load_blk<INT4, false>(rows, t0 + kBlk, t_last, n16, kq, b0);
-      else if (t0 + kBlk < t_end) load_blk<INT4, true>(rows, t0 + kBlk, t_last, n16, kq, b0);
-      process_blk<INT4, false>(st, b1, t0, t_end, kq);
-      t0 += kBlk;
-    }
-    if (t0 < t_end) {
-      // the partial block: already in b1 (odd n_full) or b0 (even n_full > 0),
-      // or not loaded yet (n_full == 0)
-      if (n_full == 0) load_blk<INT4, true>(rows, t0, t_last, n16, kq, b0);
-      if (n_full & 1) process_blk<INT4, true>(st, b1, t0, t_end, kq);
-      else process_blk<INT4, true>(st, b0, t0, t_end, kq);
+    // ping-pong without copies: the next block streams in while this one is
+    // processed; bases are wave-uniform, lane offsets fixed
+    uint32_t mag_lo, mag_hi;     // fp16 pairs (1024, 1024), (64, 64) as v_and_or operands
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(mag_lo));
+    asm("v_mov_b32 %0, 0x54005400" : "=v"(mag_hi));
+    const Off4 o4 = lane_offsets4(n16, kq);
+    const bool has_tail = ((t_end - t_begin) % kBlk) != 0;
+    State<true>& s4 = reinterpret_cast<State<true>&>(st);
+    Blk4 b0, b1;
+    if (n_full == 0) {
+      if (has_tail) {
+        load4<true>(rows, t0, t_last, o4, n16, kq, b0);
+        process4<true>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+      }
+    } else {
+      load4<false>(rows, t0, t_last, o4, n16, kq, b0);
+      // b0 holds block i at the top; blocks i + 1 and i + 2 are full
+      int i = 0;
+      for (; i + 2 < n_full; i += 2) {
+        load4<false>(rows, t0 + kBlk, t_last, o4, n16, kq, b1);
+        process4<false>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+        t0 += kBlk;
+        load4<false>(rows, t0 + kBlk, t_last, o4, n16, kq, b0);
+        process4<false>(s4, b1, t0, t_end, kq, mag_lo, mag_hi);
+        t0 += kBlk;
+      }
+      // one or two full blocks left, then maybe the tail
+      if (n_full - i == 2) {
+        load4<false>(rows, t0 + kBlk, t_last, o4, n16, kq, b1);
+        process4<false>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+        t0 += kBlk;
+        if (has_tail) load4<true>(rows, t0 + kBlk, t_last, o4, n16, kq, b0);
+        process4<false>(s4, b1, t0, t_end, kq, mag_lo, mag_hi);
+        t0 += kBlk;
+        if (has_tail) process4<true>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+      } else {
+        if (has_tail) load4<true>(rows, t0 + kBlk, t_last, o4, n16, kq, b1);
+        process4<false>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+        t0 += kBlk;
+        if (has_tail) process4<true>(s4, b1, t0, t_end, kq, mag_lo, mag_hi);
+      }
     }
   } else {
     // the fp16 tile is four times larger: one buffer, occupancy hides latency
@@ -540,7 +742,6 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           v[c] = st.acc[c][i];
-          if (INT4 && (c & 1)) v[c] *= 0.0625f;
         }
         float* dst = a.part_acc + ((ws_base + i) * a.S + s) * 128 + 8 * n16;
         *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
@@ -669,14 +870,14 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnArgs a, int int4) 
   }
 }
 
-// Split count: about 16 waves per CU across the grid, at least 256 tokens
-// per split.
+// Split count: one round of the waves a CU holds at once (waves_per_cu),
+// at least 256 tokens per split.
 void split_geometry(int64_t B, int64_t Hq, int64_t Hkv, int64_t seq_len, int64_t& S, int64_t& chunk,
-                    int64_t& n_hchunks, int cus) {
+                    int64_t& n_hchunks, int cus, int waves_per_cu) {
   const int64_t rep = Hq / Hkv;
   n_hchunks = (rep + kHeadsPerWave - 1) / kHeadsPerWave;
   const int64_t units = B * Hkv * n_hchunks;
-  const int64_t target = static_cast<int64_t>(cus) * 16;
+  const int64_t target = static_cast<int64_t>(cus) * waves_per_cu;
   int64_t s = units > 0 ? (target + units - 1) / units : 1;
   const int64_t max_s = (seq_len + 255) / 256;
   if (s > max_s) s = max_s;
@@ -714,7 +915,7 @@ int64_t max_splits(int64_t seq_len) { return (seq_len + 255) / 256 > 0 ? (seq_le
 
 int64_t attn_num_splits(int64_t B, int64_t Hkv, int64_t seq_len) {
   int64_t S, chunk, nh;
-  split_geometry(B, Hkv * 4, Hkv, seq_len, S, chunk, nh, device_cu_count());
+  split_geometry(B, Hkv * 4, Hkv, seq_len, S, chunk, nh, device_cu_count(), kWavesPerCuInt4);
   return S;
 }
 
@@ -747,7 +948,8 @@ hipError_t launch_attention(const AttnDesc& d) {
   a.seq_len = d.seq_len;
   a.sm_scale = d.sm_scale;
   for (int i = 0; i < 4; ++i) a.signs[i] = d.signs[i];
-  split_geometry(d.B, d.Hq, d.Hkv, d.seq_len, a.S, a.chunk, a.n_hchunks, device_cu_count());
+  split_geometry(d.B, d.Hq, d.Hkv, d.seq_len, a.S, a.chunk, a.n_hchunks, device_cu_count(),
+                 d.int4 ? kWavesPerCuInt4 : kWavesPerCuF16);
   const int64_t ms = max_splits(d.seq_len);
   if (a.S > ms) return hipErrorInvalidValue;
   const size_t rows = static_cast<size_t>(d.B * d.Hq);
