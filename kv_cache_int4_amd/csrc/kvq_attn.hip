@@ -97,6 +97,22 @@ __device__ __forceinline__ uint32_t sign_bit(const uint64_t (&s)[4], int i) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Maximum of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows):
+// v_permlane16_swap / v_permlane32_swap exchange rows inside the VALU, so
+// each step leaves the pair (x[l], x[l ^ 16]) (then ^ 32) in its two
+// registers.  Written as assembly: the compiler folds the max of the two
+// results of its swap intrinsics down to one of them.  The s_nop covers the
+// VALU write of the operands just before the swap.
+__device__ __forceinline__ float max_over_rows(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  x = fmaxf(a, b);
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 __device__ __forceinline__ int bitrev6(int x) {
   return static_cast<int>(__builtin_bitreverse32(static_cast<uint32_t>(x)) >> 26);
 }
@@ -337,8 +353,7 @@ __device__ __forceinline__ void process_blk(State<INT4>& st, const Blk<INT4>& cu
   // ---- online softmax (base 2, exact running max) ----
   float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                    fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-  bm = fmaxf(bm, shfl_xor(bm, 16));
-  bm = fmaxf(bm, shfl_xor(bm, 32));
+  bm = max_over_rows(bm);
   if (__builtin_amdgcn_ballot_w64(bm > st.m_run) != 0) {
     const float m_new = fmaxf(st.m_run, bm);
     const float alpha = (st.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
@@ -519,8 +534,7 @@ __device__ __forceinline__ void process4(State<true>& st, const Blk4& cur, uint3
   // ---- online softmax (base 2, exact running max) ----
   float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                    fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-  bm = fmaxf(bm, shfl_xor(bm, 16));
-  bm = fmaxf(bm, shfl_xor(bm, 32));
+  bm = max_over_rows(bm);
   if (__builtin_amdgcn_ballot_w64(bm > st.m_run) != 0) {
     const float m_new = fmaxf(st.m_run, bm);
     const float alpha = (st.m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
