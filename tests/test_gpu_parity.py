@@ -306,6 +306,46 @@ def test_attention_small(rot, Hq, Hkv, L):
     say(f"   fp16 comparator: rel err {worst:.2e}")
 
 
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+def test_attention_dominant_token(rot):
+    """A token whose score exceeds every other by far more than exp2's range
+    (about 150 in log2 units): the softmax must take its maximum over every
+    row of the block and every split, else exp2 overflows.  The dominant
+    tokens sit in rows 1, 2 and 3 of a block, in the tail block and in a
+    later split; the output is then (nearly) that token's value vector."""
+    D, B, Hq, Hkv = 128, 2, 8, 2
+    L = 2051
+    Tcap = L + 5
+    plan = K.Plan(D, 32, rot, 57)
+    say(f"[attn-dominant] rot={rot} L={L}")
+    k16, v16, lam_k, lam_v, q = W.decode_inputs(B, Hkv, Hq, Tcap, D, 23, "cuda")
+    rep = Hq // Hkv
+    # (b, query head, dominant token)
+    spots = [(0, 0, 5), (0, 3, 1000 + 32 + 12 + 3), (1, 5, L - 1), (1, 6, 300 + 16 + 8), (1, 1, 1601)]
+    for b, h, t in spots:
+        qv = q[b, h].float()
+        c = 1200.0 / float((qv * qv).sum())
+        k16[b, h // rep, t] = (c * qv).to(torch.float16)
+    kc = torch.empty((B, Hkv, Tcap, D // 2), dtype=torch.uint8, device="cuda")
+    ksc = torch.empty((B, Hkv, Tcap, D // 32), dtype=torch.float16, device="cuda")
+    vc, vsc = torch.empty_like(kc), torch.empty_like(ksc)
+    K.encode(plan, k16[:, :, :L], lam_k, kc, ksc, 0)
+    K.encode(plan, v16[:, :, :L], lam_v, vc, vsc, 0)
+    sm = 1 / math.sqrt(D)
+    signs = O.plan_signs(D, ROTS[rot], plan.seed)
+    ref = O.attention_int4(np16(q), kc.cpu().numpy(), ksc.cpu().numpy(), lam_k.cpu().numpy(),
+                           vc.cpu().numpy(), vsc.cpu().numpy(), lam_v.cpu().numpy(), L, sm, ROTS[rot], signs)
+    # the reference itself is dominated by the planted token
+    for b, h, t in spots:
+        vhat = O.decode(vc[b, h // rep, t].cpu().numpy(), vsc[b, h // rep, t].cpu().numpy(),
+                        lam_v[h // rep].cpu().numpy(), ROTS[rot], signs)
+        assert np.max(np.abs(ref[b, h] - vhat)) <= 1e-6 * np.max(np.abs(vhat)) + 1e-9
+    for dt in (torch.float32, torch.float16):
+        out = run_attn(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, dt)
+        worst = P.compare_attention(np16(out), ref)
+        say(f"   int4 {dt}: rel err {worst:.2e}")
+
+
 def test_attention_decode_step_full_size():
     """The decode step at full size: batch 64, Hq 8 / Hkv 2, D=128, 32768
     cached tokens plus one appended with kvq_encode (T=1, t0=32768), then
