@@ -35,6 +35,27 @@ namespace kvq {
 namespace {
 
 // One plan-independent description of a codec launch.
+// Division by a call constant d (1 <= d < 2^32) of n < 2^32 (tile and row
+// indices): with M = floor((2^64 - 1) / d) + 1 = ceil(2^64 / d), n * M / 2^64
+// exceeds n / d by less than n / 2^64 < 2^-32, while n / d is at least 1/d
+// below the next integer, so the high 64 bits of n * M are floor(n / d).
+// d = 1 uses M = 0 and returns n.
+struct FastDiv {
+  uint64_t magic;
+  uint64_t d;
+};
+
+inline FastDiv make_fastdiv(uint64_t d) {
+  FastDiv f;
+  f.d = d;
+  f.magic = d <= 1 ? 0 : (~0ull / d) + 1;
+  return f;
+}
+
+__device__ __forceinline__ uint64_t fdiv(uint64_t n, const FastDiv& f) {
+  return f.magic == 0 ? n : __umul64hi(n, f.magic);
+}
+
 struct CodecArgs {
   const uint16_t* x;          // encode / rotate input, fp16
   const uint8_t* codes_in;    // decode input
@@ -48,6 +69,7 @@ struct CodecArgs {
   int64_t sb, sh, st;         // strides of x (encode, rotate) or y (decode)
   int64_t lambda_sb;
   int64_t tiles_per_row, n_tiles;
+  FastDiv div_tpr, div_h;     // by tiles_per_row and by H
   uint64_t signs[4];
 };
 
@@ -112,9 +134,9 @@ struct Tile {
 template <int D>
 __device__ __forceinline__ Tile tile_info(const CodecArgs& a, int64_t tile) {
   Tile t;
-  t.row = tile / a.tiles_per_row;
+  t.row = static_cast<int64_t>(fdiv(static_cast<uint64_t>(tile), a.div_tpr));
   t.t_start = (tile - t.row * a.tiles_per_row) * Geo<D>::VPT;
-  t.b = t.row / a.H;
+  t.b = static_cast<int64_t>(fdiv(static_cast<uint64_t>(t.row), a.div_h));
   t.h = t.row - t.b * a.H;
   const int64_t left = a.T - t.t_start;
   t.nv = static_cast<int>(left < Geo<D>::VPT ? left : Geo<D>::VPT);
@@ -466,10 +488,11 @@ __device__ __forceinline__ uint32_t pair_mask128(const CodecArgs& a, int k) {
 
 template <int ROT, int MODE>
 __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
-  // two LDS objects, so that reads of the masks need not wait for the
-  // direct loads into the tile
+  // separate LDS objects, so that reads of the masks and of lambda need not
+  // wait for the direct loads into the tile
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
   __shared__ __attribute__((aligned(16))) uint32_t mask_lds[64];
+  __shared__ __attribute__((aligned(16))) float lam_lds[128];
   const int lane = threadIdx.x;
   constexpr float kScale = rot_scale<128, ROT>();
 
@@ -480,10 +503,17 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
     const int r = 4 * i + (lane >> 4);
     off4[i] = static_cast<uint32_t>((lane >> 4) * 2 * a.st + 16 * ((lane & 15) ^ (r & 15)));
   }
+  // lambda of a tile: lane l holds channels l and l + 64 in registers from
+  // loads issued right after the tile's direct loads (so the one wait at the
+  // top of the loop covers both), and writes them to LDS there
+  float lam_r0 = 0.f, lam_r1 = 0.f;
   int64_t tile = blockIdx.x;
   if (tile < a.n_tiles) {
     const Tile t = tile_info<128>(a, tile);
     dma_tile128(a, t, lds, lane, off4);
+    const float* lr = a.lambda + t.b * a.lambda_sb + t.h * 128;
+    lam_r0 = lr[lane];
+    lam_r1 = lr[lane + 64];
   }
   __syncthreads();
   // codes and scales of the previous tile, stored only after the next tile's
@@ -499,6 +529,8 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
     // the tile's direct loads have landed in LDS (everything issued after
     // them is a store of the tile before, a transform ago)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lam_lds[lane] = lam_r0;
+    lam_lds[lane + 64] = lam_r1;
     const uint4* masks = reinterpret_cast<const uint4*>(mask_lds);
     uint32_t p[64];
 #pragma unroll
@@ -513,7 +545,13 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
     // the tile is in registers: the buffer takes the next one
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t nxt = tile + gridDim.x;
-    if (nxt < a.n_tiles) dma_tile128(a, tile_info<128>(a, nxt), lds, lane, off4);
+    if (nxt < a.n_tiles) {
+      const Tile tn = tile_info<128>(a, nxt);
+      dma_tile128(a, tn, lds, lane, off4);
+      const float* lr = a.lambda + tn.b * a.lambda_sb + tn.h * 128;
+      lam_r0 = lr[lane];
+      lam_r1 = lr[lane + 64];
+    }
     if (MODE == 0 && pend_valid) {
       *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
 #pragma unroll
@@ -523,10 +561,10 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
 
     float v[128];
     rotate_packed<ROT>(p, v);
-    // lambda of the row: scalar loads (read-only for the kernel), one group
-    // at a time so that they stay out of the transform's register budget
+    // keep the lambda reads below the transform (hoisted they would hold
+    // registers across it)
     asm volatile("" ::: "memory");
-    const cfloat* lam = (const cfloat*)(a.lambda + t.b * a.lambda_sb + t.h * 128);
+    const float4* lam4 = reinterpret_cast<const float4*>(lam_lds);
     const bool valid = lane < t.nv;
 
     if (MODE == 1) {
@@ -535,10 +573,11 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
 #pragma unroll
         for (int j = 0; j < 128; j += 4) {
           float4 o;
-          o.x = v[chan_reg<ROT>(j)] * lam[j] * kScale;
-          o.y = v[chan_reg<ROT>(j + 1)] * lam[j + 1] * kScale;
-          o.z = v[chan_reg<ROT>(j + 2)] * lam[j + 2] * kScale;
-          o.w = v[chan_reg<ROT>(j + 3)] * lam[j + 3] * kScale;
+          const float4 l4 = lam4[j / 4];
+          o.x = v[chan_reg<ROT>(j)] * l4.x * kScale;
+          o.y = v[chan_reg<ROT>(j + 1)] * l4.y * kScale;
+          o.z = v[chan_reg<ROT>(j + 2)] * l4.z * kScale;
+          o.w = v[chan_reg<ROT>(j + 3)] * l4.w * kScale;
           *reinterpret_cast<float4*>(wr + j) = o;
         }
       }
@@ -548,18 +587,25 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
       bool tiny = false;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        asm volatile("" ::: "memory");
+        asm volatile("" ::: "memory");    // one group's lambda reads at a time
         float amax = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 32; ++jj) {
+        for (int jj = 0; jj < 32; jj += 4) {
           const int j = 32 * g + jj;
-          const float wv = v[chan_reg<ROT>(j)] * lam[j];
-          v[chan_reg<ROT>(j)] = wv;
-          amax = fmaxf(amax, fabsf(wv));
+          const float4 l4 = lam4[j / 4];
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float wv = v[chan_reg<ROT>(j + e)] * lv[e];
+            v[chan_reg<ROT>(j + e)] = wv;
+            amax = fmaxf(amax, fabsf(wv));
+          }
         }
-        // scale = fp16(absmax / 7): the float32 quotient rounded to nearest
-        // even once more to fp16
-        sc[g] = f32_to_f16_bits((amax * kScale) / 7.0f);
+        // scale = fp16(absmax / 7), from absmax * fp32(1/7): the product is
+        // within an fp32 ulp of the quotient, so the fp16 rounding differs
+        // from the exact quotient's only within ~1e-7 (relative) of an fp16
+        // rounding midpoint
+        sc[g] = f32_to_f16_bits(amax * (kScale * (1.0f / 7.0f)));
         const float sf = f16_bits_to_f32(sc[g]);
         r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
         tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);    // fp16-subnormal scale
@@ -921,6 +967,8 @@ void fill_common(CodecArgs& a, const CodecDesc& d) {
   a.lambda_sb = d.lambda_sb;
   a.tiles_per_row = (d.T + Geo<D>::VPT - 1) / Geo<D>::VPT;
   a.n_tiles = d.B * d.H * a.tiles_per_row;
+  a.div_tpr = make_fastdiv(static_cast<uint64_t>(a.tiles_per_row));
+  a.div_h = make_fastdiv(static_cast<uint64_t>(d.H));
   for (int i = 0; i < 4; ++i) a.signs[i] = d.signs[i];
 }
 
@@ -933,6 +981,7 @@ hipError_t encode_dispatch(const CodecDesc& d, int mode) {
   a.scales = d.scales;
   a.w = d.w;
   if (a.n_tiles == 0) return hipSuccess;
+  if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
   const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
   if (D == 128) {
     if (mode == 0) {
@@ -956,6 +1005,7 @@ hipError_t decode_dispatch(const CodecDesc& d, bool f32) {
   a.scales_in = d.scales_in;
   a.y = d.y;
   if (a.n_tiles == 0) return hipSuccess;
+  if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
   const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
   if (D == 128 && !f32) {
     hipLaunchKernelGGL((decode128_kernel<ROT>), grid, dim3(64), 0, d.stream, a);
