@@ -679,13 +679,27 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
   const int n_full = static_cast<int>((t_end - t_begin) / kBlk);   // blocks entirely inside
   uint32_t t0 = t_begin;
   if (INT4) {
-    // ping-pong without copies: the next block streams in while this one is
-    // processed; bases are wave-uniform, lane offsets fixed
+    // Split s takes the row's 32-token blocks s, s + S, s + 2 S, ...: the
+    // splits of a row running side by side then read neighbouring blocks,
+    // so each array streams from a contiguous window of memory.  The row's
+    // last block is partial when seq_len is not a multiple of 32; it is the
+    // tail of the split it falls to.  Ping-pong without copies: the next
+    // block streams in while this one is processed; bases are wave-uniform,
+    // lane offsets fixed.
     uint32_t mag_lo, mag_hi;     // fp16 pairs (1024, 1024), (64, 64) as v_and_or operands
     asm("v_mov_b32 %0, 0x64006400" : "=v"(mag_lo));
     asm("v_mov_b32 %0, 0x54005400" : "=v"(mag_hi));
     const Off4 o4 = lane_offsets4(n16, kq);
-    const bool has_tail = ((t_end - t_begin) % kBlk) != 0;
+    const uint32_t seq = static_cast<uint32_t>(a.seq_len);
+    const uint32_t nbr = (seq + kBlk - 1) / kBlk;                    // blocks of the row
+    const uint32_t S = static_cast<uint32_t>(a.S);
+    const uint32_t sp = static_cast<uint32_t>(s);
+    const uint32_t cnt = nbr > sp ? (nbr - 1 - sp) / S + 1 : 0;      // blocks of this split
+    const bool has_tail = (seq % kBlk) != 0 && (nbr - 1) % S == sp;
+    const int n_full = static_cast<int>(cnt) - (has_tail ? 1 : 0);
+    const uint32_t step = kBlk * S;
+    const uint32_t t_end = seq, t_last = seq - 1;
+    uint32_t t0 = kBlk * sp;
     State<true>& s4 = reinterpret_cast<State<true>&>(st);
     Blk4 b0, b1;
     if (n_full == 0) {
@@ -698,26 +712,26 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
       // b0 holds block i at the top; blocks i + 1 and i + 2 are full
       int i = 0;
       for (; i + 2 < n_full; i += 2) {
-        load4<false>(rows, t0 + kBlk, t_last, o4, n16, kq, b1);
+        load4<false>(rows, t0 + step, t_last, o4, n16, kq, b1);
         process4<false>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
-        t0 += kBlk;
-        load4<false>(rows, t0 + kBlk, t_last, o4, n16, kq, b0);
+        t0 += step;
+        load4<false>(rows, t0 + step, t_last, o4, n16, kq, b0);
         process4<false>(s4, b1, t0, t_end, kq, mag_lo, mag_hi);
-        t0 += kBlk;
+        t0 += step;
       }
       // one or two full blocks left, then maybe the tail
       if (n_full - i == 2) {
-        load4<false>(rows, t0 + kBlk, t_last, o4, n16, kq, b1);
+        load4<false>(rows, t0 + step, t_last, o4, n16, kq, b1);
         process4<false>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
-        t0 += kBlk;
-        if (has_tail) load4<true>(rows, t0 + kBlk, t_last, o4, n16, kq, b0);
+        t0 += step;
+        if (has_tail) load4<true>(rows, t0 + step, t_last, o4, n16, kq, b0);
         process4<false>(s4, b1, t0, t_end, kq, mag_lo, mag_hi);
-        t0 += kBlk;
+        t0 += step;
         if (has_tail) process4<true>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
       } else {
-        if (has_tail) load4<true>(rows, t0 + kBlk, t_last, o4, n16, kq, b1);
+        if (has_tail) load4<true>(rows, t0 + step, t_last, o4, n16, kq, b1);
         process4<false>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
-        t0 += kBlk;
+        t0 += step;
         if (has_tail) process4<true>(s4, b1, t0, t_end, kq, mag_lo, mag_hi);
       }
     }
