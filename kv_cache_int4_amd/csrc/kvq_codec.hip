@@ -471,6 +471,9 @@ __device__ __forceinline__ void quant_group(const float (&v)[128], int g, float 
 
 constexpr int kLdsTile = 16384;              // LDS tile of the D=128 encoder
 
+// LDS memory as the direct-load builtins take it.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
 // Read-only data for scalar loads (the constant address space).
 typedef __attribute__((address_space(4))) const float cfloat;
 
@@ -628,6 +631,211 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
     }
   }
   if (MODE == 0 && pend_valid) {
+    *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(pend_cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) = pend_c[q];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// D = 256 encode: a lane pair per vector, 32 vectors (16 KiB) per tile in the
+// D = 128 tile layout with rows = half vectors (row 2v + h = channels
+// 128h .. 128h + 127 of vector v).  SRFT by decimation in time: lane 2v + h
+// takes the complex pairs 2k + h (k < 64), transforms them with the 64-point
+// FFT, the odd lane multiplies by W_128^m, and one butterfly across the pair
+// leaves Z_m on lane 0 and Z_{m+64} on lane 1.  SRHT (Sylvester H_256 =
+// H_2 (x) H_128 on the top index bit): the butterfly across the pair comes
+// first (x_lo + x_hi, x_lo - x_hi), then H_128 in each lane.  Either way a
+// lane ends with a contiguous half of the output channels and quantizes it
+// like a D = 128 vector.  The butterfly computes own + sign * partner, which
+// on the odd lane is the negated value; the sign is folded into that lane's
+// half of the lambda table.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void dma_tile256(const CodecArgs& a, const Tile& t, lds_u8* lds, int lane,
+                                            const uint32_t (&off4)[4]) {
+  const char* base = reinterpret_cast<const char*>(a.x + t.b * a.sb + t.h * a.sh + t.t_start * a.st);
+  const int64_t step = 4 * a.st;        // bytes of two vectors (four rows)
+  if (t.nv == 32) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_global_load_lds(base + i * step + off4[i & 3], lds + 1024 * i, 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (2 * i + (lane >> 5) < t.nv)
+        __builtin_amdgcn_global_load_lds(base + i * step + off4[i & 3], lds + 1024 * i, 16, 0, 0);
+  }
+}
+
+// Sign mask of local pair k of lane half h: SRFT pair 2k + h (decimation in
+// time), SRHT channels 128h + 2k, 128h + 2k + 1.
+template <int ROT>
+__device__ __forceinline__ uint32_t pair_mask256(const CodecArgs& a, int h, int k) {
+  if (ROT == KVQ_ROT_SRFT) {
+    const int P = 2 * k + h;
+    return ((a.signs[P >> 6] >> (P & 63)) & 1u) ? 0x80008000u : 0u;
+  }
+  if (ROT == KVQ_ROT_SRHT) {
+    const int c = 128 * h + 2 * k;
+    const uint64_t w = a.signs[c >> 6];
+    const int i = c & 63;
+    return (static_cast<uint32_t>((w >> i) & 1u) << 15) | (static_cast<uint32_t>((w >> (i + 1)) & 1u) << 31);
+  }
+  return 0u;
+}
+
+template <int ROT>
+__global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
+  __shared__ __attribute__((aligned(16))) uint32_t mask_lds[128];   // [h][k]
+  __shared__ __attribute__((aligned(16))) float lam_lds[256];       // [h][local channel], sign folded
+  const int lane = threadIdx.x;
+  const int hh = lane & 1;                  // half of the vector
+  constexpr float kScale = rot_scale<256, ROT>();
+  const float sgn = hh ? -1.f : 1.f;
+
+  mask_lds[lane] = pair_mask256<ROT>(a, 0, lane);
+  mask_lds[64 + lane] = pair_mask256<ROT>(a, 1, lane);
+  uint32_t off4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + (lane >> 4);      // row of the tile: vector r / 2, half r % 2
+    off4[i] = static_cast<uint32_t>((lane >> 5) * 2 * a.st + ((lane >> 4) & 1) * 256 + 16 * ((lane & 15) ^ (r & 15)));
+  }
+  // lambda of a tile: lane l holds channels l, l + 64, l + 128, l + 192
+  float lam_r[4] = {0.f, 0.f, 0.f, 0.f};
+  int64_t tile = blockIdx.x;
+  if (tile < a.n_tiles) {
+    const Tile t = tile_info<256>(a, tile);
+    dma_tile256(a, t, (lds_u8*)lds, lane, off4);
+    const float* lr = a.lambda + t.b * a.lambda_sb + t.h * 256;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lam_r[q] = lr[lane + 64 * q];
+  }
+  __syncthreads();
+  uint4 pend_c[4] = {};
+  uint2 pend_s = {};
+  bool pend_valid = false;
+  char* pend_cbase = nullptr;
+  char* pend_sbase = nullptr;
+  for (; tile < a.n_tiles; tile += gridDim.x) {
+    const Tile t = tile_info<256>(a, tile);
+    // the tile's direct loads have landed in LDS (everything issued after
+    // them is a store of the tile before, a transform ago)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lam_lds[lane + 64 * q] = (q < 2 ? 1.f : -1.f) * lam_r[q];
+    uint32_t p[64];
+    const uint4* masks = reinterpret_cast<const uint4*>(mask_lds);   // [hh * 16 + j]
+    if (ROT == KVQ_ROT_SRFT) {
+      // pairs 2k + hh: rows 2v (k < 32) and 2v + 1, two dwords per 16-byte chunk
+      const int v2 = lane & ~1;
+#pragma unroll
+      for (int R = 0; R < 2; ++R) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const uint32_t w0 = (blk_off(v2 + R, c) >> 2) + hh;
+          p[32 * R + 2 * c] = reinterpret_cast<const uint32_t*>(lds)[w0];
+          p[32 * R + 2 * c + 1] = reinterpret_cast<const uint32_t*>(lds)[w0 + 2];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint4 w = *reinterpret_cast<const uint4*>(lds + blk_off(lane, j));
+        p[4 * j] = w.x; p[4 * j + 1] = w.y; p[4 * j + 2] = w.z; p[4 * j + 3] = w.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint4 m = masks[16 * hh + j];
+      p[4 * j] ^= m.x; p[4 * j + 1] ^= m.y; p[4 * j + 2] ^= m.z; p[4 * j + 3] ^= m.w;
+    }
+    // the tile is in registers: the buffer takes the next one
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int64_t nxt = tile + gridDim.x;
+    if (nxt < a.n_tiles) {
+      const Tile tn = tile_info<256>(a, nxt);
+      dma_tile256(a, tn, (lds_u8*)lds, lane, off4);
+      const float* lr = a.lambda + tn.b * a.lambda_sb + tn.h * 256;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lam_r[q] = lr[lane + 64 * q];
+    }
+    if (pend_valid) {
+      *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint4*>(pend_cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) = pend_c[q];
+    }
+
+    float v[128];
+    if (ROT == KVQ_ROT_SRFT) {
+      rotate_packed<KVQ_ROT_SRFT>(p, v);
+      if (hh) {
+#pragma unroll
+        for (int m = 1; m < 64; ++m) twiddle<128, false>(v[2 * rev4(m)], v[2 * rev4(m) + 1], m);
+      }
+#pragma unroll
+      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 64; ++k) {
+        v[2 * k] = f16_bits_to_f32(p[k] & 0xFFFFu);
+        v[2 * k + 1] = f16_bits_to_f32(p[k] >> 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+      if (ROT == KVQ_ROT_SRHT) wht128(v);
+    }
+    // keep the lambda reads below the transform
+    asm volatile("" ::: "memory");
+    const float4* lam4 = reinterpret_cast<const float4*>(lam_lds);   // [hh * 32 + j / 4]
+    const bool valid = (lane >> 1) < t.nv;
+
+    float r[4];
+    uint32_t sc[4];
+    bool tiny = false;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      asm volatile("" ::: "memory");
+      float amax = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 32; jj += 4) {
+        const int j = 32 * g + jj;
+        const float4 l4 = lam4[32 * hh + j / 4];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float wv = v[chan_reg<ROT>(j + e)] * lv[e];
+          v[chan_reg<ROT>(j + e)] = wv;
+          amax = fmaxf(amax, fabsf(wv));
+        }
+      }
+      sc[g] = f32_to_f16_bits(amax * (kScale * (1.0f / 7.0f)));
+      const float sf = f16_bits_to_f32(sc[g]);
+      r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
+      tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);
+    }
+    uint32_t cw[16];
+    if (__builtin_amdgcn_ballot_w64(tiny && valid) == 0) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) quant_group<ROT, false>(v, g, r[g], cw + 4 * g);
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) quant_group<ROT, true>(v, g, r[g], cw + 4 * g);
+    }
+    // lane 2v + h: codes bytes 64h .. 64h + 63 and scales 4h .. 4h + 3 of
+    // vector v, i.e. 64 and 8 contiguous bytes at lane * 64, lane * 8
+    const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;   // wave-uniform
+    pend_sbase = reinterpret_cast<char*>(a.scales + cell0 * 8);
+    pend_cbase = reinterpret_cast<char*>(a.codes + cell0 * 128);
+    pend_s = make_uint2(sc[0] | (sc[1] << 16), sc[2] | (sc[3] << 16));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pend_c[q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+    pend_valid = valid;
+  }
+  if (pend_valid) {
     *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -989,6 +1197,8 @@ hipError_t encode_dispatch(const CodecDesc& d, int mode) {
     } else {
       hipLaunchKernelGGL((encode128_kernel<ROT, 1>), grid, dim3(64), 0, d.stream, a);
     }
+  } else if (mode == 0 && ROT != KVQ_ROT_ID) {
+    hipLaunchKernelGGL((encode256_kernel<ROT>), grid, dim3(64), 0, d.stream, a);
   } else if (mode == 0) {
     hipLaunchKernelGGL((encode_kernel<D, ROT, 0>), grid, dim3(64), 0, d.stream, a);
   } else {
