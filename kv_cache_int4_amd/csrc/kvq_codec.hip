@@ -1,25 +1,23 @@
 // Encode / rotate / decode kernels of the int4 KV-cache codec (gfx950).
 //
 // Work decomposition.  A wave owns a tile of 16 KiB of fp16 input: 64 head
-// vectors of D=128 (one per lane) or 32 vectors of D=256 (two lanes each).
+// vectors of D=128 (one per lane) or 32 vectors of D=256 (a lane pair each).
 // Tiles never cross a (batch, head) row, so the lambda row is wave-uniform.
 // Waves are persistent: each walks the tiles with a stride of the grid; two
 // waves share every SIMD, so one streams its tile in while the other
 // computes.
 //
-// Data movement per tile (encode):
-//   HBM --(coalesced 16-byte loads: 16 consecutive lanes read one 256-byte
-//   row)--> VGPRs --(sign xor, ds_write into a per-lane LDS block with an
-//   XOR swizzle)--> LDS --(each lane reads its own 256-byte block)--> VGPRs
-//   --(fp32 transform, lambda, group abs-max, int4, nibble pack)--> LDS
-//   --(coalesced 16-byte stores)--> HBM codes; scales go straight out with
-//   one 8-byte store per lane.
-// The random signs are applied to the fp16 words in the coalesced layout,
-// where every lane always holds the same 16-byte column of a row, so each
-// lane's four sign masks are fixed for the whole kernel.
+// Hot kernels (encode128/256, decode128/256): the next tile's input goes
+// straight from HBM into LDS with direct (global -> LDS) loads while the
+// current tile computes in registers; each lane then reads its own vector
+// (or half vector) from a bank-swizzled LDS block, runs the fp32 transform,
+// lambda, group abs-max and int4 packing (or the reverse), and the results
+// leave through coalesced 16-byte stores.  Random signs are applied as XOR
+// masks on fp16 words where each lane's masks are fixed for the kernel.
 //
-// Decode runs the same path backwards; the fp16 output leaves through the
-// same swizzled LDS blocks and coalesced stores.
+// The general kernels (encode_kernel for rotate-only output and the D=256
+// identity encode, decode_f32_kernel for fp32 output) stage rows through
+// registers and LDS with ordinary loads.
 //
 // Method (gist.science explainer of "When Quantization Is Free",
 // "Methodik" 1-2): sign -> FFT over the D/2 complex pairs -> pack ->
@@ -1000,17 +998,238 @@ __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode
+// D = 256 decode to fp16: a lane pair per vector, 32 vectors per tile, the
+// same direct-load / staging scheme as D = 128 with rows = half vectors.
+// SRFT by decimation in time: lane 2v + h gathers the code bytes of the odd
+// or even frequencies (Z_{2m+h}, one byte perm per two code dwords), runs the
+// inverse 64-point FFT, the odd lane multiplies by conj(W_128^k), and one
+// butterfly across the pair leaves z_k on lane 0 and z_{k+64} on lane 1: a
+// contiguous half of the output row per lane.  SRHT: the butterfly across
+// the pair comes first, then H_128 in each lane (H_256 = H_2 (x) H_128).  The
+// butterfly computes own + sign * partner; the odd lane's half of the
+// 1 / lambda table is negated so that both lanes end with the plain result.
 // ---------------------------------------------------------------------------
-template <int D, int ROT, int OUT_F32>
-__global__ void __launch_bounds__(64, 2) decode_kernel(CodecArgs a) {
+constexpr int kDec2Lam = 4608;           // 1 KiB lambda row (codes, scales as for D = 128)
+constexpr int kLdsDec2In = 5632;
+constexpr int kDec2Rl = 0;               // 1 KiB: [h][local channel] unitary scale / lambda
+constexpr int kDec2Out = 1024;           // 9 KiB staging, rows = half vectors
+constexpr int kLdsDec2Work = kDec2Out + 64 * kDecPitch;
+
+// Slot 64 i + lane: chunk q of vector v = 8 i + lane / 8, stored at LDS byte
+// 128 v + 16 ((q ^ v) % 8) (a lane-parallel read of one chunk of eight rows
+// then spans all banks).
+__device__ __forceinline__ void dma_codes256(const CodecArgs& a, const Tile& t, lds_u8* lds, int lane_in) {
+  // the lane's offsets are recomputed per call (a few integer operations):
+  // hoisted out of the tile loop they would hold registers the transform
+  // needs, and their spill reloads would wait on the loads just issued
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;
+  const char* cb = reinterpret_cast<const char*>(a.codes_in + cell0 * 128);
+  const char* sb = reinterpret_cast<const char*>(a.scales_in + cell0 * 8);
+  const uint32_t off = static_cast<uint32_t>(128 * (lane >> 3) + 16 * ((lane & 7) ^ ((lane >> 3) & 7)));
+  const uint32_t off16 = static_cast<uint32_t>(16 * lane);
+  // the instruction offset (1 KiB per slot row) advances the global and the
+  // LDS address alike
+  const char* g = cb + off;
+  lds_u8* l = lds + kDecCodes;
+  if (t.nv == 32) {
+    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, l, 16, 1024, 0);
+    __builtin_amdgcn_global_load_lds(g, l, 16, 2048, 0);
+    __builtin_amdgcn_global_load_lds(g, l, 16, 3072, 0);
+  } else {
+    // vector 8 i + lane / 8: one lane value against a wave-uniform bound
+    const int r = lane >> 3;
+    if (r < t.nv) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+    if (r < t.nv - 8) __builtin_amdgcn_global_load_lds(g, l, 16, 1024, 0);
+    if (r < t.nv - 16) __builtin_amdgcn_global_load_lds(g, l, 16, 2048, 0);
+    if (r < t.nv - 24) __builtin_amdgcn_global_load_lds(g, l, 16, 3072, 0);
+  }
+  // 16 bytes of scales per vector: lanes below nv (at most 32)
+  if (lane < t.nv) __builtin_amdgcn_global_load_lds(sb + off16, lds + kDecScales, 16, 0, 0);
+  const char* lr = reinterpret_cast<const char*>(a.lambda + t.b * a.lambda_sb + t.h * 256);
+  __builtin_amdgcn_global_load_lds(lr + off16, lds + kDec2Lam, 16, 0, 0);
+}
+
+__device__ __forceinline__ uint64_t sign_word(const CodecArgs& a, int i) {
+  return i == 0 ? a.signs[0] : i == 1 ? a.signs[1] : i == 2 ? a.signs[2] : a.signs[3];
+}
+
+// Sign mask of output pair kg (channels 2 kg, 2 kg + 1) of a D = 256 vector.
+template <int ROT>
+__device__ __forceinline__ uint32_t out_mask256(const CodecArgs& a, int kg) {
+  if (ROT == KVQ_ROT_SRFT) return ((sign_word(a, kg >> 6) >> (kg & 63)) & 1u) ? 0x80008000u : 0u;
+  if (ROT == KVQ_ROT_SRHT) {
+    const uint64_t w = sign_word(a, kg >> 5);
+    const int i = (2 * kg) & 63;
+    return (static_cast<uint32_t>((w >> i) & 1u) << 15) | (static_cast<uint32_t>((w >> (i + 1)) & 1u) << 31);
+  }
+  return 0u;
+}
+
+template <int ROT>
+__global__ void __launch_bounds__(64, 2) decode256_kernel(CodecArgs a) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsDec2In];
+  __shared__ __attribute__((aligned(16))) uint8_t work[kLdsDec2Work];
+  const int lane = threadIdx.x;
+  const int hh = lane & 1;                  // half of the vector
+  const int vec = lane >> 1;
+  constexpr float kScale = rot_scale<256, ROT>();
+  const float sgn = hh ? 1.f : -1.f;
+  uint32_t magic;   // fp16 pair (1024, 1024): a register operand for v_and_or
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  // bytes h, h + 2 of two code dwords: frequencies 2m + h
+  const uint32_t sel = 0x06040200u + 0x01010101u * static_cast<uint32_t>(hh);
+
+  // where this lane's lambda entries c = lane + 64 q go in the 1 / lambda
+  // table, and their sign (negated on the odd half)
+  uint32_t rl_dst[4];
+  float rl_mul[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = lane + 64 * q;
+    int h, j;
+    if (ROT == KVQ_ROT_SRFT) { h = (c >> 1) & 1; j = 2 * (c >> 2) + (c & 1); }
+    else { h = c >> 7; j = c & 127; }
+    rl_dst[q] = static_cast<uint32_t>(4 * (128 * h + j));
+    rl_mul[q] = (ROT != KVQ_ROT_ID && h) ? -kScale : kScale;
+  }
+
+  // rows 8 i + lane / 8 of a half-row pass: vector 4 i + lane / 16, half
+  // (lane / 8) % 2, 16-byte chunk lane % 8
+  const uint32_t out_lane = static_cast<uint32_t>((lane >> 4) * 2 * a.st + ((lane >> 3) & 1) * 256 + 16 * (lane & 7));
+  const int64_t out_step = 8 * a.st;      // bytes of four vectors
+
+  int64_t tile = blockIdx.x;
+  if (tile < a.n_tiles) dma_codes256(a, tile_info<256>(a, tile), (lds_u8*)lds, lane);
+  __syncthreads();
+  for (; tile < a.n_tiles; tile += gridDim.x) {
+    const Tile t = tile_info<256>(a, tile);
+    uint32_t cw[16];
+    uint32_t s16[8];
+    const uint8_t* crow = lds + kDecCodes + 128 * vec;
+    if (ROT == KVQ_ROT_SRFT) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 w = *reinterpret_cast<const uint4*>(crow + 16 * (q ^ (vec & 7)));
+        cw[2 * q] = __builtin_amdgcn_perm(w.y, w.x, sel);
+        cw[2 * q + 1] = __builtin_amdgcn_perm(w.w, w.z, sel);
+      }
+      const uint4 s4 = *reinterpret_cast<const uint4*>(lds + kDecScales + 16 * vec);
+      const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { s16[2 * i] = sw[i] & 0xFFFFu; s16[2 * i + 1] = sw[i] >> 16; }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w = *reinterpret_cast<const uint4*>(crow + 16 * ((4 * hh + q) ^ (vec & 7)));
+        cw[4 * q] = w.x; cw[4 * q + 1] = w.y; cw[4 * q + 2] = w.z; cw[4 * q + 3] = w.w;
+      }
+      const uint2 s2 = *reinterpret_cast<const uint2*>(lds + kDecScales + 16 * vec + 8 * hh);
+      s16[0] = s2.x & 0xFFFFu; s16[1] = s2.x >> 16; s16[2] = s2.y & 0xFFFFu; s16[3] = s2.y >> 16;
+      s16[4] = s16[5] = s16[6] = s16[7] = 0u;
+    }
+    float lq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lq[q] = reinterpret_cast<const float*>(lds + kDec2Lam)[lane + 64 * q];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int64_t nxt = tile + gridDim.x;
+    if (nxt < a.n_tiles) dma_codes256(a, tile_info<256>(a, nxt), (lds_u8*)lds, lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float*>(work + kDec2Rl + rl_dst[q]) = rl_mul[q] * __builtin_amdgcn_rcpf(lq[q]);
+    lds_sync();
+
+    // code dword d holds local pairs 4d .. 4d + 3 (SRFT: frequencies
+    // 2 (4d + b) + h, group d / 2; otherwise channels 8d .., group d / 4 of
+    // the lane's half); dequantized exactly as for D = 128
+    const float4* rl4 = reinterpret_cast<const float4*>(work + kDec2Rl) + 32 * hh;
+    float v[128];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      if ((d & 1) == 0) asm volatile("" ::: "memory");
+      const float sg = f16_bits_to_f32(s16[ROT == KVQ_ROT_SRFT ? d >> 1 : d >> 2]);
+      const float m_lo = -1032.f * sg;
+      const float sg16 = sg * 0.0625f;
+      const float m_hi = -72.f * sg;
+      const uint32_t x = cw[d], y = x >> 8;
+      const h2_t h0 = __builtin_bit_cast(h2_t, (x & 0x000F000Fu) | magic);
+      const h2_t h1 = __builtin_bit_cast(h2_t, (x & 0x00F000F0u) | magic);
+      const h2_t h2 = __builtin_bit_cast(h2_t, (y & 0x000F000Fu) | magic);
+      const h2_t h3 = __builtin_bit_cast(h2_t, (y & 0x00F000F0u) | magic);
+      const int j = 8 * d;
+      const float4 ra = rl4[2 * d], rb = rl4[2 * d + 1];
+      v[j] = fmaf(static_cast<float>(h0[0]), sg, m_lo) * ra.x;
+      v[j + 1] = fmaf(static_cast<float>(h1[0]), sg16, m_hi) * ra.y;
+      v[j + 2] = fmaf(static_cast<float>(h2[0]), sg, m_lo) * ra.z;
+      v[j + 3] = fmaf(static_cast<float>(h3[0]), sg16, m_hi) * ra.w;
+      v[j + 4] = fmaf(static_cast<float>(h0[1]), sg, m_lo) * rb.x;
+      v[j + 5] = fmaf(static_cast<float>(h1[1]), sg16, m_hi) * rb.y;
+      v[j + 6] = fmaf(static_cast<float>(h2[1]), sg, m_lo) * rb.z;
+      v[j + 7] = fmaf(static_cast<float>(h3[1]), sg16, m_hi) * rb.w;
+    }
+
+    if (ROT == KVQ_ROT_SRFT) {
+      fft64<true>(v);
+      if (hh) {
+#pragma unroll
+        for (int k = 1; k < 64; ++k) twiddle<128, true>(v[2 * rev4(k)], v[2 * rev4(k) + 1], k);
+      }
+#pragma unroll
+      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+    } else if (ROT == KVQ_ROT_SRHT) {
+#pragma unroll
+      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+      wht128(v);
+    }
+    // the next tile's direct loads have had the transform to land
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    const char* ybase = reinterpret_cast<const char*>(static_cast<uint16_t*>(a.y) + t.b * a.sb + t.h * a.sh +
+                                                      t.t_start * a.st);
+    const int ho = (lane >> 3) & 1;         // half of the rows this lane stores
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 32 * hf + 4 * c + e;
+          const int pp = ROT == KVQ_ROT_SRFT ? rev4(k) : k;
+          wv[e] = pack_f16x2(v[2 * pp], v[2 * pp + 1]);
+        }
+        *reinterpret_cast<uint4*>(work + kDec2Out + lane * kDecPitch + 16 * c) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
+      lds_sync();
+      const int k0 = 64 * ho + 32 * hf + 4 * (lane & 7);
+      const uint4 mk = make_uint4(out_mask256<ROT>(a, k0), out_mask256<ROT>(a, k0 + 1),
+                                  out_mask256<ROT>(a, k0 + 2), out_mask256<ROT>(a, k0 + 3));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        uint4 w = *reinterpret_cast<const uint4*>(work + kDec2Out + r * kDecPitch + 16 * c);
+        w.x ^= mk.x; w.y ^= mk.y; w.z ^= mk.z; w.w ^= mk.w;
+        // vector 4 i + lane / 16: one lane value against a wave-uniform bound
+        if ((lane >> 4) < t.nv - 4 * i) st_stream16(const_cast<char*>(ybase) + i * out_step + hf * 128 + out_lane, w);
+      }
+      lds_sync();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode to fp32 (exact transform output, for checking): each lane writes its
+// own channels
+// ---------------------------------------------------------------------------
+template <int D, int ROT>
+__global__ void __launch_bounds__(64, 2) decode_f32_kernel(CodecArgs a) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[16384];
   const int lane = threadIdx.x;
   constexpr float kScale = rot_scale<D, ROT>();
-  const int col = lane % G::CPR;
-  const uint4 mask = make_uint4(word_mask<D, ROT>(a.signs, 4 * col), word_mask<D, ROT>(a.signs, 4 * col + 1),
-                                word_mask<D, ROT>(a.signs, 4 * col + 2), word_mask<D, ROT>(a.signs, 4 * col + 3));
 
   auto load_codes = [&](const Tile& tt, uint4 (&cb)[4], uint2& sbuf) {
     const int64_t cell = tt.row * a.Tcap + a.t0 + tt.t_start;
@@ -1089,45 +1308,8 @@ __global__ void __launch_bounds__(64, 2) decode_kernel(CodecArgs a) {
     }
 
     const int vec = lane / G::L;
-    if (!OUT_F32) {
-      // fp16 words of the lane's 64 pairs, through LDS to coalesced stores
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k = 4 * j + e;
-          const int p = ROT == KVQ_ROT_SRFT ? rev4(k) : k;
-          wv[e] = pack_f16x2(v[2 * p], v[2 * p + 1]);
-        }
-        *reinterpret_cast<uint4*>(lds + blk_off(lane, j)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-      }
-      __syncthreads();
-      uint16_t* yb = static_cast<uint16_t*>(a.y);
-      const int c = lane % G::CPR;
-      const int r0 = lane / G::CPR;
-#pragma unroll
-      for (int i = 0; i < G::NLD; ++i) {
-        const int vv = i * G::RPI + r0;
-        uint4 w;
-        if (D == 128) {
-          w = *reinterpret_cast<const uint4*>(lds + blk_off(vv, c));
-        } else if (ROT != KVQ_ROT_SRFT) {
-          w = *reinterpret_cast<const uint4*>(lds + blk_off(2 * vv + (c >> 4), c & 15));
-        } else {
-          const uint32_t off = (c & 1) * 8;
-          const uint2 e = *reinterpret_cast<const uint2*>(lds + blk_off(2 * vv, c >> 1) + off);
-          const uint2 o = *reinterpret_cast<const uint2*>(lds + blk_off(2 * vv + 1, c >> 1) + off);
-          w = make_uint4(e.x, o.x, e.y, o.y);
-        }
-        w.x ^= mask.x; w.y ^= mask.y; w.z ^= mask.z; w.w ^= mask.w;
-        if (vv < t.nv) {
-          uint16_t* dst = yb + t.b * a.sb + t.h * a.sh + (t.t_start + vv) * a.st + c * 8;
-          st_stream16(dst, w);
-        }
-      }
-    } else if (vec < t.nv) {
-      // fp32 parity output: each lane writes its own channels
+    if (vec < t.nv) {
+      // each lane writes its own channels
       float* yr = static_cast<float*>(a.y) + t.b * a.sb + t.h * a.sh + (t.t_start + vec) * a.st;
 #pragma unroll
       for (int k = 0; k < 64; ++k) {
@@ -1217,12 +1399,12 @@ hipError_t decode_dispatch(const CodecDesc& d, bool f32) {
   if (a.n_tiles == 0) return hipSuccess;
   if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
   const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
-  if (D == 128 && !f32) {
+  if (f32) {
+    hipLaunchKernelGGL((decode_f32_kernel<D, ROT>), grid, dim3(64), 0, d.stream, a);
+  } else if (D == 128) {
     hipLaunchKernelGGL((decode128_kernel<ROT>), grid, dim3(64), 0, d.stream, a);
-  } else if (f32) {
-    hipLaunchKernelGGL((decode_kernel<D, ROT, 1>), grid, dim3(64), 0, d.stream, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, ROT, 0>), grid, dim3(64), 0, d.stream, a);
+    hipLaunchKernelGGL((decode256_kernel<ROT>), grid, dim3(64), 0, d.stream, a);
   }
   return hipGetLastError();
 }
