@@ -10,12 +10,14 @@ One step = the whole hot path over one batch of synthetic input:
 Steps rotate over four prefix batches and two int4 caches, so the working
 set (about 1.8 GB) is far beyond the 256 MB Infinity Cache.  The fp16-cache
 comparator (same attention over an unquantized cache) is timed in its own
-loop right after the timed region.
+loop right after the timed region, and so is the D=256 leg: encode and
+decode of the Gemma-3-1B-shaped prefix (212,992 vectors) with SRFT and SRHT
+(field "d256").
 
 Prints ONE JSON line.  `value` is the encode throughput (Mvec/s) over the
-timed region, measured with HIP events around each encode launch on the
-stream the kernels run on; ns/vec, GB/s and the attention microseconds per
-step are extra fields.
+timed region, measured with HIP events at the phase boundaries on the stream
+the kernels run on; ns/vec, GB/s and the attention microseconds per step are
+extra fields.
 """
 
 from __future__ import annotations
@@ -38,12 +40,12 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # the kernel sources they were taken on (sha256 prefix of the listed files);
 # reported as null once those change.
 TRAFFIC = {
-    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "22555fa1dfde4b8f",
-             "bytes": (111.0 + 296095.1 + 4210.5) * 2 * 1024 + (224.0 + 8709.2 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "ab208ef2cf33cb9d",
-               "bytes": 57703.3 * 2 * 1024 + 32256.0 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "ab208ef2cf33cb9d",
-               "bytes": 18287.5 * 2 * 1024 + 118299.2 * 1024},
+    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "84d8ed862823e749",
+             "bytes": (111.0 + 296152.6 + 4210.5) * 2 * 1024 + (224.0 + 8725.5 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "26a1b9821aee5881",
+               "bytes": 57712.7 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "26a1b9821aee5881",
+               "bytes": 16456.4 * 2 * 1024 + 114794.1 * 1024},
 }
 
 
@@ -167,6 +169,56 @@ def cpu_baseline(n_vec: int = 458752):
     }
 
 
+def d256_setup(K, W, torch, dev, n_sets):
+    """Input batches of the Gemma-3-1B-shaped prefix (26 layers x {K,V} x 1
+    KV head x 4096 tokens, D=256: 212,992 vectors), with code, scale and
+    output buffers."""
+    cfg = W.CONFIGS["gemma"]
+    D = cfg.D
+    sets = []
+    for i in range(n_sets):
+        c = W.Config(cfg.name, D, cfg.B, cfg.H, cfg.T, cfg.law, cfg.index + 10 * i)
+        x, lam = W.prefix_inputs(c, dev)
+        codes = torch.empty((cfg.B, cfg.H, cfg.T, D // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((cfg.B, cfg.H, cfg.T, D // 32), dtype=torch.float16, device=dev)
+        sets.append((x, lam, codes, scales, torch.empty_like(x)))
+    return cfg, sets
+
+
+def d256_leg(K, torch, stream, cfg, sets, n):
+    """Encode and decode of the D=256 batches with SRFT and with SRHT, each
+    timed over n launches with HIP events on the kernels' stream, rotating
+    over the batches (beyond the Infinity Cache)."""
+    D = cfg.D
+    nbytes = cfg.vectors * (2 * D + D // 2 + 2 * (D // 32))         # 656 B / vector
+    ns = len(sets)
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    res = {"workload": "Gemma-3-1B-shaped prefix (26 layers x {K,V} x 1 KV head x 4096 tokens, D=256, "
+                       "group 32)", "vectors": cfg.vectors, "bytes_per_call": nbytes}
+    for rot in ("srft", "srht"):
+        plan = K.Plan(D, 32, rot, cfg.sign_seed)
+        enc = timed(lambda i: K.encode(plan, *sets[i % ns][:4]))
+        dec = timed(lambda i: K.decode(plan, sets[i % ns][2], sets[i % ns][3], sets[i % ns][1], sets[i % ns][4]))
+        res[rot] = {
+            "encode_us": round(enc, 2), "encode_GB_s": round(nbytes / enc / 1e3, 1),
+            "encode_frac_hbm": round(nbytes / enc / 1e3 / HBM_PEAK_GBS, 4),
+            "decode_us": round(dec, 2), "decode_GB_s": round(nbytes / dec / 1e3, 1),
+            "decode_frac_hbm": round(nbytes / dec / 1e3 / HBM_PEAK_GBS, 4),
+        }
+    return res
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -226,46 +278,51 @@ def main():
     ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     sm = 1.0 / math.sqrt(D)
+    g_cfg, g_sets = d256_setup(K, W, torch, dev, args.sets)
     torch.cuda.synchronize()
-    log("decode-step caches ready")
+    log("decode-step caches and D=256 batches ready")
 
     phases = ("encode", "decode", "append", "attn")
 
-    def step(i, ev):
+    def run_phase(p, i):
         x, lam, codes, scales, y = sets[i % len(sets)]
         kc, ks, vc, vs = caches[i % 2]
-        if ev: ev[0].record(stream)
-        K.encode(plan, x, lam, codes, scales)
-        if ev: ev[1].record(stream)
-        K.decode(plan, codes, scales, lam, y)
-        if ev: ev[2].record(stream)
-        K.encode(aplan, k_new, lam_k, kc, ks, T0)
-        K.encode(aplan, v_new, lam_v, vc, vs, T0)
-        if ev: ev[3].record(stream)
-        K.attn_decode(aplan, q, kc, ks, lam_k, vc, vs, lam_v, L, sm, out, ws)
-        if ev: ev[4].record(stream)
+        if p == "encode":
+            K.encode(plan, x, lam, codes, scales)
+        elif p == "decode":
+            K.decode(plan, codes, scales, lam, y)
+        elif p == "append":
+            K.encode(aplan, k_new, lam_k, kc, ks, T0)
+            K.encode(aplan, v_new, lam_v, vc, vs, T0)
+        else:
+            K.attn_decode(aplan, q, kc, ks, lam_k, vc, vs, lam_v, L, sm, out, ws)
 
     for i in range(args.warmup):
-        step(i, None)
+        for p in phases:
+            run_phase(p, i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # The K steps run phase-major (K encodes, K decodes, K appends, K
+    # attention steps: the same work as K passes of the whole path, each
+    # decode reading codes its set's encode wrote), with one event at each
+    # phase boundary, so per-launch times are not padded by event records
+    # between launches.
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
     torch.cuda.synchronize()
     if args.profile_marks:
         torch.cuda._sleep(MARK_CYCLES)
         torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(i, events[i])
+    events[0].record(stream)
+    for j, p in enumerate(phases):
+        for i in range(args.steps):
+            run_phase(p, i)
+        events[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"timed {args.steps} steps in {wall:.3f} s")
 
-    ms = {p: 0.0 for p in phases}
-    for ev in events:
-        for j, p in enumerate(phases):
-            ms[p] += ev[j].elapsed_time(ev[j + 1])
-    ms = {p: v / args.steps for p, v in ms.items()}
+    ms = {p: events[j].elapsed_time(events[j + 1]) / args.steps for j, p in enumerate(phases)}
 
     # ---- fp16-cache comparator, same shape ----
     for _ in range(3):
@@ -279,6 +336,9 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     f16_us = e0.elapsed_time(e1) / n16 * 1e3
+    # ---- D=256 (Gemma-3-1B-shaped prefix), both rotations, timed apart ----
+    gemma = d256_leg(K, torch, stream, g_cfg, g_sets, max(10, args.steps))
+    del g_sets
     if args.profile_marks:
         src = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -359,6 +419,7 @@ def main():
                       "fp16_us_per_step": round(f16_us, 2),
                       "fp16_GB_s": round(attn16_bytes / (f16_us / 1e6) / 1e9, 1),
                       "int4_over_fp16": round(attn_us / f16_us, 4)},
+        "d256": gemma,
     }
     print(json.dumps(res), flush=True)
 

@@ -1,16 +1,18 @@
 // Decode-step attention over the int4 cache (and the fp16-cache comparator).
 //
-// Three launches per step on the caller's stream:
-//   1. qrot:    q~ = sm_scale * log2(e) * (R q) / lambda_K for every query
-//               vector (one lane each, the codec's in-register transform).
-//               Scores can then be taken directly against the stored codes:
-//               the cache holds lambda * R k, and q . k^ = (R q) . (R k^).
-//               For the int4 cache q~ is written as three int8 limbs per
-//               32-channel group, q~ ~= s (Q1 + Q2/256 + Q3/65536) with
-//               s = max|q~| / 127 (about 23 bits); for the fp16 cache as
-//               fp16 hi + lo halves.
-//   2. split:   one wave per (b, kv head, group of <= 4 query heads, context
-//               split) streams its slice of the cache 32 tokens at a time:
+// Two launches per step on the caller's stream:
+//   1. split:   one wave per (b, kv head, group of <= 4 query heads, context
+//               split).  While its first block of the cache streams in, the
+//               wave forms q~ = sm_scale * log2(e) * (R q) / lambda_K for
+//               its heads (one lane per channel pair, the codec's transform
+//               across lanes).  Scores can then be taken directly against
+//               the stored codes: the cache holds lambda * R k, and
+//               q . k^ = (R q) . (R k^).  For the int4 cache q~ is held as
+//               three int8 limbs per 32-channel group,
+//               q~ ~= s (Q1 + Q2/256 + Q3/65536) with s = max|q~| / 127
+//               (about 23 bits), staged through a small LDS record; for the
+//               fp16 cache as fp16 hi + lo halves.  Then the wave
+//               streams its slice of the cache 32 tokens at a time:
 //                 QK (int4): v_mfma_i32_16x16x64_i8, rows = 16 tokens,
 //                   columns = (channel group, head) pairs, so every lane
 //                   holds useful scores.  The codes enter as unsigned
@@ -29,7 +31,7 @@
 //                   relative error through cancellation across tokens.
 //               It writes the partial (max, sum, 128 weighted values) of
 //               every head to the workspace.
-//   3. combine: merges the splits (log-sum-exp), divides by lambda_V and
+//   2. combine: merges the splits (log-sum-exp), divides by lambda_V and
 //               applies the inverse rotation across the 64 lanes of a wave
 //               (radix-2 steps with cross-lane shuffles).
 //
@@ -54,13 +56,12 @@ typedef int int4_t __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kHeadsPerWave = 4;
 constexpr int kBlk = 32;              // tokens per inner step
-constexpr int kQRec = 512;            // bytes of one rotated-query record
+constexpr int kQRec = 448;            // bytes of one rotated-query record
 
 // Record layout (int4 cache): three int8 limbs per channel,
 // q~ ~= s (Q1 + Q2 / 256 + Q3 / 65536): [0,128) Q1, [128,256) Q2,
 // [256,384) Q3, [384,400) s[4] f32, [400,448) sums of Q1, Q2, Q3 per group
-// (i32[3][4]).  Record layout (fp16 cache): [0,256) hi fp16[128],
-// [256,512) lo fp16[128].
+// (i32[3][4]).
 constexpr int kRecS = 384;
 constexpr int kRecSum = 400;
 
@@ -76,7 +77,6 @@ struct AttnArgs {
   const float* lambda_v;
   const uint16_t* k16;
   const uint16_t* v16;
-  uint8_t* qrec;      // [B*Hq] records
   float* part_acc;    // [B*Hq][S][128]
   float* part_ml;     // [B*Hq][S][2]
   void* out;
@@ -93,7 +93,7 @@ __device__ __forceinline__ uint32_t sign_bit(const uint64_t (&s)[4], int i) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. query rotation
+// Query rotation (the start of the split kernel)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
@@ -117,108 +117,181 @@ __device__ __forceinline__ int bitrev6(int x) {
   return static_cast<int>(__builtin_bitreverse32(static_cast<uint32_t>(x)) >> 26);
 }
 
-// One wave per query vector.  Lane l owns channels 2l, 2l+1.
+// Loads of the query rotation (int4 cache): the lane's pair word of each of
+// the wave's heads, its two lambda_K entries and the twiddles of its six
+// butterfly stages.  They are issued before the first cache block, so that
+// waiting for them does not wait for the block.
+struct QueryIn {
+  uint32_t w[4];      // head hh: fp16 pair bitrev(lane) (SRFT) or lane
+  float l0, l1;       // lambda_K of channels 2 lane, 2 lane + 1
+  float cw[6], sw[6]; // SRFT stage twiddles
+};
+
 template <int ROT>
-__global__ void __launch_bounds__(64) attn_qrot_kernel(AttnArgs a, int int4) {
-  const int lane = threadIdx.x;
-  const int64_t idx = blockIdx.x;          // b * Hq + h
-  const int64_t h = idx % a.Hq;
-  const int64_t g = h / (a.Hq / a.Hkv);
-  const uint16_t* qr = a.q + idx * 128;
-  uint8_t* rec = a.qrec + idx * kQRec;
-  if (!int4) {
-    const float s = a.sm_scale * kLog2e;
-    const uint32_t w = reinterpret_cast<const uint32_t*>(qr)[lane];
-    const float x0 = f16_bits_to_f32(w & 0xFFFFu) * s, x1 = f16_bits_to_f32(w >> 16) * s;
-    const uint32_t hw = pack_f16x2(x0, x1);
-    reinterpret_cast<uint32_t*>(rec)[lane] = hw;
-    reinterpret_cast<uint32_t*>(rec + 256)[lane] =
-        pack_f16x2(x0 - f16_bits_to_f32(hw & 0xFFFFu), x1 - f16_bits_to_f32(hw >> 16));
-    return;
+__device__ __forceinline__ void query_loads(const AttnArgs& a, const uint16_t* q0, int nh, const float* lk, int lane,
+                                            QueryIn& in) {
+  const int k = ROT == KVQ_ROT_SRFT ? bitrev6(lane) : lane;
+#pragma unroll
+  for (int hh = 0; hh < kHeadsPerWave; ++hh)
+    in.w[hh] = hh < nh ? reinterpret_cast<const uint32_t*>(q0 + hh * 128)[k] : 0u;
+  in.l0 = lk[2 * lane];
+  in.l1 = lk[2 * lane + 1];
+  if (ROT == KVQ_ROT_SRFT) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int hh = 1 << i;
+      const int e = (lane & (hh - 1)) * (32 / hh);
+      in.cw[i] = kTw64Const.c[e];
+      in.sw[i] = kTw64Const.s[e];
+    }
   }
-  float y0, y1;       // rotated channels 2 lane, 2 lane + 1 (unnormalized)
+}
+
+// Rotated query records of the wave's four heads (int4 cache), computed by
+// one wave from the pair words in.w: lane l owns channels 2l, 2l+1 of every
+// head.  The heads advance together through each cross-lane step (four
+// independent shuffles per wait); the records go to LDS at rec + head * kQRec.
+template <int ROT>
+__device__ __forceinline__ void query_records(const AttnArgs& a, const QueryIn& in, int lane, uint8_t* rec) {
+  constexpr int NH = kHeadsPerWave;
+  float y0[NH], y1[NH];   // rotated channels 2 lane, 2 lane + 1 (unnormalized)
   float c = 1.f;
   if (ROT == KVQ_ROT_SRFT) {
     // forward 64-point DFT across lanes, radix-2 decimation in time: lane l
     // starts with pair bitrev(l) (signed) and ends with frequency l
-    const int k = bitrev6(lane);
-    const uint32_t w = reinterpret_cast<const uint32_t*>(qr)[k] ^ (sign_bit(a.signs, k) ? 0x80008000u : 0u);
-    float re = f16_bits_to_f32(w & 0xFFFFu), im = f16_bits_to_f32(w >> 16);
+    const uint32_t m = sign_bit(a.signs, bitrev6(lane)) ? 0x80008000u : 0u;
 #pragma unroll
-    for (int hh = 1; hh <= 32; hh <<= 1) {
-      const float pr = shfl_xor(re, hh), pi = shfl_xor(im, hh);
-      const bool upper = lane & hh;
-      // t = W^j * (the upper element), W = exp(-2 pi i / (2 hh))
-      const float ur = upper ? re : pr, ui = upper ? im : pi;
-      const int e = (lane & (hh - 1)) * (32 / hh);
-      const float cw = kTw64Const.c[e], sw = kTw64Const.s[e];
-      const float tr = ur * cw + ui * sw, ti = ui * cw - ur * sw;
-      const float br = upper ? pr : re, bi = upper ? pi : im;
-      re = upper ? br - tr : br + tr;
-      im = upper ? bi - ti : bi + ti;
+    for (int h = 0; h < NH; ++h) {
+      const uint32_t w = in.w[h] ^ m;
+      y0[h] = f16_bits_to_f32(w & 0xFFFFu);
+      y1[h] = f16_bits_to_f32(w >> 16);
     }
-    y0 = re;
-    y1 = im;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int hh = 1 << i;
+      const bool upper = lane & hh;
+      const float cw = in.cw[i], sw = in.sw[i];
+      float pr[NH], pi[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        pr[h] = shfl_xor(y0[h], hh);
+        pi[h] = shfl_xor(y1[h], hh);
+      }
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        // t = W^j * (the upper element), W = exp(-2 pi i / (2 hh))
+        const float ur = upper ? y0[h] : pr[h], ui = upper ? y1[h] : pi[h];
+        const float tr = ur * cw + ui * sw, ti = ui * cw - ur * sw;
+        const float br = upper ? pr[h] : y0[h], bi = upper ? pi[h] : y1[h];
+        y0[h] = upper ? br - tr : br + tr;
+        y1[h] = upper ? bi - ti : bi + ti;
+      }
+    }
     c = 0.125f;
   } else {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(qr)[lane];
     uint32_t m = 0;
     if (ROT == KVQ_ROT_SRHT) m = (sign_bit(a.signs, 2 * lane) << 15) | (sign_bit(a.signs, 2 * lane + 1) << 31);
-    y0 = f16_bits_to_f32((w ^ m) & 0xFFFFu);
-    y1 = f16_bits_to_f32((w ^ m) >> 16);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      y0[h] = f16_bits_to_f32((in.w[h] ^ m) & 0xFFFFu);
+      y1[h] = f16_bits_to_f32((in.w[h] ^ m) >> 16);
+    }
     if (ROT == KVQ_ROT_SRHT) {
-      const float t0 = y0 + y1, t1 = y0 - y1;
-      y0 = t0;
-      y1 = t1;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const float t0 = y0[h] + y1[h], t1 = y0[h] - y1[h];
+        y0[h] = t0;
+        y1[h] = t1;
+      }
 #pragma unroll
       for (int hh = 1; hh <= 32; hh <<= 1) {
-        const float p0 = shfl_xor(y0, hh), p1 = shfl_xor(y1, hh);
-        if (lane & hh) { y0 = p0 - y0; y1 = p1 - y1; }
-        else { y0 += p0; y1 += p1; }
+        float p0[NH], p1[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          p0[h] = shfl_xor(y0[h], hh);
+          p1[h] = shfl_xor(y1[h], hh);
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          if (lane & hh) { y0[h] = p0[h] - y0[h]; y1[h] = p1[h] - y1[h]; }
+          else { y0[h] += p0[h]; y1[h] += p1[h]; }
+        }
       }
       c = 0.0883883476483184405f;
     }
   }
   const float sc = a.sm_scale * kLog2e * c;
-  const float* lk = a.lambda_k + g * 128;
-  const float q0 = y0 * sc / lk[2 * lane], q1 = y1 * sc / lk[2 * lane + 1];
+  const float r0 = sc / in.l0, r1 = sc / in.l1;
+  float q0[NH], q1[NH], amax[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    q0[h] = y0[h] * r0;
+    q1[h] = y1[h] * r1;
+    amax[h] = fmaxf(fabsf(q0[h]), fabsf(q1[h]));
+  }
   // group = 16 lanes: abs max, three int8 limbs
-  float amax = fmaxf(fabsf(q0), fabsf(q1));
 #pragma unroll
-  for (int m = 1; m <= 8; m <<= 1) amax = fmaxf(amax, shfl_xor(amax, m));
-  const float inv = amax > 0.f ? 127.f / amax : 0.f;
-  const float t[2] = {q0 * inv, q1 * inv};
-  int li[3][2];
+  for (int m = 1; m <= 8; m <<= 1) {
+    float o[NH];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    // |t| <= 127; each residual is at most half a unit of its limb
-    float r1 = rintf(t[e]);
-    const float u = (t[e] - r1) * 256.f;
-    float r2 = rintf(u);
-    const float r3 = fminf(fmaxf(rintf((u - r2) * 256.f), -128.f), 127.f);
-    if (r2 > 127.f) {          // +128 is no int8: carry into the first limb
-      r2 -= 256.f;
-      r1 += 1.f;
+    for (int h = 0; h < NH; ++h) o[h] = shfl_xor(amax[h], m);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) amax[h] = fmaxf(amax[h], o[h]);
+  }
+  int li[NH][3][2];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const float inv = amax[h] > 0.f ? 127.f / amax[h] : 0.f;
+    const float t[2] = {q0[h] * inv, q1[h] * inv};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      // |t| <= 127; each residual is at most half a unit of its limb
+      float r1 = rintf(t[e]);
+      const float u = (t[e] - r1) * 256.f;
+      float r2 = rintf(u);
+      const float r3 = fminf(fmaxf(rintf((u - r2) * 256.f), -128.f), 127.f);
+      if (r2 > 127.f) {          // +128 is no int8: carry into the first limb
+        r2 -= 256.f;
+        r1 += 1.f;
+      }
+      li[h][0][e] = static_cast<int>(r1);
+      li[h][1][e] = static_cast<int>(r2);
+      li[h][2][e] = static_cast<int>(r3);
     }
-    li[0][e] = static_cast<int>(r1);
-    li[1][e] = static_cast<int>(r2);
-    li[2][e] = static_cast<int>(r3);
+  }
+  float sum[NH][3];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int limb = 0; limb < 3; ++limb) sum[h][limb] = static_cast<float>(li[h][limb][0] + li[h][limb][1]);
+#pragma unroll
+  for (int m = 1; m <= 8; m <<= 1) {
+    float o[NH][3];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int limb = 0; limb < 3; ++limb) o[h][limb] = shfl_xor(sum[h][limb], m);
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int limb = 0; limb < 3; ++limb) sum[h][limb] += o[h][limb];
   }
   const int grp = lane >> 4;
 #pragma unroll
-  for (int limb = 0; limb < 3; ++limb) {
-    reinterpret_cast<uint16_t*>(rec + 128 * limb)[lane] =
-        static_cast<uint16_t>((li[limb][0] & 0xFF) | ((li[limb][1] & 0xFF) << 8));
-    float sum = static_cast<float>(li[limb][0] + li[limb][1]);
+  for (int h = 0; h < NH; ++h) {
+    uint8_t* r = rec + h * kQRec;
 #pragma unroll
-    for (int m = 1; m <= 8; m <<= 1) sum += shfl_xor(sum, m);
-    if ((lane & 15) == 0) reinterpret_cast<int*>(rec + kRecSum)[4 * limb + grp] = static_cast<int>(sum);
+    for (int limb = 0; limb < 3; ++limb) {
+      reinterpret_cast<uint16_t*>(r + 128 * limb)[lane] =
+          static_cast<uint16_t>((li[h][limb][0] & 0xFF) | ((li[h][limb][1] & 0xFF) << 8));
+      if ((lane & 15) == 0) reinterpret_cast<int*>(r + kRecSum)[4 * limb + grp] = static_cast<int>(sum[h][limb]);
+    }
+    if ((lane & 15) == 0) reinterpret_cast<float*>(r + kRecS)[grp] = amax[h] > 0.f ? amax[h] / 127.f : 0.f;
   }
-  if ((lane & 15) == 0) reinterpret_cast<float*>(rec + kRecS)[grp] = amax > 0.f ? amax / 127.f : 0.f;
 }
 
 // ---------------------------------------------------------------------------
-// 2. split-K streaming kernel
+// 1. split-K streaming kernel
 // ---------------------------------------------------------------------------
 // x + (x of lane (l + n) mod 16 within the row): DPP row_ror
 template <int N>
@@ -602,8 +675,10 @@ __device__ __forceinline__ void process4(State<true>& st, const Blk4& cur, uint3
 constexpr int kWavesPerCuInt4 = 16;
 constexpr int kWavesPerCuF16 = 16;
 
-template <bool INT4>
+template <bool INT4, int ROT>
 __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
+  // rotated query records of the wave's heads (int4 cache)
+  __shared__ __attribute__((aligned(16))) uint8_t qrec[kHeadsPerWave * kQRec];
   const int lane = threadIdx.x;
   const int n16 = lane & 15;
   const int kq = lane >> 4;
@@ -634,10 +709,19 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
   // pairs with head = n16 & 3; fp16 columns are heads.
   const int my_head = INT4 ? (n16 & 3) : n16;
   const bool head_ok = my_head < nh;
-  const uint8_t* rec = a.qrec + (b * a.Hq + hq0 + (head_ok ? my_head : 0)) * kQRec;
+  const int64_t qrow0 = b * a.Hq + hq0;
 
   State<INT4> st;
-  if (INT4) {
+  // int4 cache: rotate and quantize the wave's query heads into LDS records,
+  // then gather this lane's MFMA operand.  Runs once the first block's loads
+  // are in flight.
+  QueryIn qin;
+  auto init_query = [&]() {
+    // all four records (heads past nh hold a zero word and are never read)
+    query_records<ROT>(a, qin, lane, qrec);
+    // one wave: its LDS writes are visible once its LDS counter drains
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const uint8_t* rec = qrec + (head_ok ? my_head : 0) * kQRec;
     const int grp = n16 >> 2;
     const bool live = head_ok && grp == kq;
 #pragma unroll
@@ -659,14 +743,25 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
       st.corr[limb] = (int4_t){-8 * sum, -8 * sum, -8 * sum, -8 * sum};
     }
     st.sfac = head_ok ? reinterpret_cast<const float*>(rec + kRecS)[grp] * (1.f / 65536.f) : 0.f;
-  } else {
+  };
+  if (!INT4) {
+    // fp16 cache: q * sm_scale * log2(e) as fp16 hi + lo halves, channels
+    // 32 grp + 8 kq .. + 7 of head n16
+    const float sc = a.sm_scale * kLog2e;
+    const uint16_t* qr = a.q + (qrow0 + (head_ok ? my_head : 0)) * 128;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
-      const uint4 h = head_ok ? *reinterpret_cast<const uint4*>(rec + 2 * (32 * grp + 8 * kq)) : make_uint4(0, 0, 0, 0);
-      const uint4 l = head_ok ? *reinterpret_cast<const uint4*>(rec + 256 + 2 * (32 * grp + 8 * kq))
-                              : make_uint4(0, 0, 0, 0);
-      st.qh[grp] = __builtin_bit_cast(half8_t, h);
-      st.ql[grp] = __builtin_bit_cast(half8_t, l);
+      const uint4 w = head_ok ? *reinterpret_cast<const uint4*>(qr + 32 * grp + 8 * kq) : make_uint4(0, 0, 0, 0);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = f16_bits_to_f32(ws[e] & 0xFFFFu) * sc, x1 = f16_bits_to_f32(ws[e] >> 16) * sc;
+        hw[e] = pack_f16x2(x0, x1);
+        lw[e] = pack_f16x2(x0 - f16_bits_to_f32(hw[e] & 0xFFFFu), x1 - f16_bits_to_f32(hw[e] >> 16));
+      }
+      st.qh[grp] = __builtin_bit_cast(half8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      st.ql[grp] = __builtin_bit_cast(half8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
     }
   }
 #pragma unroll
@@ -701,14 +796,15 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
     const uint32_t t_end = seq, t_last = seq - 1;
     uint32_t t0 = kBlk * sp;
     State<true>& s4 = reinterpret_cast<State<true>&>(st);
+    query_loads<ROT>(a, a.q + qrow0 * 128, nh, a.lambda_k + g * 128, lane, qin);
     Blk4 b0, b1;
     if (n_full == 0) {
-      if (has_tail) {
-        load4<true>(rows, t0, t_last, o4, n16, kq, b0);
-        process4<true>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
-      }
+      if (has_tail) load4<true>(rows, t0, t_last, o4, n16, kq, b0);
+      init_query();
+      if (has_tail) process4<true>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
     } else {
       load4<false>(rows, t0, t_last, o4, n16, kq, b0);
+      init_query();
       // b0 holds block i at the top; blocks i + 1 and i + 2 are full
       int i = 0;
       for (; i + 2 < n_full; i += 2) {
@@ -780,7 +876,7 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. combine splits, inverse rotation across the wave
+// 2. combine splits, inverse rotation across the wave
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -918,13 +1014,11 @@ void split_geometry(int64_t B, int64_t Hq, int64_t Hkv, int64_t seq_len, int64_t
 template <int ROT>
 hipError_t run_attention(const AttnDesc& d, AttnArgs& a) {
   const int int4 = d.int4 ? 1 : 0;
-  const unsigned nq = static_cast<unsigned>(d.B * d.Hq);
-  hipLaunchKernelGGL((attn_qrot_kernel<ROT>), dim3(nq), dim3(64), 0, d.stream, a, int4);
   const unsigned nsplit = static_cast<unsigned>(d.B * d.Hkv * a.n_hchunks * a.S);
   if (d.int4) {
-    hipLaunchKernelGGL((attn_split_kernel<true>), dim3(nsplit), dim3(64), 0, d.stream, a);
+    hipLaunchKernelGGL((attn_split_kernel<true, ROT>), dim3(nsplit), dim3(64), 0, d.stream, a);
   } else {
-    hipLaunchKernelGGL((attn_split_kernel<false>), dim3(nsplit), dim3(64), 0, d.stream, a);
+    hipLaunchKernelGGL((attn_split_kernel<false, KVQ_ROT_ID>), dim3(nsplit), dim3(64), 0, d.stream, a);
   }
   const unsigned nc = static_cast<unsigned>(d.B * d.Hq);
   if (d.out_f32) {
@@ -947,14 +1041,14 @@ int64_t attn_num_splits(int64_t B, int64_t Hkv, int64_t seq_len) {
   return S;
 }
 
-// Workspace layout (256-aligned sections): query records [B*Hq][512 B],
-// (max, sum) [B*Hq][S][2] f32, partial sums [B*Hq][S][128] f32, sized for
-// the largest split count any shape with this seq_len can use.
+// Workspace layout (256-aligned sections): (max, sum) [B*Hq][S][2] f32,
+// partial sums [B*Hq][S][128] f32, sized for the largest split count any
+// shape with this seq_len can use.
 size_t attn_workspace_bytes(int D, int64_t B, int64_t Hq, int64_t seq_len) {
   (void)D;
   const int64_t S = max_splits(seq_len);
   const size_t rows = static_cast<size_t>(B * Hq);
-  return align256(rows * kQRec) + align256(rows * S * 2 * 4) + align256(rows * S * 128 * 4);
+  return align256(rows * S * 2 * 4) + align256(rows * S * 128 * 4);
 }
 
 hipError_t launch_attention(const AttnDesc& d) {
@@ -982,9 +1076,8 @@ hipError_t launch_attention(const AttnDesc& d) {
   if (a.S > ms) return hipErrorInvalidValue;
   const size_t rows = static_cast<size_t>(d.B * d.Hq);
   uint8_t* ws = static_cast<uint8_t*>(d.workspace);
-  a.qrec = ws;
-  a.part_ml = reinterpret_cast<float*>(ws + align256(rows * kQRec));
-  a.part_acc = reinterpret_cast<float*>(ws + align256(rows * kQRec) + align256(rows * ms * 2 * 4));
+  a.part_ml = reinterpret_cast<float*>(ws);
+  a.part_acc = reinterpret_cast<float*>(ws + align256(rows * ms * 2 * 4));
   switch (d.int4 ? d.rotation : KVQ_ROT_ID) {
     case KVQ_ROT_SRFT: return run_attention<KVQ_ROT_SRFT>(d, a);
     case KVQ_ROT_SRHT: return run_attention<KVQ_ROT_SRHT>(d, a);
