@@ -40,8 +40,8 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # the kernel sources they were taken on (sha256 prefix of the listed files);
 # reported as null once those change.
 TRAFFIC = {
-    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "84d8ed862823e749",
-             "bytes": (111.0 + 296152.6 + 4210.5) * 2 * 1024 + (224.0 + 8725.5 + 128.0) * 1024},
+    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "48c61fdbfaf66cfd",
+             "bytes": (295675.5 + 4210.5) * 2 * 1024 + (8721.7 + 128.0) * 1024},
     "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "26a1b9821aee5881",
                "bytes": 57712.7 * 2 * 1024 + 32256.0 * 1024},
     "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "26a1b9821aee5881",
@@ -364,7 +364,7 @@ def main():
     shares = {"attn": ms["attn"], "encode": ms["encode"], "decode": ms["decode"]}
     dom = max(shares, key=shares.get)
     if dom == "attn":
-        rl = {"kernel": "kvq_attn_decode (qrot + split-K stream + combine)", "bytes": attn_bytes,
+        rl = {"kernel": "kvq_attn_decode (split-K stream with query rotation + combine)", "bytes": attn_bytes,
               "seconds": ms["attn"] / 1e3, "traffic": measured_traffic("attn")}
     elif dom == "encode":
         rl = {"kernel": "kvq_encode", "bytes": enc_bytes, "seconds": enc_s,
