@@ -33,6 +33,10 @@ Readings where the pages are silent (each listed in the design notes):
   R8  codes round half to even.
   R10 an all-zero group stores scale +0 and code 0 (nibble 8).
   R12 nibble = q + 8 (offset binary); the even channel sits in the low nibble.
+  B8  the int8 variant (explainer, "Methodik" 2: rounding to signed int4 or
+      int8) takes scale = fp16(absmax / 127), codes clamped to [-128, 127]
+      and stored as two's-complement bytes, one per channel.  Groups of 16
+      (explainer, "Methodik" 3) are the G = 16 case of the same quantizer.
   DP  where a floating-point value decides an integer (the fp16 scale, the
       int4 code) the decision is taken in float32, the precision the GPU
       kernel computes in: w is the float64 rotation rounded to float32, the
@@ -55,7 +59,8 @@ __all__ = [
     "SRFT", "SRHT", "IDENTITY", "ROTATIONS", "GROUP",
     "splitmix64", "plan_signs",
     "rotate_forward", "rotate_inverse",
-    "quantize_groups", "pack_nibbles", "unpack_nibbles",
+    "quantize_groups", "pack_nibbles", "unpack_nibbles", "pack_codes", "unpack_codes",
+    "code_range",
     "encode", "decode", "rotate",
     "boundary_distances",
     "attention_int4", "attention_f16",
@@ -218,28 +223,37 @@ def srht_matrix_bruteforce(D: int, signs) -> list[list[float]]:
 # Quantizer (explainer, Methodik 2 and 3)
 # ---------------------------------------------------------------------------
 
-def quantize_groups(w: np.ndarray, G: int = GROUP):
-    """Per-group abs-max scale and int4 codes of the lambda-scaled rotation.
+def code_range(bits: int):
+    """(qmin, qmax) of signed codes of the given width: (-8, 7) for int4,
+    (-128, 127) for int8.  The scale divides the group abs-max by qmax."""
+    if bits not in (4, 8):
+        raise ValueError(f"code width {bits} is not 4 or 8")
+    return -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+
+
+def quantize_groups(w: np.ndarray, G: int = GROUP, bits: int = 4):
+    """Per-group abs-max scale and signed codes of the lambda-scaled rotation.
 
     Takes w (float64, last axis D) and returns
-      q      int8  [..., D]     codes in [-8, 7]
+      q      int8  [..., D]     codes in [qmin, qmax] (code_range(bits))
       scale  float16 [..., D/G] one scale per group of G consecutive channels
     Decision precision (reading DP): w is rounded to float32; the group
-    abs-max a is exact in float32; scale = fp16_RNE(fp32(a / 7)); the code is
-    rint_half_even(fp32(w / scale)) clamped to [-8, 7], and 0 where the scale
-    is zero (reading R10).
+    abs-max a is exact in float32; scale = fp16_RNE(fp32(a / qmax)); the code
+    is rint_half_even(fp32(w / scale)) clamped to [qmin, qmax], and 0 where
+    the scale is zero (reading R10).
     """
+    qmin, qmax = code_range(bits)
     w32 = np.asarray(w, dtype=np.float64).astype(np.float32)
     D = w32.shape[-1]
     assert D % G == 0
     wg = w32.reshape(w32.shape[:-1] + (D // G, G))
     a = np.max(np.abs(wg), axis=-1)                       # float32, exact
     with np.errstate(over="raise"):
-        scale = (a / np.float32(7.0)).astype(np.float16)  # fp32 quotient -> fp16 RNE
+        scale = (a / np.float32(qmax)).astype(np.float16)  # fp32 quotient -> fp16 RNE
     s32 = scale.astype(np.float32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = wg / s32                                  # IEEE float32 division
-    q = np.where(s32 == 0, np.float32(0), np.clip(np.rint(ratio), -8, 7))
+    q = np.where(s32 == 0, np.float32(0), np.clip(np.rint(ratio), qmin, qmax))
     return q.reshape(w32.shape).astype(np.int8), scale
 
 
@@ -262,6 +276,26 @@ def unpack_nibbles(b: np.ndarray) -> np.ndarray:
     return q.astype(np.int8)
 
 
+def pack_codes(q: np.ndarray, bits: int = 4) -> np.ndarray:
+    """Code bytes of one vector: int4 as nibbles (pack_nibbles), int8 as
+    two's-complement bytes, one per channel (reading B8)."""
+    if bits == 4:
+        return pack_nibbles(q)
+    qmin, qmax = code_range(bits)
+    q = np.asarray(q, dtype=np.int16)
+    assert q.min(initial=0) >= qmin and q.max(initial=0) <= qmax
+    return (q & 0xFF).astype(np.uint8)
+
+
+def unpack_codes(b: np.ndarray, bits: int = 4) -> np.ndarray:
+    """Inverse of pack_codes: code bytes -> signed codes int16 [..., D]."""
+    if bits == 4:
+        return unpack_nibbles(b).astype(np.int16)
+    code_range(bits)
+    b = np.asarray(b, dtype=np.uint8).astype(np.int16)
+    return np.where(b >= 128, b - 256, b).astype(np.int16)
+
+
 # ---------------------------------------------------------------------------
 # Encode / decode
 # ---------------------------------------------------------------------------
@@ -273,18 +307,19 @@ def rotate(x16: np.ndarray, lam: np.ndarray, rotation: int, signs: np.ndarray) -
     return np.asarray(lam, dtype=np.float64) * rotate_forward(x, rotation, signs)
 
 
-def encode(x16, lam, rotation: int, signs: np.ndarray, G: int = GROUP):
+def encode(x16, lam, rotation: int, signs: np.ndarray, G: int = GROUP, bits: int = 4):
     """The full write path: x (fp16, [..., D]) and lambda ([..., D], broadcast
-    like numpy) -> (codes uint8 [..., D/2], scales fp16 [..., D/G], w float64)."""
+    like numpy) -> (codes uint8 [..., D*bits/8], scales fp16 [..., D/G],
+    w float64)."""
     w = rotate(x16, lam, rotation, signs)
-    q, scale = quantize_groups(w, G)
-    return pack_nibbles(q), scale, w
+    q, scale = quantize_groups(w, G, bits)
+    return pack_codes(q, bits), scale, w
 
 
-def decode(codes, scales, lam, rotation: int, signs: np.ndarray, G: int = GROUP) -> np.ndarray:
+def decode(codes, scales, lam, rotation: int, signs: np.ndarray, G: int = GROUP, bits: int = 4) -> np.ndarray:
     """The read path: unpack, rescale by the group scale, divide by lambda,
     inverse rotation (R^T).  Returns float64 [..., D]."""
-    q = unpack_nibbles(codes).astype(np.float64)
+    q = unpack_codes(codes, bits).astype(np.float64)
     D = q.shape[-1]
     s = np.asarray(scales, dtype=np.float16).astype(np.float64)
     s_full = np.repeat(s, G, axis=-1)
@@ -293,15 +328,16 @@ def decode(codes, scales, lam, rotation: int, signs: np.ndarray, G: int = GROUP)
     return rotate_inverse(y, rotation, signs)
 
 
-def boundary_distances(w: np.ndarray, scale_used: np.ndarray, G: int = GROUP):
+def boundary_distances(w: np.ndarray, scale_used: np.ndarray, G: int = GROUP, bits: int = 4):
     """How close each decision was to a rounding boundary, in float64.
 
     Returns (code_dist [..., D], scale_rel_dist [..., D/G]):
       code_dist  = | w/scale - (k + 1/2) | for the nearest half-integer, in
                    code units, computed with the scale actually used;
-      scale_rel_dist = | a/7 - m | / (a/7) for the nearest fp16 rounding
-                   midpoint m (inf where a = 0).
+      scale_rel_dist = | a/qmax - m | / (a/qmax) for the nearest fp16
+                   rounding midpoint m (inf where a = 0).
     """
+    qmax = code_range(bits)[1]
     w = np.asarray(w, dtype=np.float64)
     D = w.shape[-1]
     s = np.repeat(np.asarray(scale_used, dtype=np.float16).astype(np.float64), G, axis=-1)
@@ -310,7 +346,7 @@ def boundary_distances(w: np.ndarray, scale_used: np.ndarray, G: int = GROUP):
     code_dist = np.abs(r - (np.floor(r) + 0.5))
     code_dist = np.where(s > 0, code_dist, np.inf)
     a = np.max(np.abs(w.reshape(w.shape[:-1] + (D // G, G))), axis=-1)
-    t = a / 7.0
+    t = a / float(qmax)
     # fp16 neighbours of t and their midpoint
     lo = t.astype(np.float16)
     lo = np.where(lo.astype(np.float64) > t, np.nextafter(lo, np.float16(0)), lo)
@@ -336,10 +372,11 @@ def _softmax_weighted(q, K, V, sm_scale):
 
 
 def attention_int4(q16, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v,
-                   seq_len: int, sm_scale: float, rotation: int, signs, G: int = GROUP):
-    """Decode-step attention over the int4 cache.
+                   seq_len: int, sm_scale: float, rotation: int, signs, G: int = GROUP, bits: int = 4):
+    """Decode-step attention over the quantized cache (int4 codes, or int8
+    with bits = 8).
 
-    Shapes: q [B, Hq, D] fp16; codes [B, Hkv, Tcap, D/2]; scales
+    Shapes: q [B, Hq, D] fp16; codes [B, Hkv, Tcap, D*bits/8]; scales
     [B, Hkv, Tcap, D/G]; lambda [Hkv, D].  Tokens 0..seq_len-1 of each
     (b, kv head) are decoded with ``decode`` and query head h reads kv head
     h // (Hq / Hkv).  Returns float64 [B, Hq, D].
@@ -351,8 +388,8 @@ def attention_int4(q16, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v,
     out = np.zeros((B, Hq, D))
     for b in range(B):
         for g in range(Hkv):
-            K = decode(k_codes[b, g, :seq_len], k_scales[b, g, :seq_len], lam_k[g], rotation, signs, G)
-            V = decode(v_codes[b, g, :seq_len], v_scales[b, g, :seq_len], lam_v[g], rotation, signs, G)
+            K = decode(k_codes[b, g, :seq_len], k_scales[b, g, :seq_len], lam_k[g], rotation, signs, G, bits)
+            V = decode(v_codes[b, g, :seq_len], v_scales[b, g, :seq_len], lam_v[g], rotation, signs, G, bits)
             for h in range(g * rep, (g + 1) * rep):
                 out[b, h] = _softmax_weighted(q[b, h], K, V, sm_scale)
     return out

@@ -62,8 +62,15 @@ def _inv_no_signs(y, rotation, signs):
     return _orig["rotate_inverse"](y, rotation, np.ones_like(signs))
 
 
-def _quant_factory(div=7.0, half_away=False, lo=-8, hi=7, strided=False):
-    def q(w, G=K.GROUP):
+def _quant_factory(div=7.0, half_away=False, lo=-8, hi=7, strided=False, div8=127.0, lo8=-128, hi8=127,
+                   half_away8=False, g16_as_32=False):
+    def q(w, G=K.GROUP, bits=4):
+        if bits == 8:
+            d, l, h, away = div8, lo8, hi8, half_away8
+        else:
+            d, l, h, away = div, lo, hi, half_away
+        if g16_as_32 and G == 16:
+            G = 32
         w32 = np.asarray(w, dtype=np.float64).astype(np.float32)
         D = w32.shape[-1]
         if strided:   # groups of every (D/G)-th channel instead of consecutive ones
@@ -71,16 +78,28 @@ def _quant_factory(div=7.0, half_away=False, lo=-8, hi=7, strided=False):
         else:
             wg = w32.reshape(w32.shape[:-1] + (D // G, G))
         a = np.max(np.abs(wg), axis=-1)
-        scale = (a / np.float32(div)).astype(np.float16)
+        scale = (a / np.float32(d)).astype(np.float16)
         s32 = scale.astype(np.float32)[..., None]
         with np.errstate(divide="ignore", invalid="ignore"):
             r = wg / s32
-        rr = np.sign(r) * np.floor(np.abs(r) + 0.5) if half_away else np.rint(r)
-        qq = np.where(s32 == 0, 0, np.clip(rr, lo, hi))
+        rr = np.sign(r) * np.floor(np.abs(r) + 0.5) if away else np.rint(r)
+        qq = np.where(s32 == 0, 0, np.clip(rr, l, h))
         if strided:
             qq = np.swapaxes(qq, -1, -2)
         return qq.reshape(w32.shape).astype(np.int8), scale
     return q
+
+
+def _pack_codes_offset8(q, bits=4):
+    if bits == 8:   # offset binary q + 128 instead of two's complement
+        return (np.asarray(q, dtype=np.int16) + 128).astype(np.uint8)
+    return _orig["pack_codes"](q, bits)
+
+
+def _unpack_codes_unsigned8(b, bits=4):
+    if bits == 8:   # bytes read as unsigned
+        return np.asarray(b, dtype=np.uint8).astype(np.int16)
+    return _orig["unpack_codes"](b, bits)
 
 
 def _pack_swapped(q):
@@ -101,12 +120,12 @@ def _pack_twos(q):
     return ((q[..., 0::2] & 0xF) | ((q[..., 1::2] & 0xF) << 4)).astype(np.uint8)
 
 
-def _decode_mul_lambda(codes, scales, lam, rotation, signs, G=K.GROUP):
-    return _orig["decode"](codes, scales, 1.0 / np.asarray(lam, dtype=np.float64), rotation, signs, G)
+def _decode_mul_lambda(codes, scales, lam, rotation, signs, G=K.GROUP, bits=4):
+    return _orig["decode"](codes, scales, 1.0 / np.asarray(lam, dtype=np.float64), rotation, signs, G, bits)
 
 
-def _attn_bad_gqa(q16, kc, ks, lk, vc, vs, lv, seq_len, sm_scale, rotation, signs, G=K.GROUP):
-    out = _orig["attention_int4"](q16, kc, ks, lk, vc, vs, lv, seq_len, sm_scale, rotation, signs, G)
+def _attn_bad_gqa(q16, kc, ks, lk, vc, vs, lv, seq_len, sm_scale, rotation, signs, G=K.GROUP, bits=4):
+    out = _orig["attention_int4"](q16, kc, ks, lk, vc, vs, lv, seq_len, sm_scale, rotation, signs, G, bits)
     # interleaved head -> kv-head map (h % Hkv) instead of blocks (h // rep)
     B, Hq, D = out.shape
     Hkv = kc.shape[1]
@@ -115,9 +134,9 @@ def _attn_bad_gqa(q16, kc, ks, lk, vc, vs, lv, seq_len, sm_scale, rotation, sign
     return out[:, perm]
 
 
-def _attn_double_scale(q16, kc, ks, lk, vc, vs, lv, seq_len, sm_scale, rotation, signs, G=K.GROUP):
+def _attn_double_scale(q16, kc, ks, lk, vc, vs, lv, seq_len, sm_scale, rotation, signs, G=K.GROUP, bits=4):
     return _orig["attention_int4"](q16, kc, ks, lk, vc, vs, lv, seq_len, sm_scale * sm_scale,
-                                   rotation, signs, G)
+                                   rotation, signs, G, bits)
 
 
 def _splitmix_bad(seed, n):
@@ -159,6 +178,12 @@ MUTANTS = {
     "attention-gqa-interleaved": ("attention_int4", _attn_bad_gqa),
     "attention-double-scale": ("attention_int4", _attn_double_scale),
     "splitmix-wrong-shift": ("splitmix64", _splitmix_bad),
+    "int8-scale-absmax-over-128": ("quantize_groups", _quant_factory(div8=128.0)),
+    "int8-clamp-symmetric-127": ("quantize_groups", _quant_factory(lo8=-127)),
+    "int8-round-half-away": ("quantize_groups", _quant_factory(half_away8=True)),
+    "g16-grouped-as-32": ("quantize_groups", _quant_factory(g16_as_32=True)),
+    "int8-offset-binary": ("pack_codes", _pack_codes_offset8),
+    "int8-unpack-unsigned": ("unpack_codes", _unpack_codes_unsigned8),
     "signs-bit-order": ("plan_signs", _signs_msb_first),
 }
 
@@ -181,6 +206,13 @@ CHECKS = [
     P.test_decode_inverts_rotation_on_grid_values,
     P.check_attention_bruteforce,
     P.test_attention_special_cases,
+    P.check_exact_construction_int8,
+    P.check_half_even_ties_int8,
+    P.check_subnormal_scale_int8,
+    lambda: P.check_error_bound_variants(n=300),
+    P.check_codes_int8_exhaustive,
+    P.check_compression_variants,
+    P.check_attention_bruteforce_int8,
 ]
 
 

@@ -161,11 +161,11 @@ def test_identity_rotation():
 
 # ------------------------------------------------------------ quantizer ----
 
-def _ident_encode(x_vals, lam_vals):
+def _ident_encode(x_vals, lam_vals, G=O.GROUP, bits=4):
     """Encode one vector with the identity rotation: w = lambda * x."""
     x = np.asarray(x_vals, dtype=np.float16)[None, :]
     lam = np.asarray(lam_vals, dtype=np.float32)[None, :]
-    codes, scales, w = O.encode(x, lam, O.IDENTITY, O.plan_signs(x.shape[-1], O.IDENTITY, 0))
+    codes, scales, w = O.encode(x, lam, O.IDENTITY, O.plan_signs(x.shape[-1], O.IDENTITY, 0), G, bits)
     return codes[0], scales[0], w[0]
 
 
@@ -281,6 +281,153 @@ def test_nibble_layout_exhaustive():
     check_nibbles_exhaustive()
 
 
+# ------------------------------------------ int8 codes and groups of 16 --
+# The explainer ("Methodik" 2) rounds to signed int4 or int8, and its scaling
+# section ("Methodik" 3) uses groups of 16: scale = fp16(absmax / 127) for
+# int8, codes clamped to [-128, 127] and stored as two's-complement bytes.
+
+def check_exact_construction_int8():
+    """w_j = k_j * sigma with max |k_j| = qmax gives sigma and k back exactly,
+    for int8 (groups of 32 and 16) and int4 in groups of 16."""
+    rng = _rng(13)
+    D = 64
+    for bits, G in ((8, 32), (8, 16), (4, 16)):
+        qmax = 127 if bits == 8 else 7
+        for sigma in (np.float16(0.0137), np.float16(1.0), np.float16(3.75), np.float16(61.5)):
+            k = rng.integers(-qmax, qmax + 1, D)
+            for g in range(D // G):           # every group reaches +-qmax
+                k[g * G + 1] = qmax if g % 2 == 0 else -qmax
+            codes, scales, _ = _ident_encode(k.astype(np.float16), np.full(D, np.float32(sigma)), G, bits)
+            assert scales.shape == (D // G,) and np.all(scales == sigma), (bits, G, sigma, scales)
+            assert codes.shape == (D * bits // 8,)
+            assert np.array_equal(O.unpack_codes(codes[None], bits)[0], k), (bits, G)
+
+
+def check_half_even_ties_int8():
+    D = 32
+    x = np.zeros(D, dtype=np.float16)
+    x[:8] = [127, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5]   # a = 127 -> sigma = 1
+    x[16:24] = [126.5, -126.5, 125.5, 64.5, -64.5, 0, 1, -1]
+    codes, scales, _ = _ident_encode(x, np.ones(D), 16, 8)
+    assert scales[0] == 1 and scales[1] == np.float16(126.5 / 127)
+    q = O.unpack_codes(codes[None], 8)[0]
+    assert list(q[:8]) == [127, 0, 2, 2, 0, -2, -2, 4]
+    # second group: sigma = fp16(126.5/127); each code against exact rationals
+    sig = Fraction(float(scales[1]))
+    for j in range(16, 24):
+        r = Fraction(float(x[j])) / sig
+        fl = math.floor(r)
+        k = fl + (1 if (r - fl > Fraction(1, 2) or (r - fl == Fraction(1, 2) and fl % 2 == 1)) else 0)
+        assert q[j] == max(-128, min(127, k)), (j, q[j], k)
+
+
+def check_subnormal_scale_int8():
+    """a / 127 below the fp16 normal range: the scale rounds to a subnormal
+    and both ends of the int8 clamp engage; expected values by exact
+    rational arithmetic."""
+    D = 32
+    ulp = Fraction(1, 2 ** 24)                 # fp16 subnormal spacing
+    mult = [190, -190, 3, -3, 1, 0, 127, -128, -129, 128, 5] + [0] * 21
+    x = np.array([float(m * ulp) for m in mult], dtype=np.float16)
+    codes, scales, _ = _ident_encode(x, np.ones(D), 32, 8)
+    a = max(abs(m) for m in mult) * ulp
+    t = a / 127                                 # 190/127 ulp -> rounds to 1 ulp
+    sig = Fraction(round(t / ulp)) * ulp
+    assert Fraction(float(scales[0])) == sig
+    want = []
+    for m in mult:
+        r = Fraction(m) * ulp / sig
+        k = math.floor(r + Fraction(1, 2))
+        want.append(max(-128, min(127, k)))
+    assert list(O.unpack_codes(codes[None], 8)[0]) == want
+    assert -128 in want and 127 in want
+
+
+def check_error_bound_variants(n=2000, D=128, seed=4):
+    """|w - q sigma| <= sigma / 2 on every normal-scale group, and the
+    x-domain bound through orthogonality, for int4/G16, int8/G32, int8/G16."""
+    rng = _rng(seed)
+    x = (rng.standard_normal((n, D)) * np.exp(0.5 * rng.standard_normal(D))).astype(np.float16)
+    lam = np.exp(0.3 * rng.standard_normal(D)).astype(np.float32)
+    for bits, G in ((4, 16), (8, 32), (8, 16)):
+        for rot in (O.SRFT, O.SRHT):
+            s = O.plan_signs(D, rot, 42)
+            codes, scales, w = O.encode(x, lam, rot, s, G, bits)
+            q = O.unpack_codes(codes, bits).astype(np.float64)
+            sig = np.repeat(scales.astype(np.float64), G, axis=-1)
+            normal = sig >= 2.0 ** -14
+            err = np.abs(w - q * sig)
+            slack = np.abs(w) * 2.0 ** -23
+            assert np.all((err <= sig / 2 + slack)[normal]), (bits, G, rot)
+            xh = O.decode(codes, scales, lam, rot, s, G, bits)
+            lhs = np.linalg.norm(x.astype(np.float64) - xh, axis=-1)
+            rhs = np.linalg.norm(sig / (2 * lam.astype(np.float64)), axis=-1)
+            assert np.all(lhs <= rhs * (1 + 1e-6) + 1e-9)
+
+
+def check_codes_int8_exhaustive():
+    q = np.arange(-128, 128, dtype=np.int16)[None, :]
+    b = O.pack_codes(q, 8)
+    assert sorted(b[0].tolist()) == list(range(256))
+    assert np.array_equal(O.unpack_codes(b, 8), q)
+    allb = np.arange(256, dtype=np.uint8)[None, :]
+    assert np.array_equal(O.pack_codes(O.unpack_codes(allb, 8), 8), allb)
+    # two's complement, one byte per channel in channel order
+    assert O.pack_codes(np.array([[-1, -128, 127, 0, 1]]), 8).tolist() == [[0xFF, 0x80, 0x7F, 0x00, 0x01]]
+
+
+def check_compression_variants():
+    """bytes(fp16) / bytes(codes + fp16 scales) = 16 / (bits + 16 / G), and the
+    oracle's buffers have exactly those sizes."""
+    for bits, G, ratio in ((4, 32, Fraction(32, 9)), (4, 16, Fraction(16, 5)),
+                           (8, 32, Fraction(32, 17)), (8, 16, Fraction(16, 9))):
+        for D in (128, 256):
+            assert abs(O.compression_ratio(D, G, bits) - float(ratio)) < 1e-15
+            x = np.zeros((1, D), dtype=np.float16)
+            codes, scales, _ = O.encode(x, np.ones(D), O.SRFT, O.plan_signs(D, O.SRFT, 0), G, bits)
+            assert Fraction(x.nbytes, codes.nbytes + scales.nbytes) == ratio
+
+
+def test_int8_and_group16_exact_construction():
+    check_exact_construction_int8()
+
+
+def test_int8_round_half_to_even():
+    check_half_even_ties_int8()
+
+
+def test_int8_subnormal_scale_exact_codes():
+    check_subnormal_scale_int8()
+
+
+def test_int8_and_group16_error_bound():
+    check_error_bound_variants()
+
+
+def test_int8_code_layout_exhaustive():
+    check_codes_int8_exhaustive()
+
+
+def test_compression_variants_closed_form():
+    check_compression_variants()
+
+
+def test_uniform_noise_statistic_int8_group16():
+    """The same uniform-noise statistic for int8 in groups of 16."""
+    rng = _rng(6)
+    n, D, G = 8000, 128, 16
+    x = (rng.standard_normal((n, D))).astype(np.float16)
+    s = O.plan_signs(D, O.SRHT, 2)
+    codes, scales, w = O.encode(x, np.ones(D), O.SRHT, s, G, 8)
+    q = O.unpack_codes(codes, 8).astype(np.float64)
+    sig = np.repeat(scales.astype(np.float64), G, axis=-1)
+    wg = np.abs(w).reshape(n, D // G, G)
+    is_max = (wg == wg.max(axis=-1, keepdims=True)).reshape(n, D)
+    ratio = ((w - q * sig) ** 2 / (sig ** 2 / 12))[~is_max]
+    assert ratio.size > 900_000
+    assert abs(ratio.mean() - 1) < 0.05, ratio.mean()
+
+
 def check_uniform_noise_statistic(n=12000, D=128, seed=5):
     """Away from the group maximum the rounding error behaves like uniform
     noise of width sigma: E[(w - q sigma)^2] / (sigma^2 / 12) ~ 1 (the
@@ -373,25 +520,29 @@ def test_decode_inverts_rotation_on_grid_values():
 
 # ------------------------------------------------------------ attention ---
 
-def _tiny_cache(B, Hkv, T, D, rot, seed):
+def _tiny_cache(B, Hkv, T, D, rot, seed, G=O.GROUP, bits=4):
     rng = _rng(seed)
     s = O.plan_signs(D, rot, seed)
     x = (rng.standard_normal((B, Hkv, T, D)) * 2).astype(np.float16)
     lam = np.exp(0.3 * rng.standard_normal((Hkv, D))).astype(np.float32)
-    codes, scales, _ = O.encode(x, lam[None, :, None, :], rot, s)
+    codes, scales, _ = O.encode(x, lam[None, :, None, :], rot, s, G, bits)
     return codes, scales, lam, s
 
 
-def _brute_attention(q16, kc, ks, lk, vc, vs, lv, L, sm_scale, D, signs):
+def _brute_attention(q16, kc, ks, lk, vc, vs, lv, L, sm_scale, D, signs, G=32, bits=4):
     """Pure-Python loops: unpack by hand, rescale, apply the brute-force
     SRFT matrix transposed, exponentiate and average."""
     R = O.srft_matrix_bruteforce(D, [int(v) for v in signs])
     def dec(code_row, scale_row, lam):
         y = []
         for j in range(D):
-            byte = int(code_row[j // 2])
-            nib = (byte & 0xF) if j % 2 == 0 else (byte >> 4)
-            y.append((nib - 8) * float(scale_row[j // 32]) / float(lam[j]))
+            if bits == 4:
+                byte = int(code_row[j // 2])
+                c = ((byte & 0xF) if j % 2 == 0 else (byte >> 4)) - 8
+            else:
+                byte = int(code_row[j])
+                c = byte - 256 if byte >= 128 else byte
+            y.append(c * float(scale_row[j // G]) / float(lam[j]))
         return [sum(R[i][c] * y[i] for i in range(D)) for c in range(D)]
     B, Hq, _ = q16.shape
     Hkv = kc.shape[1]
@@ -426,6 +577,25 @@ def check_attention_bruteforce():
 
 def test_attention_bruteforce_loops():
     check_attention_bruteforce()
+
+
+def check_attention_bruteforce_int8():
+    """Brute-force loops over int8 caches in groups of 16 and 32, and an int4
+    cache in groups of 16."""
+    D, B, Hkv, Hq, T = 32, 1, 2, 4, 5
+    q = (_rng(7).standard_normal((B, Hq, D))).astype(np.float16)
+    for bits, G in ((8, 16), (8, 32), (4, 16)):
+        kc, ks, lk, s = _tiny_cache(B, Hkv, T, D, O.SRFT, 23, G, bits)
+        vc, vs, lv, _ = _tiny_cache(B, Hkv, T, D, O.SRFT, 24, G, bits)
+        vs = vs.copy()
+        sm = 1 / math.sqrt(D)
+        got = O.attention_int4(q, kc, ks, lk, vc, vs, lv, T, sm, O.SRFT, s, G, bits)
+        want = _brute_attention(q, kc, ks, lk, vc, vs, lv, T, sm, D, s, G, bits)
+        assert np.max(np.abs(got - want)) < 1e-12, (bits, G)
+
+
+def test_attention_bruteforce_int8_group16():
+    check_attention_bruteforce_int8()
 
 
 def test_attention_special_cases():
