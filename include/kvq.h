@@ -33,6 +33,11 @@
  *     rounded to nearest even, subnormals kept; code = clamp(rint_even(w /
  *     scale), -8, 7), 0 where scale == 0; nibble = code + 8, channel 2m in
  *     the low nibble of byte m.
+ *   - variants (kvq_plan_create_ex): groups of G = 16 channels ([M3] uses
+ *     groups of 16), and int8 codes ([M2] rounds to signed int4 or int8):
+ *     scale = fp16(absmax / 127), code = clamp(rint_even(w / scale), -128,
+ *     127), stored as one two's-complement byte per channel, in channel
+ *     order.  A token's codes take D * bits / 8 bytes, its scales D / G fp16.
  *
  * Memory: every tensor pointer is a DEVICE pointer owned by the caller.  No
  * entry point allocates, frees or synchronizes; kernels are enqueued on the
@@ -94,6 +99,12 @@ const char* kvq_last_error(void);
 kvq_status kvq_plan_create(int32_t D, int32_t G, kvq_rotation rotation, uint64_t seed,
                            kvq_plan** out);
 
+/* Create a plan with a code width and group size: bits = 4 (int4 nibbles) or
+ * 8 (int8 bytes), G = 32 or 16; otherwise as kvq_plan_create, which is this
+ * call with bits = 4.  KVQ_ERR_UNSUPPORTED for other widths or groups. */
+kvq_status kvq_plan_create_ex(int32_t D, int32_t G, int32_t bits, kvq_rotation rotation, uint64_t seed,
+                              kvq_plan** out);
+
 /* Release a plan (NULL is a no-op).  Work already enqueued does not use the
  * plan object: its constants travel with each launch. */
 void kvq_plan_destroy(kvq_plan* plan);
@@ -105,12 +116,16 @@ kvq_status kvq_plan_signs(const kvq_plan* plan, int8_t* host_signs, int64_t n);
 /* Read back D, G and the rotation of a plan (any output may be NULL). */
 kvq_status kvq_plan_info(const kvq_plan* plan, int32_t* D, int32_t* G, int32_t* rotation);
 
+/* The same with the code width (4 or 8); any output may be NULL. */
+kvq_status kvq_plan_info_ex(const kvq_plan* plan, int32_t* D, int32_t* G, int32_t* bits, int32_t* rotation);
+
 /* Encode [M2]: for b < B, h < H, t < T rotate x[b,h,t,:] (fp16, element
  * (b,h,t,j) at x + b*x_sb + h*x_sh + t*x_st + j; each row 16-byte aligned),
  * multiply by lambda[b*lambda_sb + h*D + j] (fp32; lambda_sb = 0 shares one
  * [H,D] table across the batch), quantize per group and write token t0 + t of
- *   codes  uint8 [B, H, Tcap, D/2]   (dense, 16-byte aligned)
- *   scales fp16  [B, H, Tcap, D/G]   (dense, 8-byte aligned).
+ *   codes  uint8 [B, H, Tcap, D*bits/8]  (dense, 16-byte aligned; D/2 bytes
+ *                                         for int4)
+ *   scales fp16  [B, H, Tcap, D/G]       (dense, 8-byte aligned).
  * Requires 0 <= t0, t0 + T <= Tcap.  B, H or T of 0 is a no-op. */
 kvq_status kvq_encode(const kvq_plan* plan, const uint16_t* x, int64_t B, int64_t H, int64_t T,
                       int64_t x_sb, int64_t x_sh, int64_t x_st,
@@ -150,7 +165,9 @@ kvq_status kvq_attn_workspace_size(int32_t D, int64_t B, int64_t Hq, int64_t seq
  * dense; out is fp16 or fp32 [B, Hq, D] dense.  Scores are taken in the
  * rotated basis (q . k^ = ((R q) / lambda_k) . (lambda_k R k^)) and the
  * value average is rotated back once per head.  Requires Hq % Hkv == 0,
- * 1 <= seq_len <= Tcap, and a workspace of kvq_attn_workspace_size bytes. */
+ * 1 <= seq_len <= Tcap, and a workspace of kvq_attn_workspace_size bytes.
+ * Built for D = 128 with int4 codes in groups of 32; other plans return
+ * KVQ_ERR_UNSUPPORTED. */
 kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q,
                            const uint8_t* k_codes, const uint16_t* k_scales, const float* lambda_k,
                            const uint8_t* v_codes, const uint16_t* v_scales, const float* lambda_v,

@@ -7,7 +7,8 @@ missing the import of the entry points raises; there is no fallback.
 
 Method: "When Quantization Is Free: An int4 KV Cache That Outruns fp16 on
 Apple Silicon" (arXiv 2605.05699) -- sign-randomized FFT (or Walsh-Hadamard)
-rotation, per-channel lambda, group-32 abs-max fp16 scale, int4 nibbles.
+rotation, per-channel lambda, group-32 abs-max fp16 scale, int4 nibbles; int8
+codes and groups of 16 as plan variants.
 """
 
 from __future__ import annotations
@@ -62,9 +63,12 @@ def library() -> ctypes.CDLL:
         "kvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "kvq_last_error": (ctypes.c_char_p, []),
         "kvq_plan_create": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _u64, ctypes.POINTER(_vp)]),
+        "kvq_plan_create_ex": (ctypes.c_int, [_i32, _i32, _i32, ctypes.c_int, _u64, ctypes.POINTER(_vp)]),
         "kvq_plan_destroy": (None, [_vp]),
         "kvq_plan_signs": (ctypes.c_int, [_vp, _vp, _i64]),
         "kvq_plan_info": (ctypes.c_int, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+        "kvq_plan_info_ex": (ctypes.c_int, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                                            ctypes.POINTER(_i32)]),
         "kvq_encode": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _i64,
                                       _vp, _vp, _i64, _i64, _vp]),
         "kvq_decode": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64,
@@ -102,16 +106,22 @@ def _ptr(t) -> int:
 
 
 class Plan:
-    """Head dimension D, group G, rotation ("srft" | "srht" | "identity") and
-    the seed of the sign vector."""
+    """Head dimension D, group G, rotation ("srft" | "srht" | "identity"),
+    the seed of the sign vector and the code width (4: int4 nibbles, 8: int8
+    bytes)."""
 
-    def __init__(self, D: int = 128, G: int = GROUP, rotation="srft", seed: int = 0):
+    def __init__(self, D: int = 128, G: int = GROUP, rotation="srft", seed: int = 0, bits: int = 4):
         L = library()
         rot = _ROT_NAMES[rotation] if isinstance(rotation, str) else int(rotation)
         h = _vp()
-        _check(L.kvq_plan_create(D, G, rot, seed & ((1 << 64) - 1), ctypes.byref(h)))
+        _check(L.kvq_plan_create_ex(D, G, bits, rot, seed & ((1 << 64) - 1), ctypes.byref(h)))
         self._h = h
-        self.D, self.G, self.rotation, self.seed = D, G, rot, seed
+        self.D, self.G, self.rotation, self.seed, self.bits = D, G, rot, seed, bits
+
+    @property
+    def code_bytes(self) -> int:
+        """Code bytes per token."""
+        return self.D * self.bits // 8
 
     @property
     def handle(self):
@@ -129,6 +139,12 @@ class Plan:
         _check(library().kvq_plan_info(self._h, ctypes.byref(D), ctypes.byref(G), ctypes.byref(R)))
         return D.value, G.value, R.value
 
+    def info_ex(self):
+        D, G, b, R = _i32(), _i32(), _i32(), _i32()
+        _check(library().kvq_plan_info_ex(self._h, ctypes.byref(D), ctypes.byref(G), ctypes.byref(b),
+                                          ctypes.byref(R)))
+        return D.value, G.value, b.value, R.value
+
     def close(self):
         if getattr(self, "_h", None):
             library().kvq_plan_destroy(self._h)
@@ -141,9 +157,9 @@ class Plan:
             pass
 
 
-def cache_shapes(B: int, H: int, Tcap: int, D: int, G: int = GROUP):
-    """(codes shape, scales shape) of a dense int4 cache."""
-    return (B, H, Tcap, D // 2), (B, H, Tcap, D // G)
+def cache_shapes(B: int, H: int, Tcap: int, D: int, G: int = GROUP, bits: int = 4):
+    """(codes shape, scales shape) of a dense cache."""
+    return (B, H, Tcap, D * bits // 8), (B, H, Tcap, D // G)
 
 
 def _lam_args(lam, H, D):
@@ -162,13 +178,15 @@ def _x_args(x, D):
 
 def encode(plan: Plan, x, lam, codes, scales, t0: int = 0):
     """Quantize x [B, H, T, D] (fp16) into tokens t0..t0+T-1 of codes
-    [B, H, Tcap, D/2] (uint8) and scales [B, H, Tcap, D/G] (fp16)."""
+    [B, H, Tcap, D*bits/8] (uint8) and scales [B, H, Tcap, D/G] (fp16)."""
     import torch
     assert x.dtype == torch.float16 and codes.dtype == torch.uint8 and scales.dtype == torch.float16
     assert lam.dtype == torch.float32 and lam.is_contiguous()
     assert codes.is_contiguous() and scales.is_contiguous()
     B, H, T, sb, sh, st = _x_args(x, plan.D)
     Tcap = codes.shape[2]
+    assert codes.dim() == 4 and tuple(codes.shape) == (B, H, Tcap, plan.code_bytes), "codes shape"
+    assert scales.dim() == 4 and tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), "scales shape"
     _check(library().kvq_encode(plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam), _lam_args(lam, H, plan.D),
                                 _ptr(codes), _ptr(scales), Tcap, t0, _stream(x)))
 
@@ -178,6 +196,8 @@ def decode(plan: Plan, codes, scales, lam, y, t0: int = 0):
     import torch
     assert codes.is_contiguous() and scales.is_contiguous() and lam.is_contiguous()
     B, H, Tcap = codes.shape[0], codes.shape[1], codes.shape[2]
+    assert codes.dim() == 4 and codes.shape[3] == plan.code_bytes, "codes shape"
+    assert tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), "scales shape"
     assert y.dim() == 4 and y.shape[:2] == (B, H) and y.shape[3] == plan.D and y.stride(3) == 1
     dt = {torch.float16: _F16, torch.float32: _F32}[y.dtype]
     _check(library().kvq_decode(plan.handle, _ptr(codes), _ptr(scales), B, H, Tcap, t0, y.shape[2],

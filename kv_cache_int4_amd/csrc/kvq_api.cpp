@@ -20,6 +20,7 @@
 struct kvq_plan {
   int32_t D;
   int32_t G;
+  int32_t bits;
   int32_t rotation;
   uint64_t seed;
   uint64_t sign_bits[4];   // bit i of word i / 64 = 1 for sign -1
@@ -85,6 +86,8 @@ kvq_status check_plan(const kvq_plan* p) {
 
 void fill_signs(const kvq_plan* p, kvq::CodecDesc& d) {
   d.D = p->D;
+  d.G = p->G;
+  d.bits = p->bits;
   d.rotation = p->rotation;
   for (int i = 0; i < 4; ++i) d.signs[i] = p->sign_bits[i];
 }
@@ -145,18 +148,21 @@ const char* kvq_strerror(kvq_status s) {
 
 const char* kvq_last_error(void) { return g_last_error.c_str(); }
 
-kvq_status kvq_plan_create(int32_t D, int32_t G, kvq_rotation rotation, uint64_t seed, kvq_plan** out) {
+kvq_status kvq_plan_create_ex(int32_t D, int32_t G, int32_t bits, kvq_rotation rotation, uint64_t seed,
+                              kvq_plan** out) {
   try {
     if (!out) return fail(KVQ_ERR_INVALID, "out is NULL");
     *out = nullptr;
     if (rotation != KVQ_SRFT && rotation != KVQ_SRHT && rotation != KVQ_IDENTITY)
       return fail(KVQ_ERR_INVALID, "unknown rotation %d", (int)rotation);
     if (D != 128 && D != 256) return fail(KVQ_ERR_UNSUPPORTED, "D=%d (built: 128, 256)", (int)D);
-    if (G != 32) return fail(KVQ_ERR_UNSUPPORTED, "G=%d (built: 32)", (int)G);
+    if (G != 32 && G != 16) return fail(KVQ_ERR_UNSUPPORTED, "G=%d (built: 32, 16)", (int)G);
+    if (bits != 4 && bits != 8) return fail(KVQ_ERR_UNSUPPORTED, "bits=%d (built: 4, 8)", (int)bits);
     kvq_plan* p = new (std::nothrow) kvq_plan;
     if (!p) return fail(KVQ_ERR_INVALID, "out of host memory");
     p->D = D;
     p->G = G;
+    p->bits = bits;
     p->rotation = rotation;
     p->seed = seed;
     std::memset(p->sign_bits, 0, sizeof(p->sign_bits));
@@ -174,6 +180,10 @@ kvq_status kvq_plan_create(int32_t D, int32_t G, kvq_rotation rotation, uint64_t
   }
 }
 
+kvq_status kvq_plan_create(int32_t D, int32_t G, kvq_rotation rotation, uint64_t seed, kvq_plan** out) {
+  return kvq_plan_create_ex(D, G, 4, rotation, seed, out);
+}
+
 void kvq_plan_destroy(kvq_plan* plan) { delete plan; }
 
 kvq_status kvq_plan_signs(const kvq_plan* plan, int8_t* host_signs, int64_t n) {
@@ -187,9 +197,14 @@ kvq_status kvq_plan_signs(const kvq_plan* plan, int8_t* host_signs, int64_t n) {
 }
 
 kvq_status kvq_plan_info(const kvq_plan* plan, int32_t* D, int32_t* G, int32_t* rotation) {
+  return kvq_plan_info_ex(plan, D, G, nullptr, rotation);
+}
+
+kvq_status kvq_plan_info_ex(const kvq_plan* plan, int32_t* D, int32_t* G, int32_t* bits, int32_t* rotation) {
   if (kvq_status s = check_plan(plan)) return s;
   if (D) *D = plan->D;
   if (G) *G = plan->G;
+  if (bits) *bits = plan->bits;
   if (rotation) *rotation = plan->rotation;
   return ok();
 }
@@ -333,6 +348,9 @@ kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q, const uint8_
   try {
     if (kvq_status s = check_plan(plan)) return s;
     if (plan->D != 128) return fail(KVQ_ERR_UNSUPPORTED, "attention is built for D=128 (plan D=%d)", plan->D);
+    if (plan->bits != 4 || plan->G != 32)
+      return fail(KVQ_ERR_UNSUPPORTED, "attention is built for int4 codes in groups of 32 (plan: %d-bit, G=%d)",
+                  plan->bits, plan->G);
     if (kvq_status s = check_attn_common(plan->D, q, B, Hq, Hkv, Tcap, seq_len, out, out_dtype, workspace,
                                          workspace_bytes))
       return s;

@@ -15,9 +15,9 @@
 // leave through coalesced 16-byte stores.  Random signs are applied as XOR
 // masks on fp16 words where each lane's masks are fixed for the kernel.
 //
-// The general kernels (encode_kernel for rotate-only output and the D=256
-// identity encode, decode_f32_kernel for fp32 output) stage rows through
-// registers and LDS with ordinary loads.
+// The general kernels (rotate_kernel for the D=256 rotate-only output,
+// decode_f32_kernel for fp32 output) stage rows through registers and LDS
+// with ordinary loads.
 //
 // Method (gist.science explainer of "When Quantization Is Free",
 // "Methodik" 1-2): sign -> FFT over the D/2 complex pairs -> pack ->
@@ -229,10 +229,10 @@ __device__ __forceinline__ void forward_rotation(float (&v)[128], int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Encode (MODE 0) and rotate (MODE 1)
+// Rotate only, D = 256 (fp32 output, for checking): w = lambda * R x
 // ---------------------------------------------------------------------------
-template <int D, int ROT, int MODE>
-__global__ void __launch_bounds__(64, 2) encode_kernel(CodecArgs a) {
+template <int D, int ROT>
+__global__ void __launch_bounds__(64, 2) rotate_kernel(CodecArgs a) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[16384];
   const int lane = threadIdx.x;
@@ -261,74 +261,16 @@ __global__ void __launch_bounds__(64, 2) encode_kernel(CodecArgs a) {
     const int half = (D == 256) ? (lane & 1) : 0;
     const float* lam = a.lambda + t.b * a.lambda_sb + t.h * D + half * 128;
     const int vec = lane / G::L;           // vector index inside the tile
-    const bool valid = vec < t.nv;
-
-    if (MODE == 1) {
-      float* wr = a.w + ((t.row * a.T) + t.t_start + vec) * D + half * 128;
-      if (valid) {
+    float* wr = a.w + ((t.row * a.T) + t.t_start + vec) * D + half * 128;
+    if (vec < t.nv) {
 #pragma unroll
-        for (int j = 0; j < 128; j += 4) {
-          float4 o;
-          o.x = v[chan_reg<ROT>(j)] * lam[j] * kScale;
-          o.y = v[chan_reg<ROT>(j + 1)] * lam[j + 1] * kScale;
-          o.z = v[chan_reg<ROT>(j + 2)] * lam[j + 2] * kScale;
-          o.w = v[chan_reg<ROT>(j + 3)] * lam[j + 3] * kScale;
-          *reinterpret_cast<float4*>(wr + j) = o;
-        }
-      }
-    } else {
-      uint32_t cw[16];
-      uint32_t sc[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float amax = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 32; ++jj) {
-          const int j = 32 * g + jj;
-          const float wv = v[chan_reg<ROT>(j)] * lam[j];
-          v[chan_reg<ROT>(j)] = wv;
-          amax = fmaxf(amax, fabsf(wv));
-        }
-        // scale = fp16(absmax / 7): the float32 quotient, rounded to nearest
-        // even once more to fp16
-        const float amax_true = amax * kScale;
-        const uint32_t s16 = f32_to_f16_bits(amax_true / 7.0f);
-        sc[g] = s16;
-        const float sf = f16_bits_to_f32(s16);
-        const float r = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t by[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 32 * g + 8 * q + 2 * e;
-            by[e] = pair_byte(quant_bits(v[chan_reg<ROT>(j)], r), quant_bits(v[chan_reg<ROT>(j + 1)], r));
-          }
-          cw[4 * g + q] = pack4(by[0], by[1], by[2], by[3]);
-        }
-      }
-
-      // scales: 8 bytes per lane, contiguous across the tile
-      const int64_t cell = (t.row * a.Tcap + a.t0 + t.t_start);
-      if (valid) {
-        uint2 s2 = make_uint2(sc[0] | (sc[1] << 16), sc[2] | (sc[3] << 16));
-        *reinterpret_cast<uint2*>(a.scales + cell * (D / 32) + lane * 4) = s2;
-      }
-      // codes: through LDS to coalesced 16-byte stores
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        *reinterpret_cast<uint4*>(lds + code_off(lane, q)) =
-            make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
-      }
-      __syncthreads();
-      uint8_t* cbase = a.codes + cell * (D / 2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = i * 64 + lane;
-        const int r = s >> 2;
-        const int q = (s & 3) ^ ((r >> 2) & 3);
-        const uint4 o = *reinterpret_cast<const uint4*>(lds + s * 16);
-        if (r / G::L < t.nv) *reinterpret_cast<uint4*>(cbase + r * 64 + q * 16) = o;
+      for (int j = 0; j < 128; j += 4) {
+        float4 o;
+        o.x = v[chan_reg<ROT>(j)] * lam[j] * kScale;
+        o.y = v[chan_reg<ROT>(j + 1)] * lam[j + 1] * kScale;
+        o.z = v[chan_reg<ROT>(j + 2)] * lam[j + 2] * kScale;
+        o.w = v[chan_reg<ROT>(j + 3)] * lam[j + 3] * kScale;
+        *reinterpret_cast<float4*>(wr + j) = o;
       }
     }
     __syncthreads();
@@ -442,28 +384,59 @@ __device__ __forceinline__ void rotate_packed(const uint32_t (&p)[64], float (&v
   }
 }
 
-// Codes of one group of 32 channels (16 pair bytes -> 4 words) from w and
-// r = 1 / scale.  Without CLAMP the magic-number rounding alone gives the
-// code: with a normal fp16 scale |w r| <= 7 (1 + 2^-11) (1 + 2^-23) < 7.5.
-template <int ROT, bool CLAMP>
+// Code format of a plan: FMT = 2 * (bits == 8) + (G == 16).  A lane owns 128
+// channels (a D=128 vector or half a D=256 vector); these are its sizes.
+template <int FMT>
+struct Fmt {
+  static constexpr int BITS = (FMT & 2) ? 8 : 4;
+  static constexpr int G = (FMT & 1) ? 16 : 32;
+  static constexpr int NG = 128 / G;            // groups per lane
+  static constexpr int CW = 128 * BITS / 32;    // code words per lane (16 or 32)
+  static constexpr int CB = 4 * CW;             // code bytes per lane (64 or 128)
+  static constexpr int SB = 2 * NG;             // scale bytes per lane (8 or 16)
+  static constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
+};
+
+// Codes of group g (G channels) from w and r = 1 / scale: int4 as pair
+// bytes (G / 8 words), int8 as two's-complement channel bytes (G / 4 words),
+// written to cw[0 ..].  Without CLAMP the magic-number rounding alone gives
+// the code: with a normal fp16 scale |w r| <= qmax (1 + 2^-11) (1 + 2^-23) <
+// qmax + 1/2.
+template <int ROT, bool CLAMP, int FMT>
 __device__ __forceinline__ void quant_group(const float (&v)[128], int g, float r, uint32_t* cw) {
+  using F = Fmt<FMT>;
+  if (F::BITS == 4) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t by[4];
+    for (int q = 0; q < F::G / 8; ++q) {
+      uint32_t by[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 32 * g + 8 * q + 2 * e;
-      uint32_t lo, hi;
-      if (CLAMP) {
-        lo = quant_bits(v[chan_reg<ROT>(j)], r);
-        hi = quant_bits(v[chan_reg<ROT>(j + 1)], r);
-      } else {
-        lo = __builtin_bit_cast(uint32_t, fmaf(v[chan_reg<ROT>(j)], r, kMagic));
-        hi = __builtin_bit_cast(uint32_t, fmaf(v[chan_reg<ROT>(j + 1)], r, kMagic));
+      for (int e = 0; e < 4; ++e) {
+        const int j = F::G * g + 8 * q + 2 * e;
+        uint32_t lo, hi;
+        if (CLAMP) {
+          lo = quant_bits(v[chan_reg<ROT>(j)], r);
+          hi = quant_bits(v[chan_reg<ROT>(j + 1)], r);
+        } else {
+          lo = __builtin_bit_cast(uint32_t, fmaf(v[chan_reg<ROT>(j)], r, kMagic));
+          hi = __builtin_bit_cast(uint32_t, fmaf(v[chan_reg<ROT>(j + 1)], r, kMagic));
+        }
+        by[e] = pair_byte(lo, hi);
       }
-      by[e] = pair_byte(lo, hi);
+      cw[q] = pack4(by[0], by[1], by[2], by[3]);
     }
-    cw[q] = pack4(by[0], by[1], by[2], by[3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < F::G / 4; ++q) {
+      uint32_t by[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = F::G * g + 4 * q + e;
+        by[e] = CLAMP ? quant_bits8(v[chan_reg<ROT>(j)], r)
+                      : __builtin_bit_cast(uint32_t, fmaf(v[chan_reg<ROT>(j)], r, kMagic8));
+      }
+      // offset bytes q + 128 -> two's complement
+      cw[q] = pack4(by[0], by[1], by[2], by[3]) ^ 0x80808080u;
+    }
   }
 }
 
@@ -487,8 +460,25 @@ __device__ __forceinline__ uint32_t pair_mask128(const CodecArgs& a, int k) {
   return 0u;
 }
 
-template <int ROT, int MODE>
+// One lane's codes (F::CB bytes) and scales (F::SB bytes) at byte offsets
+// lane * CB and lane * SB of wave-uniform bases.
+template <typename F>
+__device__ __forceinline__ void store_lane_codes(char* cbase, char* sbase, int lane, const uint4 (&c)[F::CB / 16],
+                                                 const uint32_t (&sw)[F::NG / 2]) {
+  if (F::NG == 4) {
+    *reinterpret_cast<uint2*>(sbase + static_cast<uint32_t>(lane * F::SB)) = make_uint2(sw[0], sw[1]);
+  } else {
+    *reinterpret_cast<uint4*>(sbase + static_cast<uint32_t>(lane * F::SB)) =
+        make_uint4(sw[0], sw[1 % (F::NG / 2)], sw[2 % (F::NG / 2)], sw[3 % (F::NG / 2)]);
+  }
+#pragma unroll
+  for (int q = 0; q < F::CB / 16; ++q)
+    *reinterpret_cast<uint4*>(cbase + static_cast<uint32_t>(lane * F::CB + 16 * q)) = c[q];
+}
+
+template <int ROT, int MODE, int FMT>
 __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
+  using F = Fmt<FMT>;
   // separate LDS objects, so that reads of the masks and of lambda need not
   // wait for the direct loads into the tile
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
@@ -520,8 +510,8 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
   // codes and scales of the previous tile, stored only after the next tile's
   // loads are on their way (so that the wait for those loads at the top of
   // the loop never waits on fresh stores)
-  uint4 pend_c[4] = {};
-  uint2 pend_s = {};
+  uint4 pend_c[F::CB / 16] = {};
+  uint32_t pend_s[F::NG / 2] = {};
   bool pend_valid = false;
   char* pend_cbase = nullptr;
   char* pend_sbase = nullptr;
@@ -553,12 +543,7 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
       lam_r0 = lr[lane];
       lam_r1 = lr[lane + 64];
     }
-    if (MODE == 0 && pend_valid) {
-      *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint4*>(pend_cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) = pend_c[q];
-    }
+    if (MODE == 0 && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 
     float v[128];
     rotate_packed<ROT>(p, v);
@@ -583,16 +568,16 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
         }
       }
     } else {
-      float r[4];
-      uint32_t sc[4];
+      float r[F::NG];
+      uint32_t sc[F::NG];
       bool tiny = false;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < F::NG; ++g) {
         asm volatile("" ::: "memory");    // one group's lambda reads at a time
         float amax = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 32; jj += 4) {
-          const int j = 32 * g + jj;
+        for (int jj = 0; jj < F::G; jj += 4) {
+          const int j = F::G * g + jj;
           const float4 l4 = lam4[j / 4];
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
@@ -602,38 +587,36 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
             amax = fmaxf(amax, fabsf(wv));
           }
         }
-        // scale = fp16(absmax / 7), from absmax * fp32(1/7): the product is
-        // within an fp32 ulp of the quotient, so the fp16 rounding differs
-        // from the exact quotient's only within ~1e-7 (relative) of an fp16
-        // rounding midpoint
-        sc[g] = f32_to_f16_bits(amax * (kScale * (1.0f / 7.0f)));
+        // scale = fp16(absmax / qmax), from absmax * fp32(1/qmax): the
+        // product is within an fp32 ulp of the quotient, so the fp16 rounding
+        // differs from the exact quotient's only within ~1e-7 (relative) of
+        // an fp16 rounding midpoint
+        sc[g] = f32_to_f16_bits(amax * (kScale * (1.0f / F::QMAX)));
         const float sf = f16_bits_to_f32(sc[g]);
         r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
         tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);    // fp16-subnormal scale
       }
-      uint32_t cw[16];
+      uint32_t cw[F::CW];
+      constexpr int kWordsPerGroup = F::CW / F::NG;
       if (__builtin_amdgcn_ballot_w64(tiny && valid) == 0) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) quant_group<ROT, false>(v, g, r[g], cw + 4 * g);
+        for (int g = 0; g < F::NG; ++g) quant_group<ROT, false, FMT>(v, g, r[g], cw + kWordsPerGroup * g);
       } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) quant_group<ROT, true>(v, g, r[g], cw + 4 * g);
+        for (int g = 0; g < F::NG; ++g) quant_group<ROT, true, FMT>(v, g, r[g], cw + kWordsPerGroup * g);
       }
       const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;   // wave-uniform
-      pend_sbase = reinterpret_cast<char*>(a.scales + cell0 * 4);
-      pend_cbase = reinterpret_cast<char*>(a.codes + cell0 * 64);
-      pend_s = make_uint2(sc[0] | (sc[1] << 16), sc[2] | (sc[3] << 16));
+      pend_sbase = reinterpret_cast<char*>(a.scales + cell0 * F::NG);
+      pend_cbase = reinterpret_cast<char*>(a.codes + cell0 * F::CB);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pend_c[q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+      for (int i = 0; i < F::NG / 2; ++i) pend_s[i] = sc[2 * i] | (sc[2 * i + 1] << 16);
+#pragma unroll
+      for (int q = 0; q < F::CB / 16; ++q)
+        pend_c[q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
       pend_valid = valid;
     }
   }
-  if (MODE == 0 && pend_valid) {
-    *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<uint4*>(pend_cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) = pend_c[q];
-  }
+  if (MODE == 0 && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -683,8 +666,9 @@ __device__ __forceinline__ uint32_t pair_mask256(const CodecArgs& a, int h, int 
   return 0u;
 }
 
-template <int ROT>
+template <int ROT, int FMT>
 __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
+  using F = Fmt<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
   __shared__ __attribute__((aligned(16))) uint32_t mask_lds[128];   // [h][k]
   __shared__ __attribute__((aligned(16))) float lam_lds[256];       // [h][local channel], sign folded
@@ -692,6 +676,9 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
   const int hh = lane & 1;                  // half of the vector
   constexpr float kScale = rot_scale<256, ROT>();
   const float sgn = hh ? -1.f : 1.f;
+  // the butterfly across the pair leaves the odd lane's half negated
+  // (rotations only); its lambda half carries the sign back
+  constexpr bool kPair = ROT != KVQ_ROT_ID;
 
   mask_lds[lane] = pair_mask256<ROT>(a, 0, lane);
   mask_lds[64 + lane] = pair_mask256<ROT>(a, 1, lane);
@@ -712,8 +699,8 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     for (int q = 0; q < 4; ++q) lam_r[q] = lr[lane + 64 * q];
   }
   __syncthreads();
-  uint4 pend_c[4] = {};
-  uint2 pend_s = {};
+  uint4 pend_c[F::CB / 16] = {};
+  uint32_t pend_s[F::NG / 2] = {};
   bool pend_valid = false;
   char* pend_cbase = nullptr;
   char* pend_sbase = nullptr;
@@ -723,7 +710,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     // them is a store of the tile before, a transform ago)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lam_lds[lane + 64 * q] = (q < 2 ? 1.f : -1.f) * lam_r[q];
+    for (int q = 0; q < 4; ++q) lam_lds[lane + 64 * q] = (q < 2 || !kPair ? 1.f : -1.f) * lam_r[q];
     uint32_t p[64];
     const uint4* masks = reinterpret_cast<const uint4*>(mask_lds);   // [hh * 16 + j]
     if (ROT == KVQ_ROT_SRFT) {
@@ -760,12 +747,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) lam_r[q] = lr[lane + 64 * q];
     }
-    if (pend_valid) {
-      *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint4*>(pend_cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) = pend_c[q];
-    }
+    if (pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 
     float v[128];
     if (ROT == KVQ_ROT_SRFT) {
@@ -782,8 +764,10 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
         v[2 * k] = f16_bits_to_f32(p[k] & 0xFFFFu);
         v[2 * k + 1] = f16_bits_to_f32(p[k] >> 16);
       }
+      if (kPair) {
 #pragma unroll
-      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+        for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+      }
       if (ROT == KVQ_ROT_SRHT) wht128(v);
     }
     // keep the lambda reads below the transform
@@ -791,16 +775,16 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     const float4* lam4 = reinterpret_cast<const float4*>(lam_lds);   // [hh * 32 + j / 4]
     const bool valid = (lane >> 1) < t.nv;
 
-    float r[4];
-    uint32_t sc[4];
+    float r[F::NG];
+    uint32_t sc[F::NG];
     bool tiny = false;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < F::NG; ++g) {
       asm volatile("" ::: "memory");
       float amax = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < 32; jj += 4) {
-        const int j = 32 * g + jj;
+      for (int jj = 0; jj < F::G; jj += 4) {
+        const int j = F::G * g + jj;
         const float4 l4 = lam4[32 * hh + j / 4];
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
@@ -810,35 +794,33 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
           amax = fmaxf(amax, fabsf(wv));
         }
       }
-      sc[g] = f32_to_f16_bits(amax * (kScale * (1.0f / 7.0f)));
+      sc[g] = f32_to_f16_bits(amax * (kScale * (1.0f / F::QMAX)));
       const float sf = f16_bits_to_f32(sc[g]);
       r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
       tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);
     }
-    uint32_t cw[16];
+    uint32_t cw[F::CW];
+    constexpr int kWordsPerGroup = F::CW / F::NG;
     if (__builtin_amdgcn_ballot_w64(tiny && valid) == 0) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) quant_group<ROT, false>(v, g, r[g], cw + 4 * g);
+      for (int g = 0; g < F::NG; ++g) quant_group<ROT, false, FMT>(v, g, r[g], cw + kWordsPerGroup * g);
     } else {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) quant_group<ROT, true>(v, g, r[g], cw + 4 * g);
+      for (int g = 0; g < F::NG; ++g) quant_group<ROT, true, FMT>(v, g, r[g], cw + kWordsPerGroup * g);
     }
-    // lane 2v + h: codes bytes 64h .. 64h + 63 and scales 4h .. 4h + 3 of
-    // vector v, i.e. 64 and 8 contiguous bytes at lane * 64, lane * 8
+    // lane 2v + h: the code and scale bytes of half h of vector v, i.e. CB
+    // and SB contiguous bytes at lane * CB, lane * SB
     const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;   // wave-uniform
-    pend_sbase = reinterpret_cast<char*>(a.scales + cell0 * 8);
-    pend_cbase = reinterpret_cast<char*>(a.codes + cell0 * 128);
-    pend_s = make_uint2(sc[0] | (sc[1] << 16), sc[2] | (sc[3] << 16));
+    pend_sbase = reinterpret_cast<char*>(a.scales + cell0 * 2 * F::NG);
+    pend_cbase = reinterpret_cast<char*>(a.codes + cell0 * 2 * F::CB);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) pend_c[q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+    for (int i = 0; i < F::NG / 2; ++i) pend_s[i] = sc[2 * i] | (sc[2 * i + 1] << 16);
+#pragma unroll
+    for (int q = 0; q < F::CB / 16; ++q)
+      pend_c[q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
     pend_valid = valid;
   }
-  if (pend_valid) {
-    *reinterpret_cast<uint2*>(pend_sbase + static_cast<uint32_t>(lane * 8)) = pend_s;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<uint4*>(pend_cbase + static_cast<uint32_t>(lane * 64 + 16 * q)) = pend_c[q];
-  }
+  if (pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -846,11 +828,15 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
 // arrive in LDS by direct loads while the current tile computes; the fp16
 // rows leave through a 9 KiB LDS stage, one half-row (64 channels) at a time.
 // ---------------------------------------------------------------------------
-// Direct-load targets (one LDS object) ...
-constexpr int kDecCodes = 0;             // 4 KiB: 64 code rows of 64 B, swizzled
-constexpr int kDecScales = 4096;         // 512 B
-constexpr int kDecLam = 4608;            // 512 B
-constexpr int kLdsDecIn = 5120;
+// Direct-load targets (one LDS object): 64 code rows of F::CB bytes
+// (swizzled), their scales (F::SB each) and the lambda row ...
+template <typename F>
+struct DecIn {
+  static constexpr int kCodes = 0;
+  static constexpr int kScales = 64 * F::CB;
+  static constexpr int kLam = kScales + 64 * F::SB;
+  static constexpr int kBytes = kLam + 512;
+};
 // ... and the LDS the compute phase uses (another object, so that its reads
 // need not wait for the direct loads in flight)
 constexpr int kDecRl = 0;                // 512 B: unitary scale / lambda
@@ -858,26 +844,52 @@ constexpr int kDecOut = 512;             // 9 KiB: half rows of 128 B at a 144 B
 constexpr int kDecPitch = 144;           // 16 B of padding: conflict-free both ways
 constexpr int kLdsDecWork = kDecOut + 64 * kDecPitch;
 
-__device__ __forceinline__ void dma_codes128(const CodecArgs& a, const Tile& t, uint8_t* lds, int lane) {
+// LDS byte offset of 16-byte chunk q of the code row of lane r: rows of 4
+// chunks (int4) or 8 chunks (int8), the chunk index XOR-swizzled with the
+// row so that a lane-parallel read of one chunk spreads over the banks.
+template <typename F>
+__device__ __forceinline__ uint32_t code_off_f(int r, int q) {
+  if (F::CB == 64) return code_off(r, q);
+  return static_cast<uint32_t>(r * 128 + (((q ^ r) & 7) << 4));
+}
+
+template <typename F>
+__device__ __forceinline__ void dma_codes128(const CodecArgs& a, const Tile& t, lds_u8* lds, int lane) {
+  using L = DecIn<F>;
   const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;
-  const char* cb = reinterpret_cast<const char*>(a.codes_in + cell0 * 64);
-  const char* sb = reinterpret_cast<const char*>(a.scales_in + cell0 * 4);
-  // slot 64 i + lane holds chunk q of vector v, at code_off(v, q)
+  const char* cb = reinterpret_cast<const char*>(a.codes_in + cell0 * F::CB);
+  const char* sb = reinterpret_cast<const char*>(a.scales_in + cell0 * F::NG);
+  constexpr int kRowsPerLoad = 1024 / F::CB;       // code rows per 64-lane load
+  constexpr int kChunks = F::CB / 16;
+  // (every pointer goes through a local first: inside a template the
+  // direct-load builtin rejects value-dependent pointer expressions)
+  // slot 64 i + lane holds chunk q of vector v, at code_off_f(v, q)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = 16 * i + (lane >> 2);
-    const int q = (lane & 3) ^ ((v >> 2) & 3);
-    if (v < t.nv)
-      __builtin_amdgcn_global_load_lds(cb + static_cast<uint32_t>(64 * v + 16 * q), lds + kDecCodes + 1024 * i, 16, 0, 0);
+  for (int i = 0; i < 64 / kRowsPerLoad; ++i) {
+    const int v = kRowsPerLoad * i + lane / kChunks;
+    const int p = lane % kChunks;                  // position in the LDS row
+    const int q = F::CB == 64 ? p ^ ((v >> 2) & 3) : (p ^ v) & 7;
+    const char* g = cb + static_cast<uint32_t>(F::CB * v + 16 * q);
+    lds_u8* l = lds + L::kCodes + 1024 * i;
+    if (v < t.nv) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
   }
-  // scales: one dword (two scales) per lane and instruction
+  if (F::SB == 8) {
+    // scales: one dword (two scales) per lane and instruction
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (32 * i + (lane >> 1) < t.nv)
-      __builtin_amdgcn_global_load_lds(sb + static_cast<uint32_t>(256 * i + 4 * lane), lds + kDecScales + 256 * i, 4, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const char* g = sb + static_cast<uint32_t>(256 * i + 4 * lane);
+      lds_u8* l = lds + L::kScales + 256 * i;
+      if (32 * i + (lane >> 1) < t.nv) __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+    }
+  } else {
+    // 16 bytes of scales per vector, one vector per lane
+    const char* g = sb + static_cast<uint32_t>(16 * lane);
+    lds_u8* l = lds + L::kScales;
+    if (lane < t.nv) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
   }
-  if (lane < 32)
-    __builtin_amdgcn_global_load_lds(a.lambda + t.b * a.lambda_sb + t.h * 128 + 4 * lane, lds + kDecLam, 16, 0, 0);
+  const float* gl = a.lambda + t.b * a.lambda_sb + t.h * 128 + 4 * lane;
+  lds_u8* ll = lds + L::kLam;
+  if (lane < 32) __builtin_amdgcn_global_load_lds(gl, ll, 16, 0, 0);
 }
 
 // The kernels of this file run one wave per workgroup, and a wave's LDS
@@ -886,10 +898,70 @@ __device__ __forceinline__ void dma_codes128(const CodecArgs& a, const Tile& t, 
 // the vector-memory counter, i.e. for the next tile's direct loads.)
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int ROT>
-__global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
+// code * scale * rl for the lane's 128 channels.  cw holds the lane's code
+// words, whose channels are v[8d ..] (int4: byte b of word d holds v[8d+2b]
+// low and v[8d+2b+1] high; the word is unpacked as channel pairs (0,4),
+// (1,5), (2,6), (3,7)) or v[4d ..] (int8: byte e of word d is v[4d+e]); runs
+// of DPG consecutive words share one scale, s16[d / DPG]; rl4 (LDS) holds the
+// per-channel factor (unitary scale / lambda) of v[j] at float j.
+//   int4: (n - 8) * scale exactly: the nibble under the exponent of 1024 is
+//         the fp16 number 1024 + n (low nibble of a byte) or 1024 + 16 n
+//         (high nibble); one fma_mix removes the bias.
+//   int8: the byte with its top bit flipped is q + 128 (v_cvt_f32_ubyte),
+//         one fma removes the bias.
+template <typename F, int DPG>
+__device__ __forceinline__ void dequant_lane(const uint32_t (&cw)[F::CW], const uint32_t* s16, const float4* rl4,
+                                             uint32_t magic, float (&v)[128]) {
   typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsDecIn];
+#pragma unroll
+  for (int g = 0; g < F::CW / DPG; ++g) {
+    // one group's rl reads at a time (hoisted, they would hold 128 registers)
+    asm volatile("" ::: "memory");
+    const float sg = f16_bits_to_f32(s16[g]);
+    if (F::BITS == 4) {
+      const float m_lo = -1032.f * sg;
+      const float sg16 = sg * 0.0625f;
+      const float m_hi = -72.f * sg;       // -1152 * sg / 16
+#pragma unroll
+      for (int k = 0; k < DPG; ++k) {
+        const int d = DPG * g + k;
+        const uint32_t x = cw[d], y = x >> 8;
+        const h2_t h0 = __builtin_bit_cast(h2_t, (x & 0x000F000Fu) | magic);   // channels 0, 4
+        const h2_t h1 = __builtin_bit_cast(h2_t, (x & 0x00F000F0u) | magic);   // channels 1, 5
+        const h2_t h2 = __builtin_bit_cast(h2_t, (y & 0x000F000Fu) | magic);   // channels 2, 6
+        const h2_t h3 = __builtin_bit_cast(h2_t, (y & 0x00F000F0u) | magic);   // channels 3, 7
+        const int j = 8 * d;
+        const float4 ra = rl4[2 * d], rb = rl4[2 * d + 1];
+        v[j] = fmaf(static_cast<float>(h0[0]), sg, m_lo) * ra.x;
+        v[j + 1] = fmaf(static_cast<float>(h1[0]), sg16, m_hi) * ra.y;
+        v[j + 2] = fmaf(static_cast<float>(h2[0]), sg, m_lo) * ra.z;
+        v[j + 3] = fmaf(static_cast<float>(h3[0]), sg16, m_hi) * ra.w;
+        v[j + 4] = fmaf(static_cast<float>(h0[1]), sg, m_lo) * rb.x;
+        v[j + 5] = fmaf(static_cast<float>(h1[1]), sg16, m_hi) * rb.y;
+        v[j + 6] = fmaf(static_cast<float>(h2[1]), sg, m_lo) * rb.z;
+        v[j + 7] = fmaf(static_cast<float>(h3[1]), sg16, m_hi) * rb.w;
+      }
+    } else {
+      const float m = -128.f * sg;
+#pragma unroll
+      for (int k = 0; k < DPG; ++k) {
+        const int d = DPG * g + k;
+        const uint32_t x = cw[d] ^ 0x80808080u;
+        const float4 ra = rl4[d];
+        v[4 * d] = fmaf(static_cast<float>(x & 0xFFu), sg, m) * ra.x;
+        v[4 * d + 1] = fmaf(static_cast<float>((x >> 8) & 0xFFu), sg, m) * ra.y;
+        v[4 * d + 2] = fmaf(static_cast<float>((x >> 16) & 0xFFu), sg, m) * ra.z;
+        v[4 * d + 3] = fmaf(static_cast<float>(x >> 24), sg, m) * ra.w;
+      }
+    }
+  }
+}
+
+template <int ROT, int FMT>
+__global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
+  using F = Fmt<FMT>;
+  using L = DecIn<F>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t work[kLdsDecWork];
   const int lane = threadIdx.x;
   constexpr float kScale = rot_scale<128, ROT>();
@@ -900,60 +972,39 @@ __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
   const int64_t out_step = 16 * a.st;     // bytes of eight rows
 
   int64_t tile = blockIdx.x;
-  if (tile < a.n_tiles) dma_codes128(a, tile_info<128>(a, tile), lds, lane);
+  if (tile < a.n_tiles) dma_codes128<F>(a, tile_info<128>(a, tile), (lds_u8*)lds, lane);
   __syncthreads();
   for (; tile < a.n_tiles; tile += gridDim.x) {
     const Tile t = tile_info<128>(a, tile);
-    uint32_t cw[16];
+    uint32_t cw[F::CW];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 w = *reinterpret_cast<const uint4*>(lds + kDecCodes + code_off(lane, q));
+    for (int q = 0; q < F::CB / 16; ++q) {
+      const uint4 w = *reinterpret_cast<const uint4*>(lds + L::kCodes + code_off_f<F>(lane, q));
       cw[4 * q] = w.x; cw[4 * q + 1] = w.y; cw[4 * q + 2] = w.z; cw[4 * q + 3] = w.w;
     }
-    const uint2 s2 = *reinterpret_cast<const uint2*>(lds + kDecScales + 8 * lane);
-    const float l0 = reinterpret_cast<const float*>(lds + kDecLam)[lane];
-    const float l1 = reinterpret_cast<const float*>(lds + kDecLam)[lane + 64];
+    uint32_t s16[F::NG];
+    if (F::SB == 8) {
+      const uint2 s2 = *reinterpret_cast<const uint2*>(lds + L::kScales + 8 * lane);
+      const uint32_t sw[2] = {s2.x, s2.y};
+#pragma unroll
+      for (int i = 0; i < F::NG; ++i) s16[i] = (sw[(i / 2) % 2] >> (16 * (i % 2))) & 0xFFFFu;
+    } else {
+      const uint4 s4 = *reinterpret_cast<const uint4*>(lds + L::kScales + 16 * lane);
+      const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int i = 0; i < F::NG; ++i) s16[i] = (sw[(i / 2) % 4] >> (16 * (i % 2))) & 0xFFFFu;
+    }
+    const float l0 = reinterpret_cast<const float*>(lds + L::kLam)[lane];
+    const float l1 = reinterpret_cast<const float*>(lds + L::kLam)[lane + 64];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t nxt = tile + gridDim.x;
-    if (nxt < a.n_tiles) dma_codes128(a, tile_info<128>(a, nxt), lds, lane);
+    if (nxt < a.n_tiles) dma_codes128<F>(a, tile_info<128>(a, nxt), (lds_u8*)lds, lane);
     reinterpret_cast<float*>(work + kDecRl)[lane] = kScale * __builtin_amdgcn_rcpf(l0);
     reinterpret_cast<float*>(work + kDecRl)[lane + 64] = kScale * __builtin_amdgcn_rcpf(l1);
     lds_sync();
 
-    // (n - 8) * scale exactly: the nibble under the exponent of 1024 is the
-    // fp16 number 1024 + n (low nibble of a byte) or 1024 + 16 n (high
-    // nibble); one fma_mix removes the bias.  Then * (unitary scale / lambda).
-    const float4* rl4 = reinterpret_cast<const float4*>(work + kDecRl);
-    const uint32_t s16[4] = {s2.x & 0xFFFFu, s2.x >> 16, s2.y & 0xFFFFu, s2.y >> 16};
     float v[128];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // one group's 1/lambda reads at a time (hoisted, they would hold 128
-      // registers)
-      asm volatile("" ::: "memory");
-      const float sg = f16_bits_to_f32(s16[g]);
-      const float m_lo = -1032.f * sg;
-      const float sg16 = sg * 0.0625f;
-      const float m_hi = -72.f * sg;       // -1152 * sg / 16
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t x = cw[4 * g + k], y = x >> 8;
-        const h2_t h0 = __builtin_bit_cast(h2_t, (x & 0x000F000Fu) | magic);   // channels 0, 4
-        const h2_t h1 = __builtin_bit_cast(h2_t, (x & 0x00F000F0u) | magic);   // channels 1, 5
-        const h2_t h2 = __builtin_bit_cast(h2_t, (y & 0x000F000Fu) | magic);   // channels 2, 6
-        const h2_t h3 = __builtin_bit_cast(h2_t, (y & 0x00F000F0u) | magic);   // channels 3, 7
-        const int j = 32 * g + 8 * k;
-        const float4 ra = rl4[j / 4], rb = rl4[j / 4 + 1];
-        v[j] = fmaf(static_cast<float>(h0[0]), sg, m_lo) * ra.x;
-        v[j + 1] = fmaf(static_cast<float>(h1[0]), sg16, m_hi) * ra.y;
-        v[j + 2] = fmaf(static_cast<float>(h2[0]), sg, m_lo) * ra.z;
-        v[j + 3] = fmaf(static_cast<float>(h3[0]), sg16, m_hi) * ra.w;
-        v[j + 4] = fmaf(static_cast<float>(h0[1]), sg, m_lo) * rb.x;
-        v[j + 5] = fmaf(static_cast<float>(h1[1]), sg16, m_hi) * rb.y;
-        v[j + 6] = fmaf(static_cast<float>(h2[1]), sg, m_lo) * rb.z;
-        v[j + 7] = fmaf(static_cast<float>(h3[1]), sg16, m_hi) * rb.w;
-      }
-    }
+    dequant_lane<F, F::CW / F::NG>(cw, s16, reinterpret_cast<const float4*>(work + kDecRl), magic, v);
 
     if (ROT == KVQ_ROT_SRFT) fft64<true>(v);
     else if (ROT == KVQ_ROT_SRHT) wht128(v);
@@ -1009,47 +1060,75 @@ __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
 // butterfly computes own + sign * partner; the odd lane's half of the
 // 1 / lambda table is negated so that both lanes end with the plain result.
 // ---------------------------------------------------------------------------
-constexpr int kDec2Lam = 4608;           // 1 KiB lambda row (codes, scales as for D = 128)
-constexpr int kLdsDec2In = 5632;
+// Direct-load targets: 32 code rows of 2 F::CB bytes (R = F::CB / 8 chunks
+// of 16 bytes; chunk q of vector v at LDS byte 2 CB v + 16 ((q ^ v) % R), so
+// that a lane-parallel read of one chunk of consecutive rows spans the
+// banks), their scales (2 F::SB bytes each) and the 1 KiB lambda row; the
+// compute side's 1/lambda table and output stage.
+template <typename F>
+struct DecIn256 {
+  static constexpr int kCodes = 0;
+  static constexpr int kScales = 64 * F::CB;
+  static constexpr int kLam = kScales + 64 * F::SB;
+  static constexpr int kBytes = kLam + 1024;
+};
 constexpr int kDec2Rl = 0;               // 1 KiB: [h][local channel] unitary scale / lambda
 constexpr int kDec2Out = 1024;           // 9 KiB staging, rows = half vectors
 constexpr int kLdsDec2Work = kDec2Out + 64 * kDecPitch;
 
-// Slot 64 i + lane: chunk q of vector v = 8 i + lane / 8, stored at LDS byte
-// 128 v + 16 ((q ^ v) % 8) (a lane-parallel read of one chunk of eight rows
-// then spans all banks).
+template <typename F>
 __device__ __forceinline__ void dma_codes256(const CodecArgs& a, const Tile& t, lds_u8* lds, int lane_in) {
+  using L = DecIn256<F>;
   // the lane's offsets are recomputed per call (a few integer operations):
   // hoisted out of the tile loop they would hold registers the transform
   // needs, and their spill reloads would wait on the loads just issued
   int lane = lane_in;
   asm volatile("" : "+v"(lane));
   const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;
-  const char* cb = reinterpret_cast<const char*>(a.codes_in + cell0 * 128);
-  const char* sb = reinterpret_cast<const char*>(a.scales_in + cell0 * 8);
-  const uint32_t off = static_cast<uint32_t>(128 * (lane >> 3) + 16 * ((lane & 7) ^ ((lane >> 3) & 7)));
+  const char* cb = reinterpret_cast<const char*>(a.codes_in + cell0 * 2 * F::CB);
+  const char* sb = reinterpret_cast<const char*>(a.scales_in + cell0 * 2 * F::NG);
   const uint32_t off16 = static_cast<uint32_t>(16 * lane);
-  // the instruction offset (1 KiB per slot row) advances the global and the
-  // LDS address alike
-  const char* g = cb + off;
-  lds_u8* l = lds + kDecCodes;
-  if (t.nv == 32) {
-    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(g, l, 16, 1024, 0);
-    __builtin_amdgcn_global_load_lds(g, l, 16, 2048, 0);
-    __builtin_amdgcn_global_load_lds(g, l, 16, 3072, 0);
+  // (every pointer goes through a local first: inside a template the
+  // direct-load builtin rejects value-dependent pointer expressions)
+  lds_u8* l = lds + L::kCodes;
+  if (F::CB == 64) {
+    // slot 64 i + lane: row 8 i + lane / 8, LDS position lane % 8; the lane's
+    // global offset is the same for every i, and the instruction offset
+    // (1 KiB per slot row) advances the global and the LDS address alike
+    const uint32_t off = static_cast<uint32_t>(128 * (lane >> 3) + 16 * ((lane & 7) ^ ((lane >> 3) & 7)));
+    const char* g = cb + off;
+    if (t.nv == 32) {
+      __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(g, l, 16, 1024, 0);
+      __builtin_amdgcn_global_load_lds(g, l, 16, 2048, 0);
+      __builtin_amdgcn_global_load_lds(g, l, 16, 3072, 0);
+    } else {
+      // vector 8 i + lane / 8: one lane value against a wave-uniform bound
+      const int r = lane >> 3;
+      if (r < t.nv) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+      if (r < t.nv - 8) __builtin_amdgcn_global_load_lds(g, l, 16, 1024, 0);
+      if (r < t.nv - 16) __builtin_amdgcn_global_load_lds(g, l, 16, 2048, 0);
+      if (r < t.nv - 24) __builtin_amdgcn_global_load_lds(g, l, 16, 3072, 0);
+    }
   } else {
-    // vector 8 i + lane / 8: one lane value against a wave-uniform bound
-    const int r = lane >> 3;
-    if (r < t.nv) __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-    if (r < t.nv - 8) __builtin_amdgcn_global_load_lds(g, l, 16, 1024, 0);
-    if (r < t.nv - 16) __builtin_amdgcn_global_load_lds(g, l, 16, 2048, 0);
-    if (r < t.nv - 24) __builtin_amdgcn_global_load_lds(g, l, 16, 3072, 0);
+    // 256-byte rows: slot 64 i + lane is row 4 i + lane / 16, LDS position
+    // lane % 16, global chunk (lane % 16) ^ row (mod 16)
+    const int vr = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t off = static_cast<uint32_t>(256 * vr + 16 * ((p ^ (4 * i + vr)) & 15));
+      const char* g = cb + 1024 * i + off;
+      lds_u8* li = l + 1024 * i;
+      if (vr < t.nv - 4 * i) __builtin_amdgcn_global_load_lds(g, li, 16, 0, 0);
+    }
   }
-  // 16 bytes of scales per vector: lanes below nv (at most 32)
-  if (lane < t.nv) __builtin_amdgcn_global_load_lds(sb + off16, lds + kDecScales, 16, 0, 0);
-  const char* lr = reinterpret_cast<const char*>(a.lambda + t.b * a.lambda_sb + t.h * 256);
-  __builtin_amdgcn_global_load_lds(lr + off16, lds + kDec2Lam, 16, 0, 0);
+  // 2 F::SB bytes of scales per vector: 16 per lane
+  const char* gs = sb + off16;
+  lds_u8* ls = lds + L::kScales;
+  if (lane < t.nv * (2 * F::SB / 16)) __builtin_amdgcn_global_load_lds(gs, ls, 16, 0, 0);
+  const char* gl = reinterpret_cast<const char*>(a.lambda + t.b * a.lambda_sb + t.h * 256) + off16;
+  lds_u8* ll = lds + L::kLam;
+  __builtin_amdgcn_global_load_lds(gl, ll, 16, 0, 0);
 }
 
 __device__ __forceinline__ uint64_t sign_word(const CodecArgs& a, int i) {
@@ -1068,20 +1147,30 @@ __device__ __forceinline__ uint32_t out_mask256(const CodecArgs& a, int kg) {
   return 0u;
 }
 
-template <int ROT>
+template <int ROT, int FMT>
 __global__ void __launch_bounds__(64, 2) decode256_kernel(CodecArgs a) {
-  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsDec2In];
+  using F = Fmt<FMT>;
+  using L = DecIn256<F>;
+  constexpr int R = F::CB / 8;              // 16-byte chunks per code row
+  // SRFT lanes see every scale of their vector, through code words of DPG
+  // words per group (int4: 4 frequencies = 8 channels in 4 code bytes per
+  // word; int8: 2 frequencies per word); the others their half's scales
+  constexpr int DPG = ROT == KVQ_ROT_SRFT ? F::G * F::BITS / 64 : F::CW / F::NG;
+  constexpr int NS = F::CW / DPG;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t work[kLdsDec2Work];
   const int lane = threadIdx.x;
   const int hh = lane & 1;                  // half of the vector
   const int vec = lane >> 1;
   constexpr float kScale = rot_scale<256, ROT>();
+  constexpr bool kPair = ROT != KVQ_ROT_ID;
   const float sgn = hh ? 1.f : -1.f;
   uint32_t magic;   // fp16 pair (1024, 1024): a register operand for v_and_or
   asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
-  // bytes h, h + 2 of two code dwords: frequencies 2m + h
-  const uint32_t sel = 0x06040200u + 0x01010101u * static_cast<uint32_t>(hh);
+  // int4: bytes h, h + 2 of two code dwords (frequencies 2m + h); int8:
+  // half-word h of two code dwords (both bytes of frequency 2m + h)
+  const uint32_t sel = F::BITS == 4 ? 0x06040200u + 0x01010101u * static_cast<uint32_t>(hh)
+                                    : 0x05040100u + 0x02020202u * static_cast<uint32_t>(hh);
 
   // where this lane's lambda entries c = lane + 64 q go in the 1 / lambda
   // table, and their sign (negated on the odd half)
@@ -1094,7 +1183,7 @@ __global__ void __launch_bounds__(64, 2) decode256_kernel(CodecArgs a) {
     if (ROT == KVQ_ROT_SRFT) { h = (c >> 1) & 1; j = 2 * (c >> 2) + (c & 1); }
     else { h = c >> 7; j = c & 127; }
     rl_dst[q] = static_cast<uint32_t>(4 * (128 * h + j));
-    rl_mul[q] = (ROT != KVQ_ROT_ID && h) ? -kScale : kScale;
+    rl_mul[q] = (kPair && h) ? -kScale : kScale;
   }
 
   // rows 8 i + lane / 8 of a half-row pass: vector 4 i + lane / 16, half
@@ -1103,73 +1192,61 @@ __global__ void __launch_bounds__(64, 2) decode256_kernel(CodecArgs a) {
   const int64_t out_step = 8 * a.st;      // bytes of four vectors
 
   int64_t tile = blockIdx.x;
-  if (tile < a.n_tiles) dma_codes256(a, tile_info<256>(a, tile), (lds_u8*)lds, lane);
+  if (tile < a.n_tiles) dma_codes256<F>(a, tile_info<256>(a, tile), (lds_u8*)lds, lane);
   __syncthreads();
   for (; tile < a.n_tiles; tile += gridDim.x) {
     const Tile t = tile_info<256>(a, tile);
-    uint32_t cw[16];
-    uint32_t s16[8];
-    const uint8_t* crow = lds + kDecCodes + 128 * vec;
+    uint32_t cw[F::CW];
+    uint32_t s16[NS];
+    const uint8_t* crow = lds + L::kCodes + 2 * F::CB * vec;
+    const uint8_t* srow = lds + L::kScales + 2 * F::SB * vec;
     if (ROT == KVQ_ROT_SRFT) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint4 w = *reinterpret_cast<const uint4*>(crow + 16 * (q ^ (vec & 7)));
+      for (int q = 0; q < R; ++q) {
+        const uint4 w = *reinterpret_cast<const uint4*>(crow + 16 * ((q ^ vec) & (R - 1)));
         cw[2 * q] = __builtin_amdgcn_perm(w.y, w.x, sel);
         cw[2 * q + 1] = __builtin_amdgcn_perm(w.w, w.z, sel);
       }
-      const uint4 s4 = *reinterpret_cast<const uint4*>(lds + kDecScales + 16 * vec);
-      const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+      // every scale of the vector
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { s16[2 * i] = sw[i] & 0xFFFFu; s16[2 * i + 1] = sw[i] >> 16; }
+      for (int i = 0; i < NS / 8; ++i) {
+        const uint4 s4 = *reinterpret_cast<const uint4*>(srow + 16 * i);
+        const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { s16[8 * i + 2 * e] = sw[e] & 0xFFFFu; s16[8 * i + 2 * e + 1] = sw[e] >> 16; }
+      }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 w = *reinterpret_cast<const uint4*>(crow + 16 * ((4 * hh + q) ^ (vec & 7)));
+      for (int q = 0; q < R / 2; ++q) {
+        const uint4 w = *reinterpret_cast<const uint4*>(crow + 16 * (((R / 2) * hh + q ^ vec) & (R - 1)));
         cw[4 * q] = w.x; cw[4 * q + 1] = w.y; cw[4 * q + 2] = w.z; cw[4 * q + 3] = w.w;
       }
-      const uint2 s2 = *reinterpret_cast<const uint2*>(lds + kDecScales + 16 * vec + 8 * hh);
-      s16[0] = s2.x & 0xFFFFu; s16[1] = s2.x >> 16; s16[2] = s2.y & 0xFFFFu; s16[3] = s2.y >> 16;
-      s16[4] = s16[5] = s16[6] = s16[7] = 0u;
+      // this half's scales
+      if (F::SB == 8) {
+        const uint2 s2 = *reinterpret_cast<const uint2*>(srow + 8 * hh);
+        const uint32_t sw[2] = {s2.x, s2.y};
+#pragma unroll
+        for (int i = 0; i < NS; ++i) s16[i] = (sw[(i / 2) % 2] >> (16 * (i % 2))) & 0xFFFFu;
+      } else {
+        const uint4 s4 = *reinterpret_cast<const uint4*>(srow + 16 * hh);
+        const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int i = 0; i < NS; ++i) s16[i] = (sw[(i / 2) % 4] >> (16 * (i % 2))) & 0xFFFFu;
+      }
     }
     float lq[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lq[q] = reinterpret_cast<const float*>(lds + kDec2Lam)[lane + 64 * q];
+    for (int q = 0; q < 4; ++q) lq[q] = reinterpret_cast<const float*>(lds + L::kLam)[lane + 64 * q];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t nxt = tile + gridDim.x;
-    if (nxt < a.n_tiles) dma_codes256(a, tile_info<256>(a, nxt), (lds_u8*)lds, lane);
+    if (nxt < a.n_tiles) dma_codes256<F>(a, tile_info<256>(a, nxt), (lds_u8*)lds, lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       *reinterpret_cast<float*>(work + kDec2Rl + rl_dst[q]) = rl_mul[q] * __builtin_amdgcn_rcpf(lq[q]);
     lds_sync();
 
-    // code dword d holds local pairs 4d .. 4d + 3 (SRFT: frequencies
-    // 2 (4d + b) + h, group d / 2; otherwise channels 8d .., group d / 4 of
-    // the lane's half); dequantized exactly as for D = 128
-    const float4* rl4 = reinterpret_cast<const float4*>(work + kDec2Rl) + 32 * hh;
     float v[128];
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      if ((d & 1) == 0) asm volatile("" ::: "memory");
-      const float sg = f16_bits_to_f32(s16[ROT == KVQ_ROT_SRFT ? d >> 1 : d >> 2]);
-      const float m_lo = -1032.f * sg;
-      const float sg16 = sg * 0.0625f;
-      const float m_hi = -72.f * sg;
-      const uint32_t x = cw[d], y = x >> 8;
-      const h2_t h0 = __builtin_bit_cast(h2_t, (x & 0x000F000Fu) | magic);
-      const h2_t h1 = __builtin_bit_cast(h2_t, (x & 0x00F000F0u) | magic);
-      const h2_t h2 = __builtin_bit_cast(h2_t, (y & 0x000F000Fu) | magic);
-      const h2_t h3 = __builtin_bit_cast(h2_t, (y & 0x00F000F0u) | magic);
-      const int j = 8 * d;
-      const float4 ra = rl4[2 * d], rb = rl4[2 * d + 1];
-      v[j] = fmaf(static_cast<float>(h0[0]), sg, m_lo) * ra.x;
-      v[j + 1] = fmaf(static_cast<float>(h1[0]), sg16, m_hi) * ra.y;
-      v[j + 2] = fmaf(static_cast<float>(h2[0]), sg, m_lo) * ra.z;
-      v[j + 3] = fmaf(static_cast<float>(h3[0]), sg16, m_hi) * ra.w;
-      v[j + 4] = fmaf(static_cast<float>(h0[1]), sg, m_lo) * rb.x;
-      v[j + 5] = fmaf(static_cast<float>(h1[1]), sg16, m_hi) * rb.y;
-      v[j + 6] = fmaf(static_cast<float>(h2[1]), sg, m_lo) * rb.z;
-      v[j + 7] = fmaf(static_cast<float>(h3[1]), sg16, m_hi) * rb.w;
-    }
+    dequant_lane<F, DPG>(cw, s16, reinterpret_cast<const float4*>(work + kDec2Rl) + 32 * hh, magic, v);
 
     if (ROT == KVQ_ROT_SRFT) {
       fft64<true>(v);
@@ -1224,64 +1301,63 @@ __global__ void __launch_bounds__(64, 2) decode256_kernel(CodecArgs a) {
 // Decode to fp32 (exact transform output, for checking): each lane writes its
 // own channels
 // ---------------------------------------------------------------------------
-template <int D, int ROT>
+template <int D, int ROT, int FMT>
 __global__ void __launch_bounds__(64, 2) decode_f32_kernel(CodecArgs a) {
   using G = Geo<D>;
+  using F = Fmt<FMT>;
+  constexpr int NSLOT = F::CB / 16;         // 16-byte code chunks per lane
   __shared__ __attribute__((aligned(16))) uint8_t lds[16384];
   const int lane = threadIdx.x;
   constexpr float kScale = rot_scale<D, ROT>();
 
-  auto load_codes = [&](const Tile& tt, uint4 (&cb)[4], uint2& sbuf) {
-    const int64_t cell = tt.row * a.Tcap + a.t0 + tt.t_start;
-    const uint8_t* cbase = a.codes_in + cell * (D / 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = i * 64 + lane;
-      const int r = s >> 2;
-      cb[i] = (r / G::L < tt.nv) ? ld_stream16(cbase + s * 16)
-                                 : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-    }
-    sbuf = (lane / G::L < tt.nv)
-               ? *reinterpret_cast<const uint2*>(a.scales_in + cell * (D / 32) + lane * 4)
-               : make_uint2(0, 0);
-  };
-
   for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
     const Tile t = tile_info<D>(a, tile);
-    uint4 cb[4];
-    uint2 sbuf;
-    load_codes(t, cb, sbuf);
-    // stage the code rows: slot s holds chunk (s & 3) of lane (s >> 2)
+    // a lane's codes (its vector, or its half of a D=256 vector) are the
+    // F::CB contiguous bytes at lane * CB from the tile's first cell
+    const int64_t cell = t.row * a.Tcap + a.t0 + t.t_start;
+    const uint8_t* cbase = a.codes_in + cell * (D * F::BITS / 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NSLOT; ++i) {
       const int s = i * 64 + lane;
-      *reinterpret_cast<uint4*>(lds + code_off(s >> 2, s & 3)) = cb[i];
+      const int r = s / NSLOT;               // lane row
+      const uint4 w = (r / G::L < t.nv) ? ld_stream16(cbase + s * 16) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(lds + code_off_f<F>(r, s % NSLOT)) = w;
+    }
+    uint32_t s16[F::NG];
+    {
+      const uint16_t* sp = a.scales_in + cell * (D / F::G) + lane * F::NG;
+      if (lane / G::L < t.nv) {
+#pragma unroll
+        for (int i = 0; i < F::NG; ++i) s16[i] = sp[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < F::NG; ++i) s16[i] = 0u;
+      }
     }
     __syncthreads();
-    uint32_t cw[16];
+    uint32_t cw[F::CW];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 w = *reinterpret_cast<const uint4*>(lds + code_off(lane, q));
+    for (int q = 0; q < NSLOT; ++q) {
+      const uint4 w = *reinterpret_cast<const uint4*>(lds + code_off_f<F>(lane, q));
       cw[4 * q] = w.x; cw[4 * q + 1] = w.y; cw[4 * q + 2] = w.z; cw[4 * q + 3] = w.w;
     }
-    const uint32_t s16[4] = {sbuf.x & 0xFFFFu, sbuf.x >> 16, sbuf.y & 0xFFFFu, sbuf.y >> 16};
     __syncthreads();
 
     const int half = (D == 256) ? (lane & 1) : 0;
     const float* lam = a.lambda + t.b * a.lambda_sb + t.h * D + half * 128;
     float v[128];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < F::NG; ++g) {
       const float sg = f16_bits_to_f32(s16[g]);
-      const float m8 = -8.f * sg;
 #pragma unroll
-      for (int jj = 0; jj < 32; ++jj) {
-        const int j = 32 * g + jj;
-        const uint32_t nib = (cw[j >> 3] >> (4 * (j & 7))) & 15u;
-        // (n - 8) * scale exactly, then divide by lambda (times the unitary
-        // scale of the inverse rotation)
-        const float qs = fmaf(static_cast<float>(nib), sg, m8);
-        v[j] = qs * (kScale * __builtin_amdgcn_rcpf(lam[j]));
+      for (int jj = 0; jj < F::G; ++jj) {
+        const int j = F::G * g + jj;
+        int code;
+        if (F::BITS == 4) code = static_cast<int>((cw[j >> 3] >> (4 * (j & 7))) & 15u) - 8;
+        else code = static_cast<int>(static_cast<int8_t>((cw[j >> 2] >> (8 * (j & 3))) & 0xFFu));
+        // q * scale exactly, then divide by lambda (times the unitary scale
+        // of the inverse rotation)
+        v[j] = static_cast<float>(code) * sg * (kScale * __builtin_amdgcn_rcpf(lam[j]));
       }
     }
 
@@ -1362,7 +1438,10 @@ void fill_common(CodecArgs& a, const CodecDesc& d) {
   for (int i = 0; i < 4; ++i) a.signs[i] = d.signs[i];
 }
 
-template <int D, int ROT>
+// Format index of a call: 2 * (bits == 8) + (G == 16).
+int format_of(const CodecDesc& d) { return (d.bits == 8 ? 2 : 0) + (d.G == 16 ? 1 : 0); }
+
+template <int D, int ROT, int FMT>
 hipError_t encode_dispatch(const CodecDesc& d, int mode) {
   CodecArgs a{};
   fill_common<D>(a, d);
@@ -1373,23 +1452,22 @@ hipError_t encode_dispatch(const CodecDesc& d, int mode) {
   if (a.n_tiles == 0) return hipSuccess;
   if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
   const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
-  if (D == 128) {
-    if (mode == 0) {
-      hipLaunchKernelGGL((encode128_kernel<ROT, 0>), grid, dim3(64), 0, d.stream, a);
+  if (mode == 1) {
+    // rotate only: the quantizer format plays no part
+    if (D == 128) {
+      hipLaunchKernelGGL((encode128_kernel<ROT, 1, 0>), grid, dim3(64), 0, d.stream, a);
     } else {
-      hipLaunchKernelGGL((encode128_kernel<ROT, 1>), grid, dim3(64), 0, d.stream, a);
+      hipLaunchKernelGGL((rotate_kernel<D, ROT>), grid, dim3(64), 0, d.stream, a);
     }
-  } else if (mode == 0 && ROT != KVQ_ROT_ID) {
-    hipLaunchKernelGGL((encode256_kernel<ROT>), grid, dim3(64), 0, d.stream, a);
-  } else if (mode == 0) {
-    hipLaunchKernelGGL((encode_kernel<D, ROT, 0>), grid, dim3(64), 0, d.stream, a);
+  } else if (D == 128) {
+    hipLaunchKernelGGL((encode128_kernel<ROT, 0, FMT>), grid, dim3(64), 0, d.stream, a);
   } else {
-    hipLaunchKernelGGL((encode_kernel<D, ROT, 1>), grid, dim3(64), 0, d.stream, a);
+    hipLaunchKernelGGL((encode256_kernel<ROT, FMT>), grid, dim3(64), 0, d.stream, a);
   }
   return hipGetLastError();
 }
 
-template <int D, int ROT>
+template <int D, int ROT, int FMT>
 hipError_t decode_dispatch(const CodecDesc& d, bool f32) {
   CodecArgs a{};
   fill_common<D>(a, d);
@@ -1400,30 +1478,50 @@ hipError_t decode_dispatch(const CodecDesc& d, bool f32) {
   if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
   const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
   if (f32) {
-    hipLaunchKernelGGL((decode_f32_kernel<D, ROT>), grid, dim3(64), 0, d.stream, a);
+    hipLaunchKernelGGL((decode_f32_kernel<D, ROT, FMT>), grid, dim3(64), 0, d.stream, a);
   } else if (D == 128) {
-    hipLaunchKernelGGL((decode128_kernel<ROT>), grid, dim3(64), 0, d.stream, a);
+    hipLaunchKernelGGL((decode128_kernel<ROT, FMT>), grid, dim3(64), 0, d.stream, a);
   } else {
-    hipLaunchKernelGGL((decode256_kernel<ROT>), grid, dim3(64), 0, d.stream, a);
+    hipLaunchKernelGGL((decode256_kernel<ROT, FMT>), grid, dim3(64), 0, d.stream, a);
   }
   return hipGetLastError();
+}
+
+template <int D, int ROT>
+hipError_t encode_fmt(const CodecDesc& d, int mode) {
+  switch (format_of(d)) {
+    case 1: return encode_dispatch<D, ROT, 1>(d, mode);
+    case 2: return encode_dispatch<D, ROT, 2>(d, mode);
+    case 3: return encode_dispatch<D, ROT, 3>(d, mode);
+    default: return encode_dispatch<D, ROT, 0>(d, mode);
+  }
+}
+
+template <int D, int ROT>
+hipError_t decode_fmt(const CodecDesc& d, bool f32) {
+  switch (format_of(d)) {
+    case 1: return decode_dispatch<D, ROT, 1>(d, f32);
+    case 2: return decode_dispatch<D, ROT, 2>(d, f32);
+    case 3: return decode_dispatch<D, ROT, 3>(d, f32);
+    default: return decode_dispatch<D, ROT, 0>(d, f32);
+  }
 }
 
 template <int D>
 hipError_t encode_rot(const CodecDesc& d, int mode) {
   switch (d.rotation) {
-    case KVQ_ROT_SRFT: return encode_dispatch<D, KVQ_ROT_SRFT>(d, mode);
-    case KVQ_ROT_SRHT: return encode_dispatch<D, KVQ_ROT_SRHT>(d, mode);
-    default: return encode_dispatch<D, KVQ_ROT_ID>(d, mode);
+    case KVQ_ROT_SRFT: return encode_fmt<D, KVQ_ROT_SRFT>(d, mode);
+    case KVQ_ROT_SRHT: return encode_fmt<D, KVQ_ROT_SRHT>(d, mode);
+    default: return encode_fmt<D, KVQ_ROT_ID>(d, mode);
   }
 }
 
 template <int D>
 hipError_t decode_rot(const CodecDesc& d, bool f32) {
   switch (d.rotation) {
-    case KVQ_ROT_SRFT: return decode_dispatch<D, KVQ_ROT_SRFT>(d, f32);
-    case KVQ_ROT_SRHT: return decode_dispatch<D, KVQ_ROT_SRHT>(d, f32);
-    default: return decode_dispatch<D, KVQ_ROT_ID>(d, f32);
+    case KVQ_ROT_SRFT: return decode_fmt<D, KVQ_ROT_SRFT>(d, f32);
+    case KVQ_ROT_SRHT: return decode_fmt<D, KVQ_ROT_SRHT>(d, f32);
+    default: return decode_fmt<D, KVQ_ROT_ID>(d, f32);
   }
 }
 

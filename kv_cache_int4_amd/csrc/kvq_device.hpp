@@ -229,6 +229,16 @@ __device__ __forceinline__ uint32_t quant_bits(float w, float r) {
   return static_cast<uint32_t>(min(max(b, kMagicLo), kMagicHi));
 }
 
+// int8 codes: 1.5 * 2^23 + 128 leaves rint_even(w*r) + 128 in the low byte.
+constexpr float kMagic8 = 12583040.0f;
+constexpr int kMagic8Hi = 0x4B4000FF;   // bits of 1.5 * 2^23 + 255 (code 127)
+
+// Offset byte of clamp(rint_even(w * r), -128, 127) in the low 8 bits.
+__device__ __forceinline__ uint32_t quant_bits8(float w, float r) {
+  const int b = __builtin_bit_cast(int, fmaf(w, r, kMagic8));
+  return static_cast<uint32_t>(min(max(b, kMagicLo), kMagic8Hi));
+}
+
 // Byte of a channel pair: even channel in the low nibble.
 __device__ __forceinline__ uint32_t pair_byte(uint32_t lo_bits, uint32_t hi_bits) {
   return lo_bits + (hi_bits << 4);   // low byte = n_even + 16 n_odd, no carry

@@ -12,6 +12,8 @@ enum { KVQ_ROT_SRFT = 0, KVQ_ROT_SRHT = 1, KVQ_ROT_ID = 2 };
 // A validated codec call (encode, rotate or decode).
 struct CodecDesc {
   int D;
+  int G;                      // group size: 32 or 16
+  int bits;                   // code width: 4 or 8
   int rotation;
   uint64_t signs[4];          // sign bits, bit i of word i / 64
   const uint16_t* x;          // encode / rotate input

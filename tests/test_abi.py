@@ -57,12 +57,34 @@ def test_plan_create_rejects():
     h = ctypes.c_void_p()
     assert L.kvq_plan_create(100, 32, 0, 0, ctypes.byref(h)) == UNSUPPORTED
     assert b"D=100" in L.kvq_last_error()
-    assert L.kvq_plan_create(128, 16, 0, 0, ctypes.byref(h)) == UNSUPPORTED
+    assert L.kvq_plan_create(128, 8, 0, 0, ctypes.byref(h)) == UNSUPPORTED
+    assert L.kvq_plan_create_ex(128, 32, 6, 0, 0, ctypes.byref(h)) == UNSUPPORTED
+    assert b"bits=6" in L.kvq_last_error()
+    assert L.kvq_plan_create_ex(128, 64, 8, 0, 0, ctypes.byref(h)) == UNSUPPORTED
     assert L.kvq_plan_create(128, 32, 7, 0, ctypes.byref(h)) == INVALID
     assert L.kvq_plan_create(128, 32, 0, 0, None) == INVALID
     assert L.kvq_plan_signs(None, None, 0) == INVALID
     assert L.kvq_strerror(WORKSPACE) == b"workspace missing or too small"
     L.kvq_plan_destroy(None)
+
+
+@pytest.mark.parametrize("bits,G", [(4, 32), (4, 16), (8, 32), (8, 16)])
+@pytest.mark.parametrize("D", [128, 256])
+def test_plan_formats(bits, G, D):
+    """Plans of every code width and group size: info reports them, signs are
+    the oracle's, and kvq_plan_create is the 4-bit case."""
+    p = K.Plan(D, G, "srht", 77, bits=bits)
+    assert p.info_ex() == (D, G, bits, O.SRHT)
+    assert p.info() == (D, G, O.SRHT)
+    assert p.code_bytes == D * bits // 8
+    assert np.array_equal(p.signs(), O.plan_signs(D, O.SRHT, 77))
+    assert K.cache_shapes(2, 3, 5, D, G, bits) == ((2, 3, 5, D * bits // 8), (2, 3, 5, D // G))
+    L = K.library()
+    h = ctypes.c_void_p()
+    assert L.kvq_plan_create(D, G, 0, 1, ctypes.byref(h)) == OK
+    b = ctypes.c_int32()
+    assert L.kvq_plan_info_ex(h, None, None, ctypes.byref(b), None) == OK and b.value == 4
+    L.kvq_plan_destroy(h)
 
 
 def _encode(plan, x=A, B=1, H=2, T=4, sb=1024, sh=512, st=128, lam=A, lsb=0, codes=A, scales=A,
@@ -136,6 +158,10 @@ def test_attention_validation():
     assert call(vc=None) == INVALID
     assert call(dt=5) == INVALID
     assert call(B=0) == OK                            # nothing to do
+    for bits, G in ((4, 16), (8, 32), (8, 16)):     # attention is built for int4 in groups of 32
+        pf = K.Plan(128, G, "srft", 3, bits=bits)
+        assert L.kvq_attn_decode(pf.handle, A, A, A, A, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need,
+                                 None) == UNSUPPORTED
     p256 = K.Plan(256, 32, "srft", 3)
     assert L.kvq_attn_decode(p256.handle, A, A, A, A, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need,
                              None) == UNSUPPORTED

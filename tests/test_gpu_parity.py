@@ -55,8 +55,8 @@ def gpu_encode(plan, x, lam, Tcap=None, t0=0):
     outside [t0, t0 + T) still holds its canary."""
     B, H, T, D = x.shape
     Tcap = T + t0 if Tcap is None else Tcap
-    codes = torch.full((B, H, Tcap, D // 2), 0x5A, dtype=torch.uint8, device="cuda")
-    scales = torch.full((B, H, Tcap, D // 32), 1234.0, dtype=torch.float16, device="cuda")
+    codes = torch.full((B, H, Tcap, plan.code_bytes), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((B, H, Tcap, D // plan.G), 1234.0, dtype=torch.float16, device="cuda")
     K.encode(plan, x, lam, codes, scales, t0)
     torch.cuda.synchronize()
     c, s = codes.cpu(), scales.cpu()
@@ -69,13 +69,14 @@ def gpu_encode(plan, x, lam, Tcap=None, t0=0):
 
 def check_encode(name, plan, rot, x, lam, Tcap=None, t0=0):
     B, H, T, D = x.shape
-    say(f"[encode] {name} D={D} rot={rot} B={B} H={H} T={T} t0={t0}")
+    say(f"[encode] {name} D={D} rot={rot} bits={plan.bits} G={plan.G} B={B} H={H} T={T} t0={t0}")
     xd = x.cuda() if not x.is_cuda else x
     codes_d, scales_d, c, s = gpu_encode(plan, xd, lam.cuda(), Tcap, t0)
     signs = O.plan_signs(D, ROTS[rot], plan.seed)
     xs = np16(x).reshape(-1, D)
     lv = lam_per_vector(lam, B, H, T)
-    rep = P.compare_codes(c.reshape(-1, D // 2), s.reshape(-1, D // 32), xs, lv, ROTS[rot], signs)
+    rep = P.compare_codes(c.reshape(-1, plan.code_bytes), s.reshape(-1, D // plan.G), xs, lv, ROTS[rot], signs,
+                          plan.G, plan.bits)
     say(f"   codes ok: code mismatches {rep['code_mismatch']}, scale mismatches {rep['scale_mismatch']}, "
         f"fraction {rep['mismatch_frac']:.2e}")
     return codes_d, scales_d, c, s, rep
