@@ -56,7 +56,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "SRFT", "SRHT", "IDENTITY", "ROTATIONS", "GROUP",
+    "SRFT", "SRHT", "IDENTITY", "HERMITIAN", "ROTATIONS", "GROUP",
     "splitmix64", "plan_signs",
     "rotate_forward", "rotate_inverse",
     "quantize_groups", "pack_nibbles", "unpack_nibbles", "pack_codes", "unpack_codes",
@@ -64,7 +64,7 @@ __all__ = [
     "encode", "decode", "rotate",
     "boundary_distances",
     "attention_int4", "attention_f16",
-    "srft_matrix_bruteforce", "srht_matrix_bruteforce",
+    "srft_matrix_bruteforce", "srht_matrix_bruteforce", "hermitian_matrix_bruteforce",
     "rotation_matrix",
     "compression_ratio",
 ]
@@ -72,6 +72,7 @@ __all__ = [
 SRFT = 0
 SRHT = 1
 IDENTITY = 2
+HERMITIAN = 3          # real-input DFT variant (quality study only; no kernel)
 ROTATIONS = (SRFT, SRHT, IDENTITY)
 GROUP = 32
 
@@ -107,7 +108,7 @@ def plan_signs(D: int, rotation: int, seed: int) -> np.ndarray:
 
     Bit i of the stream is bit (i mod 64) of output floor(i/64); the sign is
     1 - 2*bit.  SRFT uses D/2 signs (one per complex pair, reading R1), SRHT
-    uses D signs, IDENTITY none.
+    and the HERMITIAN variant D signs, IDENTITY none.
     """
     if rotation == IDENTITY:
         return np.zeros(0, dtype=np.int8)
@@ -153,6 +154,17 @@ def rotate_forward(x: np.ndarray, rotation: int, signs: np.ndarray) -> np.ndarra
     if rotation == SRHT:
         H = _sylvester(D)
         return ((signs.astype(np.float64) * x) @ H.T) / math.sqrt(D)
+    if rotation == HERMITIAN:
+        # real-input DFT of the signed D-vector, unitary; the Hermitian half
+        # spectrum unpacked into D reals: X_0 and X_{D/2} (real), then
+        # sqrt(2) (Re X_m, Im X_m) for 0 < m < D/2
+        X = np.fft.rfft(signs.astype(np.float64) * x, axis=-1, norm="ortho")
+        y = np.empty_like(x)
+        y[..., 0] = X[..., 0].real
+        y[..., 1] = X[..., D // 2].real
+        y[..., 2::2] = math.sqrt(2.0) * X[..., 1:D // 2].real
+        y[..., 3::2] = math.sqrt(2.0) * X[..., 1:D // 2].imag
+        return y
     raise ValueError("unknown rotation")
 
 
@@ -177,6 +189,12 @@ def rotate_inverse(y: np.ndarray, rotation: int, signs: np.ndarray) -> np.ndarra
     if rotation == SRHT:
         H = _sylvester(D)
         return signs.astype(np.float64) * ((y @ H.T) / math.sqrt(D))
+    if rotation == HERMITIAN:
+        X = np.empty(y.shape[:-1] + (D // 2 + 1,), dtype=np.complex128)
+        X[..., 0] = y[..., 0]
+        X[..., D // 2] = y[..., 1]
+        X[..., 1:D // 2] = (y[..., 2::2] + 1j * y[..., 3::2]) / math.sqrt(2.0)
+        return signs.astype(np.float64) * np.fft.irfft(X, n=D, axis=-1, norm="ortho")
     raise ValueError("unknown rotation")
 
 
@@ -205,6 +223,21 @@ def srft_matrix_bruteforce(D: int, signs) -> list[list[float]]:
             acc /= math.sqrt(M)
             R[2 * m][col] = acc.real
             R[2 * m + 1][col] = acc.imag
+    return R
+
+
+def hermitian_matrix_bruteforce(D: int, signs) -> list[list[float]]:
+    """The real-DFT variant as a D x D matrix from its cosine / sine basis:
+    row 0 = 1/sqrt(D), row 1 = (-1)^j / sqrt(D), rows 2m and 2m+1 =
+    sqrt(2/D) cos(2 pi m j / D) and -sqrt(2/D) sin(2 pi m j / D), times the
+    sign of column j."""
+    R = [[0.0] * D for _ in range(D)]
+    for j in range(D):
+        R[0][j] = signs[j] / math.sqrt(D)
+        R[1][j] = signs[j] * (-1) ** j / math.sqrt(D)
+        for m in range(1, D // 2):
+            R[2 * m][j] = signs[j] * math.sqrt(2.0 / D) * math.cos(2 * math.pi * m * j / D)
+            R[2 * m + 1][j] = -signs[j] * math.sqrt(2.0 / D) * math.sin(2 * math.pi * m * j / D)
     return R
 
 
