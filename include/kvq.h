@@ -166,8 +166,9 @@ kvq_status kvq_attn_workspace_size(int32_t D, int64_t B, int64_t Hq, int64_t seq
  * rotated basis (q . k^ = ((R q) / lambda_k) . (lambda_k R k^)) and the
  * value average is rotated back once per head.  Requires Hq % Hkv == 0,
  * 1 <= seq_len <= Tcap, and a workspace of kvq_attn_workspace_size bytes.
- * Built for D = 128 with int4 codes in groups of 32; other plans return
- * KVQ_ERR_UNSUPPORTED. */
+ * Built for D = 128, every code width and group size of the plan (codes
+ * [B, Hkv, Tcap, D*bits/8], scales [B, Hkv, Tcap, D/G]); a D = 256 plan
+ * returns KVQ_ERR_UNSUPPORTED. */
 kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q,
                            const uint8_t* k_codes, const uint16_t* k_scales, const float* lambda_k,
                            const uint8_t* v_codes, const uint16_t* v_scales, const float* lambda_v,

@@ -348,9 +348,6 @@ kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q, const uint8_
   try {
     if (kvq_status s = check_plan(plan)) return s;
     if (plan->D != 128) return fail(KVQ_ERR_UNSUPPORTED, "attention is built for D=128 (plan D=%d)", plan->D);
-    if (plan->bits != 4 || plan->G != 32)
-      return fail(KVQ_ERR_UNSUPPORTED, "attention is built for int4 codes in groups of 32 (plan: %d-bit, G=%d)",
-                  plan->bits, plan->G);
     if (kvq_status s = check_attn_common(plan->D, q, B, Hq, Hkv, Tcap, seq_len, out, out_dtype, workspace,
                                          workspace_bytes))
       return s;
@@ -365,6 +362,8 @@ kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q, const uint8_
     d.rotation = plan->rotation;
     for (int i = 0; i < 4; ++i) d.signs[i] = plan->sign_bits[i];
     d.int4 = true;
+    d.G = plan->G;
+    d.bits = plan->bits;
     d.q = q;
     d.k_codes = k_codes; d.k_scales = k_scales; d.lambda_k = lambda_k;
     d.v_codes = v_codes; d.v_scales = v_scales; d.lambda_v = lambda_v;

@@ -56,14 +56,14 @@ typedef int int4_t __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kHeadsPerWave = 4;
 constexpr int kBlk = 32;              // tokens per inner step
-constexpr int kQRec = 448;            // bytes of one rotated-query record
-
-// Record layout (int4 cache): three int8 limbs per channel,
+// Record layout (quantized cache; 448 bytes, 544 with the sums per 16
+// channels): three int8 limbs per channel,
 // q~ ~= s (Q1 + Q2 / 256 + Q3 / 65536): [0,128) Q1, [128,256) Q2,
 // [256,384) Q3, [384,400) s[4] f32, [400,448) sums of Q1, Q2, Q3 per group
 // (i32[3][4]).
 constexpr int kRecS = 384;
 constexpr int kRecSum = 400;
+constexpr int kRecSum16 = 448;        // groups of 16: sums per 16 channels, i32[3][8]
 
 __constant__ TwTable kTw64Const = make_twiddles(64);
 
@@ -150,8 +150,9 @@ __device__ __forceinline__ void query_loads(const AttnArgs& a, const uint16_t* q
 // Rotated query records of the wave's four heads (int4 cache), computed by
 // one wave from the pair words in.w: lane l owns channels 2l, 2l+1 of every
 // head.  The heads advance together through each cross-lane step (four
-// independent shuffles per wait); the records go to LDS at rec + head * kQRec.
-template <int ROT>
+// independent shuffles per wait); the records go to LDS at rec + head * REC
+// (with the per-16-channel limb sums when SUM16).
+template <int ROT, int REC, bool SUM16>
 __device__ __forceinline__ void query_records(const AttnArgs& a, const QueryIn& in, int lane, uint8_t* rec) {
   constexpr int NH = kHeadsPerWave;
   float y0[NH], y1[NH];   // rotated channels 2 lane, 2 lane + 1 (unnormalized)
@@ -264,8 +265,15 @@ __device__ __forceinline__ void query_records(const AttnArgs& a, const QueryIn& 
   for (int h = 0; h < NH; ++h)
 #pragma unroll
     for (int limb = 0; limb < 3; ++limb) sum[h][limb] = static_cast<float>(li[h][limb][0] + li[h][limb][1]);
+  float sum16[NH][3];      // after the steps over 8 lanes: sums per 16 channels
 #pragma unroll
   for (int m = 1; m <= 8; m <<= 1) {
+    if (m == 8) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int limb = 0; limb < 3; ++limb) sum16[h][limb] = sum[h][limb];
+    }
     float o[NH][3];
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -279,12 +287,14 @@ __device__ __forceinline__ void query_records(const AttnArgs& a, const QueryIn& 
   const int grp = lane >> 4;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    uint8_t* r = rec + h * kQRec;
+    uint8_t* r = rec + h * REC;
 #pragma unroll
     for (int limb = 0; limb < 3; ++limb) {
       reinterpret_cast<uint16_t*>(r + 128 * limb)[lane] =
           static_cast<uint16_t>((li[h][limb][0] & 0xFF) | ((li[h][limb][1] & 0xFF) << 8));
       if ((lane & 15) == 0) reinterpret_cast<int*>(r + kRecSum)[4 * limb + grp] = static_cast<int>(sum[h][limb]);
+      if (SUM16 && (lane & 7) == 0)
+        reinterpret_cast<int*>(r + kRecSum16)[8 * limb + (lane >> 3)] = static_cast<int>(sum16[h][limb]);
     }
     if ((lane & 15) == 0) reinterpret_cast<float*>(r + kRecS)[grp] = amax[h] > 0.f ? amax[h] / 127.f : 0.f;
   }
@@ -367,6 +377,7 @@ template <bool INT4>
 struct State {
   int4_t qb[3][2];           // int4 QK right operand: [limb][k-step]
   int4_t corr[3];            // int4 accumulator start: -8 * sum(Q) per limb
+  int4_t corr1[3];           // int4 in groups of 16: the same for k-step 1
   float sfac;                // int4: s / 256 of column (group, head)
   half8_t qh[4], ql[4];      // fp16 QK right operand: hi / lo
   float4_t acc[8];           // PV accumulators, MFMA c <-> channel 8 n16 + c
@@ -493,14 +504,27 @@ __device__ __forceinline__ void process_blk(State<INT4>& st, const Blk<INT4>& cu
   }
 }
 
-// ---- int4 cache: block loads at wave-uniform bases ----
-// Lane (n16, kq), n16 = 4 g + h: QK column (value/key group g, head h); its
+// ---- quantized cache: block loads at wave-uniform bases ----
+// Code format FMT = 2 * (bits == 8) + (G == 16), as in the codec; D = 128.
+template <int FMT>
+struct QF {
+  static constexpr int BITS = (FMT & 2) ? 8 : 4;
+  static constexpr bool G16 = (FMT & 1) != 0;
+  static constexpr int W = BITS / 4;            // K uint4s per lane and sub-block, V dwords per token
+  static constexpr int CBT = 16 * BITS;         // code bytes per token (64 or 128)
+  static constexpr int SBT = G16 ? 16 : 8;      // scale bytes per token
+  static constexpr int REC = G16 ? 544 : 448;   // query record bytes
+};
+
+// Lane (n16, kq), n16 = 4 g + h: QK column (32-channel slice g, head h); its
 // scores are those of tokens 16 sb + 4 kq + i (i < 4).
+template <int FMT>
 struct Blk4 {
-  uint4 k[2];          // 16 code bytes of token 16 sb + n16, channels 32 kq ..
-  uint32_t v[2][4];    // code dword n16 of token 16 sb + 4 kq + i
-  uint32_t ks[2];      // key scale (fp16) of token 16 sb + 4 kq + h, group g
-  uint32_t vs[2];      // value scale of the same token and group
+  uint4 k[2][QF<FMT>::W];        // code bytes of token 16 sb + n16, channels 32 kq .. 32 kq + 31
+  uint32_t v[2][4][QF<FMT>::W];  // codes of channels 8 n16 .. 8 n16 + 7 of token 16 sb + 4 kq + i
+  uint32_t ks[2];                // key scale (fp16) of token 16 sb + 4 kq + h for group g (G = 32), or
+                                 // of groups 2 g and 2 g + 1 (G = 16: low and high half)
+  uint32_t vs[2];                // value scale(s) of the same token and group(s)
 };
 
 // Lane byte offsets of a full block's loads, from the block's first token.
@@ -508,11 +532,13 @@ struct Off4 {
   uint32_t k, v, s;
 };
 
+template <int FMT>
 __device__ __forceinline__ Off4 lane_offsets4(uint32_t n16, uint32_t kq) {
+  using F = QF<FMT>;
   Off4 o;
-  o.k = (n16 << 6) + (kq << 4);
-  o.v = (kq << 8) + (n16 << 2);
-  o.s = ((4 * kq + (n16 & 3)) << 3) + ((n16 >> 2) << 1);
+  o.k = n16 * F::CBT + kq * 16 * F::W;
+  o.v = kq * 4 * F::CBT + n16 * 4 * F::W;
+  o.s = (4 * kq + (n16 & 3)) * F::SBT + (n16 >> 2) * (F::G16 ? 4 : 2);
   return o;
 }
 
@@ -525,36 +551,55 @@ __device__ __forceinline__ T ldi(const uint8_t* base, uint32_t off, int imm) {
 
 // Loads of the block starting at token t0.  In a tail block the positions
 // past t_last re-read token t_last (their scores are masked).
-template <bool TAIL>
+template <int FMT, bool TAIL>
 __device__ __forceinline__ void load4(const Rows& r, uint32_t t0, uint32_t t_last, const Off4& o, uint32_t n16,
-                                      uint32_t kq, Blk4& b) {
-  const uint8_t* kc = r.kc + static_cast<size_t>(t0) * 64;
-  const uint8_t* vc = r.vc + static_cast<size_t>(t0) * 64;
-  const uint8_t* ksc = reinterpret_cast<const uint8_t*>(r.ksc) + static_cast<size_t>(t0) * 8;
-  const uint8_t* vsc = reinterpret_cast<const uint8_t*>(r.vsc) + static_cast<size_t>(t0) * 8;
+                                      uint32_t kq, Blk4<FMT>& b) {
+  using F = QF<FMT>;
+  const uint8_t* kc = r.kc + static_cast<size_t>(t0) * F::CBT;
+  const uint8_t* vc = r.vc + static_cast<size_t>(t0) * F::CBT;
+  const uint8_t* ksc = reinterpret_cast<const uint8_t*>(r.ksc) + static_cast<size_t>(t0) * F::SBT;
+  const uint8_t* vsc = reinterpret_cast<const uint8_t*>(r.vsc) + static_cast<size_t>(t0) * F::SBT;
+  auto load_v = [&](uint32_t* dst, uint32_t off, int imm) {
+    if (F::W == 1) {
+      dst[0] = ldi<uint32_t>(vc, off, imm);
+    } else {
+      const uint2 x = ldi<uint2>(vc, off, imm);
+      dst[0] = x.x;
+      dst[F::W - 1] = x.y;
+    }
+  };
+  auto load_s = [&](uint32_t& ks, uint32_t& vs, uint32_t off, int imm) {
+    if (F::G16) {
+      ks = ldi<uint32_t>(ksc, off, imm);
+      vs = ldi<uint32_t>(vsc, off, imm);
+    } else {
+      ks = ldi<uint16_t>(ksc, off, imm);
+      vs = ldi<uint16_t>(vsc, off, imm);
+    }
+  };
   if (!TAIL) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      b.k[sb] = ldi<uint4>(kc, o.k, 1024 * sb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b.v[sb][i] = ldi<uint32_t>(vc, o.v, 64 * (16 * sb + i));
-      b.ks[sb] = ldi<uint16_t>(ksc, o.s, 128 * sb);
-      b.vs[sb] = ldi<uint16_t>(vsc, o.s, 128 * sb);
+      for (int w = 0; w < F::W; ++w) b.k[sb][w] = ldi<uint4>(kc, o.k, 16 * F::CBT * sb + 16 * w);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_v(b.v[sb][i], o.v, F::CBT * (16 * sb + i));
+      load_s(b.ks[sb], b.vs[sb], o.s, 16 * F::SBT * sb);
     }
   } else {
     const uint32_t last = t_last - t0;
 #pragma unroll
     for (uint32_t sb = 0; sb < 2; ++sb) {
       const uint32_t tk = min(16 * sb + n16, last);
-      b.k[sb] = ldi<uint4>(kc, (tk << 6) + (kq << 4), 0);
+#pragma unroll
+      for (int w = 0; w < F::W; ++w) b.k[sb][w] = ldi<uint4>(kc, tk * F::CBT + kq * 16 * F::W, 16 * w);
 #pragma unroll
       for (uint32_t i = 0; i < 4; ++i) {
         const uint32_t t = min(16 * sb + 4 * kq + i, last);
-        b.v[sb][i] = ldi<uint32_t>(vc, (t << 6) + (n16 << 2), 0);
+        load_v(b.v[sb][i], t * F::CBT + n16 * 4 * F::W, 0);
       }
       const uint32_t ts = min(16 * sb + 4 * kq + (n16 & 3), last);
-      b.ks[sb] = ldi<uint16_t>(ksc, (ts << 3) + ((n16 >> 2) << 1), 0);
-      b.vs[sb] = ldi<uint16_t>(vsc, (ts << 3) + ((n16 >> 2) << 1), 0);
+      load_s(b.ks[sb], b.vs[sb], ts * F::SBT + (n16 >> 2) * (F::G16 ? 4 : 2), 0);
     }
   }
 }
@@ -566,35 +611,84 @@ __device__ __forceinline__ float quad_bcast(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), I * 0x55, 0xF, 0xF, true));
 }
 
-template <bool TAIL>
-__device__ __forceinline__ void process4(State<true>& st, const Blk4& cur, uint32_t t0, uint32_t t_end, uint32_t kq,
-                                         uint32_t mag_lo, uint32_t mag_hi) {
+// Combined QK score of one column from its three limb accumulators: 256 c1
+// + c2 is exact in int32; the third limb joins in fp32.
+__device__ __forceinline__ float limb_score(const int4_t& c1, const int4_t& c2, const int4_t& c3, int i) {
+  return fmaf(static_cast<float>(c1[i] * 256 + c2[i]), 256.f, static_cast<float>(c3[i]));
+}
+
+// Low / high nibbles of the four bytes of a word as int8 lanes.
+__device__ __forceinline__ int lo_nib(uint32_t x) { return static_cast<int>(x & 0x0F0F0F0Fu); }
+__device__ __forceinline__ int hi_nib(uint32_t x) { return static_cast<int>((x >> 4) & 0x0F0F0F0Fu); }
+
+template <int FMT, bool TAIL>
+__device__ __forceinline__ void process4(State<true>& st, const Blk4<FMT>& cur, uint32_t t0, uint32_t t_end,
+                                         uint32_t kq, uint32_t n16, uint32_t mag_lo, uint32_t mag_hi) {
+  using F = QF<FMT>;
   // ---- scores ----
   float sc[2][4];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    const uint4 w = cur.k[sb];
-    // unsigned nibbles as int8: k-step 0 = even channels, 1 = odd channels
-    const int4_t a0 = (int4_t){static_cast<int>(w.x & 0x0F0F0F0Fu), static_cast<int>(w.y & 0x0F0F0F0Fu),
-                               static_cast<int>(w.z & 0x0F0F0F0Fu), static_cast<int>(w.w & 0x0F0F0F0Fu)};
-    const int4_t a1 = (int4_t){static_cast<int>((w.x >> 4) & 0x0F0F0F0Fu), static_cast<int>((w.y >> 4) & 0x0F0F0F0Fu),
-                               static_cast<int>((w.z >> 4) & 0x0F0F0F0Fu), static_cast<int>((w.w >> 4) & 0x0F0F0F0Fu)};
-    int4_t c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[0][0], st.corr[0], 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[0][1], c1, 0, 0, 0);
-    int4_t c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[1][0], st.corr[1], 0, 0, 0);
-    c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[1][1], c2, 0, 0, 0);
-    int4_t c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[2][0], st.corr[2], 0, 0, 0);
-    c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[2][1], c3, 0, 0, 0);
+    float xs[4];
     // key scale of token i: loaded by quad position i (same group, head i)
-    const float ksf = f16_bits_to_f32(cur.ks[sb]);
+    const float ksf = f16_bits_to_f32(cur.ks[sb] & 0xFFFFu);
     const float ks4[4] = {quad_bcast<0>(ksf), quad_bcast<1>(ksf), quad_bcast<2>(ksf), quad_bcast<3>(ksf)};
+    if (FMT == 0) {
+      const uint4 w = cur.k[sb][0];
+      // unsigned nibbles as int8: k-step 0 = even channels, 1 = odd channels
+      const int4_t a0 = (int4_t){lo_nib(w.x), lo_nib(w.y), lo_nib(w.z), lo_nib(w.w)};
+      const int4_t a1 = (int4_t){hi_nib(w.x), hi_nib(w.y), hi_nib(w.z), hi_nib(w.w)};
+      int4_t c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[0][0], st.corr[0], 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[0][1], c1, 0, 0, 0);
+      int4_t c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[1][0], st.corr[1], 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[1][1], c2, 0, 0, 0);
+      int4_t c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[2][0], st.corr[2], 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[2][1], c3, 0, 0, 0);
+      // sfac is this column's query scale
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[i] = limb_score(c1, c2, c3, i) * st.sfac * ks4[i];
+    } else {
+      // k-step s covers channels 32 kq + 16 s .. + 15 (int4: as low / high
+      // nibble words; int8: the signed code bytes in order)
+      int4_t av[2];
+      if (F::BITS == 4) {
+        const uint4 w = cur.k[sb][0];
+        av[0] = (int4_t){lo_nib(w.x), hi_nib(w.x), lo_nib(w.y), hi_nib(w.y)};
+        av[1] = (int4_t){lo_nib(w.z), hi_nib(w.z), lo_nib(w.w), hi_nib(w.w)};
+      } else {
+        av[0] = __builtin_bit_cast(int4_t, cur.k[sb][0]);
+        av[1] = __builtin_bit_cast(int4_t, cur.k[sb][F::W - 1]);
+      }
+      if (!F::G16) {
+        // one group per 32-channel slice: both k-steps into one sum
+        int4_t c[3];
+#pragma unroll
+        for (int limb = 0; limb < 3; ++limb) {
+          c[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], st.qb[limb][0], st.corr[limb], 0, 0, 0);
+          c[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[1], st.qb[limb][1], c[limb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[i] = limb_score(c[0], c[1], c[2], i) * st.sfac * ks4[i];
+      } else {
+        // groups of 16: each k-step is one group with its own key scale
+        int4_t c0[3], c1[3];
+#pragma unroll
+        for (int limb = 0; limb < 3; ++limb) {
+          c0[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], st.qb[limb][0], st.corr[limb], 0, 0, 0);
+          c1[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[1], st.qb[limb][1], st.corr1[limb], 0, 0, 0);
+        }
+        const float kgf = f16_bits_to_f32(cur.ks[sb] >> 16);
+        const float kg4[4] = {quad_bcast<0>(kgf), quad_bcast<1>(kgf), quad_bcast<2>(kgf), quad_bcast<3>(kgf)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xs[i] = fmaf(limb_score(c0[0], c0[1], c0[2], i), ks4[i], limb_score(c1[0], c1[1], c1[2], i) * kg4[i]) *
+                  st.sfac;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // 256 c1 + c2 is exact in int32; the third limb joins in fp32; sfac is
-      // this column's query scale
-      float x = fmaf(static_cast<float>(c1[i] * 256 + c2[i]), 256.f, static_cast<float>(c3[i])) * st.sfac * ks4[i];
-      x = add_row_ror<8>(x);     // + group (g + 2) mod 4
-      x = add_row_ror<4>(x);     // + groups (g + 1), (g + 3)
+      float x = add_row_ror<8>(xs[i]);   // + slice (g + 2) mod 4
+      x = add_row_ror<4>(x);             // + slices (g + 1), (g + 3)
       sc[sb][i] = x;
     }
     if (TAIL) {
@@ -625,12 +719,18 @@ __device__ __forceinline__ void process4(State<true>& st, const Blk4& cur, uint3
     }
   }
 
-  // ---- PV left operand: p times the value scale of group g, hi + lo ----
-  half8_t pa_hi, pa_lo;
+  // ---- PV left operand: p times the value scale of the row's group, hi +
+  // lo (groups of 16: a second operand pb for the odd group of the slice) ----
+  half8_t pa_hi, pa_lo, pb_hi, pb_lo;
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    const float vsf = f16_bits_to_f32(cur.vs[sb]);
+    const float vsf = f16_bits_to_f32(cur.vs[sb] & 0xFFFFu);
     const float vs4[4] = {quad_bcast<0>(vsf), quad_bcast<1>(vsf), quad_bcast<2>(vsf), quad_bcast<3>(vsf)};
+    float vg4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (F::G16) {
+      const float vgf = f16_bits_to_f32(cur.vs[sb] >> 16);
+      vg4[0] = quad_bcast<0>(vgf); vg4[1] = quad_bcast<1>(vgf); vg4[2] = quad_bcast<2>(vgf); vg4[3] = quad_bcast<3>(vgf);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float p = __builtin_amdgcn_exp2f(sc[sb][i] - st.m_run);
@@ -639,17 +739,29 @@ __device__ __forceinline__ void process4(State<true>& st, const Blk4& cur, uint3
       const _Float16 hi = static_cast<_Float16>(w);
       pa_hi[4 * sb + i] = hi;
       pa_lo[4 * sb + i] = static_cast<_Float16>(w - static_cast<float>(hi));
+      if (F::G16) {
+        const float w1 = p * vg4[i];
+        const _Float16 h1 = static_cast<_Float16>(w1);
+        pb_hi[4 * sb + i] = h1;
+        pb_lo[4 * sb + i] = static_cast<_Float16>(w1 - static_cast<float>(h1));
+      }
     }
   }
 
   // ---- PV: MFMA c takes channel 8 n16 + c; k slot 4 sb + i <-> token.
-  // A nibble masked under a biased exponent is an exact fp16 number: the
-  // low nibble under 1024 (unit in bit 0) gives 1024 + n, the high nibble
-  // under 64 (unit in bit 4) gives 64 + n; one packed subtraction leaves
-  // n - 8.  (Products of two fp16 subnormals, which a nibble masked in place
-  // would be, do not keep their full value in the matrix unit's fp32 sums.)
+  // Codes enter as exact normal fp16 integers under a biased exponent: an
+  // int4 low nibble under 1024 (unit in bit 0) gives 1024 + n, a high nibble
+  // under 64 (unit in bit 4) gives 64 + n, an int8 byte with its top bit
+  // flipped under 1024 gives 1024 + q + 128; one packed subtraction leaves
+  // the code.  (Products of two fp16 subnormals, which a nibble masked in
+  // place would be, do not keep their full value in the matrix unit's fp32
+  // sums.)  Groups of 16: the columns of the slice's odd group take the pb
+  // rows, those of its even group the pa rows; the other operand's columns
+  // are zero, so both passes accumulate into the same registers.
   const half2_t off_lo = {static_cast<_Float16>(-1032.f), static_cast<_Float16>(-1032.f)};
   const half2_t off_hi = {static_cast<_Float16>(-72.f), static_cast<_Float16>(-72.f)};
+  const half2_t off_8 = {static_cast<_Float16>(-1152.f), static_cast<_Float16>(-1152.f)};
+  const bool odd_group = ((n16 >> 1) & 1) != 0;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     uint32_t hv[4];
@@ -657,16 +769,36 @@ __device__ __forceinline__ void process4(State<true>& st, const Blk4& cur, uint3
     for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
-        const int by = c >> 1;
-        const uint32_t sel = 0x0c000c00u | (static_cast<uint32_t>(4 + by) << 16) | static_cast<uint32_t>(by);
-        const uint32_t x = __builtin_amdgcn_perm(cur.v[sb][2 * pr + 1], cur.v[sb][2 * pr], sel);
-        const uint32_t biased = (c & 1) ? ((x & 0x00F000F0u) | mag_hi) : ((x & 0x000F000Fu) | mag_lo);
-        hv[2 * sb + pr] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, biased) + ((c & 1) ? off_hi : off_lo));
+        if (F::BITS == 4) {
+          const int by = c >> 1;
+          const uint32_t sel = 0x0c000c00u | (static_cast<uint32_t>(4 + by) << 16) | static_cast<uint32_t>(by);
+          const uint32_t x = __builtin_amdgcn_perm(cur.v[sb][2 * pr + 1][0], cur.v[sb][2 * pr][0], sel);
+          const uint32_t biased = (c & 1) ? ((x & 0x00F000F0u) | mag_hi) : ((x & 0x000F000Fu) | mag_lo);
+          hv[2 * sb + pr] =
+              __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, biased) + ((c & 1) ? off_hi : off_lo));
+        } else {
+          const int wi = (c >> 2) % F::W, by = c & 3;
+          const uint32_t sel = 0x0c000c00u | (static_cast<uint32_t>(4 + by) << 16) | static_cast<uint32_t>(by);
+          const uint32_t x = __builtin_amdgcn_perm(cur.v[sb][2 * pr + 1][wi], cur.v[sb][2 * pr][wi], sel);
+          const uint32_t biased = (x ^ 0x00800080u) | mag_lo;
+          hv[2 * sb + pr] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, biased) + off_8);
+        }
       }
     }
-    const half8_t vb = __builtin_bit_cast(half8_t, make_uint4(hv[0], hv[1], hv[2], hv[3]));
-    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb, st.acc[c], 0, 0, 0);
-    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_lo, vb, st.acc[c], 0, 0, 0);
+    if (!F::G16) {
+      const half8_t vb = __builtin_bit_cast(half8_t, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, vb, st.acc[c], 0, 0, 0);
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_lo, vb, st.acc[c], 0, 0, 0);
+    } else {
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      const uint4 h4 = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+      const half8_t v0 = __builtin_bit_cast(half8_t, odd_group ? z : h4);
+      const half8_t v1 = __builtin_bit_cast(half8_t, odd_group ? h4 : z);
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_hi, v0, st.acc[c], 0, 0, 0);
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa_lo, v0, st.acc[c], 0, 0, 0);
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pb_hi, v1, st.acc[c], 0, 0, 0);
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pb_lo, v1, st.acc[c], 0, 0, 0);
+    }
   }
 }
 
@@ -675,10 +807,11 @@ __device__ __forceinline__ void process4(State<true>& st, const Blk4& cur, uint3
 constexpr int kWavesPerCuInt4 = 16;
 constexpr int kWavesPerCuF16 = 16;
 
-template <bool INT4, int ROT>
+template <bool INT4, int ROT, int FMT>
 __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
-  // rotated query records of the wave's heads (int4 cache)
-  __shared__ __attribute__((aligned(16))) uint8_t qrec[kHeadsPerWave * kQRec];
+  using F = QF<FMT>;
+  // rotated query records of the wave's heads (quantized cache)
+  __shared__ __attribute__((aligned(16))) uint8_t qrec[kHeadsPerWave * F::REC];
   const int lane = threadIdx.x;
   const int n16 = lane & 15;
   const int kq = lane >> 4;
@@ -698,10 +831,10 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
   const uint32_t t_end = static_cast<uint32_t>(min(s * a.chunk + a.chunk, a.seq_len));
   const int64_t cell0 = (b * a.Hkv + g) * a.Tcap;
   Rows rows;
-  rows.kc = a.k_codes + cell0 * 64;
-  rows.ksc = a.k_scales + cell0 * 4;
-  rows.vc = a.v_codes + cell0 * 64;
-  rows.vsc = a.v_scales + cell0 * 4;
+  rows.kc = a.k_codes + cell0 * F::CBT;
+  rows.ksc = a.k_scales + cell0 * (F::SBT / 2);
+  rows.vc = a.v_codes + cell0 * F::CBT;
+  rows.vsc = a.v_scales + cell0 * (F::SBT / 2);
   rows.k16 = a.k16 + cell0 * 128;
   rows.v16 = a.v16 + cell0 * 128;
 
@@ -718,10 +851,10 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
   QueryIn qin;
   auto init_query = [&]() {
     // all four records (heads past nh hold a zero word and are never read)
-    query_records<ROT>(a, qin, lane, qrec);
+    query_records<ROT, F::REC, F::G16 && F::BITS == 4>(a, qin, lane, qrec);
     // one wave: its LDS writes are visible once its LDS counter drains
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const uint8_t* rec = qrec + (head_ok ? my_head : 0) * kQRec;
+    const uint8_t* rec = qrec + (head_ok ? my_head : 0) * F::REC;
     const int grp = n16 >> 2;
     const bool live = head_ok && grp == kq;
 #pragma unroll
@@ -730,17 +863,44 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         d[e] = live ? reinterpret_cast<const uint32_t*>(rec + 128 * limb + 32 * kq)[e] : 0u;
-      // k slot j of k-step ks <-> channel 32 kq + 2 j + ks
+      if (FMT == 0) {
+        // k slot j of k-step ks <-> channel 32 kq + 2 j + ks
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint32_t sel = ks ? 0x07050301u : 0x06040200u;
-        st.qb[limb][ks] = (int4_t){static_cast<int>(__builtin_amdgcn_perm(d[1], d[0], sel)),
-                                   static_cast<int>(__builtin_amdgcn_perm(d[3], d[2], sel)),
-                                   static_cast<int>(__builtin_amdgcn_perm(d[5], d[4], sel)),
-                                   static_cast<int>(__builtin_amdgcn_perm(d[7], d[6], sel))};
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint32_t sel = ks ? 0x07050301u : 0x06040200u;
+          st.qb[limb][ks] = (int4_t){static_cast<int>(__builtin_amdgcn_perm(d[1], d[0], sel)),
+                                     static_cast<int>(__builtin_amdgcn_perm(d[3], d[2], sel)),
+                                     static_cast<int>(__builtin_amdgcn_perm(d[5], d[4], sel)),
+                                     static_cast<int>(__builtin_amdgcn_perm(d[7], d[6], sel))};
+        }
+      } else if (F::BITS == 4) {
+        // k-step ks covers channels 32 kq + 16 ks + (0, 2, 4, 6, 1, 3, 5, 7,
+        // 8, 10, 12, 14, 9, 11, 13, 15): the order the nibbles of four code
+        // bytes enter as low, high, low, high words
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          st.qb[limb][ks] = (int4_t){static_cast<int>(__builtin_amdgcn_perm(d[4 * ks + 1], d[4 * ks], 0x06040200u)),
+                                     static_cast<int>(__builtin_amdgcn_perm(d[4 * ks + 1], d[4 * ks], 0x07050301u)),
+                                     static_cast<int>(__builtin_amdgcn_perm(d[4 * ks + 3], d[4 * ks + 2], 0x06040200u)),
+                                     static_cast<int>(__builtin_amdgcn_perm(d[4 * ks + 3], d[4 * ks + 2], 0x07050301u))};
+      } else {
+        // int8 codes in channel order: k-step ks covers channels 32 kq + 16 ks ..
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          st.qb[limb][ks] = (int4_t){static_cast<int>(d[4 * ks]), static_cast<int>(d[4 * ks + 1]),
+                                     static_cast<int>(d[4 * ks + 2]), static_cast<int>(d[4 * ks + 3])};
       }
-      const int sum = head_ok ? reinterpret_cast<const int*>(rec + kRecSum)[4 * limb + grp] : 0;
-      st.corr[limb] = (int4_t){-8 * sum, -8 * sum, -8 * sum, -8 * sum};
+      // unsigned int4 nibbles (n = q + 8): the accumulators start at -8 sum(Q)
+      // over the channels they cover; int8 codes are signed
+      int c0 = 0, c1 = 0;
+      if (F::BITS == 4 && !F::G16) {
+        c0 = -8 * (head_ok ? reinterpret_cast<const int*>(rec + kRecSum)[4 * limb + grp] : 0);
+      } else if (F::BITS == 4) {
+        c0 = -8 * (head_ok ? reinterpret_cast<const int*>(rec + kRecSum16)[8 * limb + 2 * grp] : 0);
+        c1 = -8 * (head_ok ? reinterpret_cast<const int*>(rec + kRecSum16)[8 * limb + 2 * grp + 1] : 0);
+      }
+      st.corr[limb] = (int4_t){c0, c0, c0, c0};
+      st.corr1[limb] = (int4_t){c1, c1, c1, c1};
     }
     st.sfac = head_ok ? reinterpret_cast<const float*>(rec + kRecS)[grp] * (1.f / 65536.f) : 0.f;
   };
@@ -784,7 +944,7 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
     uint32_t mag_lo, mag_hi;     // fp16 pairs (1024, 1024), (64, 64) as v_and_or operands
     asm("v_mov_b32 %0, 0x64006400" : "=v"(mag_lo));
     asm("v_mov_b32 %0, 0x54005400" : "=v"(mag_hi));
-    const Off4 o4 = lane_offsets4(n16, kq);
+    const Off4 o4 = lane_offsets4<FMT>(n16, kq);
     const uint32_t seq = static_cast<uint32_t>(a.seq_len);
     const uint32_t nbr = (seq + kBlk - 1) / kBlk;                    // blocks of the row
     const uint32_t S = static_cast<uint32_t>(a.S);
@@ -797,38 +957,38 @@ __global__ void __launch_bounds__(64, 2) attn_split_kernel(AttnArgs a) {
     uint32_t t0 = kBlk * sp;
     State<true>& s4 = reinterpret_cast<State<true>&>(st);
     query_loads<ROT>(a, a.q + qrow0 * 128, nh, a.lambda_k + g * 128, lane, qin);
-    Blk4 b0, b1;
+    Blk4<FMT> b0, b1;
     if (n_full == 0) {
-      if (has_tail) load4<true>(rows, t0, t_last, o4, n16, kq, b0);
+      if (has_tail) load4<FMT, true>(rows, t0, t_last, o4, n16, kq, b0);
       init_query();
-      if (has_tail) process4<true>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+      if (has_tail) process4<FMT, true>(s4, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
     } else {
-      load4<false>(rows, t0, t_last, o4, n16, kq, b0);
+      load4<FMT, false>(rows, t0, t_last, o4, n16, kq, b0);
       init_query();
       // b0 holds block i at the top; blocks i + 1 and i + 2 are full
       int i = 0;
       for (; i + 2 < n_full; i += 2) {
-        load4<false>(rows, t0 + step, t_last, o4, n16, kq, b1);
-        process4<false>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+        load4<FMT, false>(rows, t0 + step, t_last, o4, n16, kq, b1);
+        process4<FMT, false>(s4, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
         t0 += step;
-        load4<false>(rows, t0 + step, t_last, o4, n16, kq, b0);
-        process4<false>(s4, b1, t0, t_end, kq, mag_lo, mag_hi);
+        load4<FMT, false>(rows, t0 + step, t_last, o4, n16, kq, b0);
+        process4<FMT, false>(s4, b1, t0, t_end, kq, n16, mag_lo, mag_hi);
         t0 += step;
       }
       // one or two full blocks left, then maybe the tail
       if (n_full - i == 2) {
-        load4<false>(rows, t0 + step, t_last, o4, n16, kq, b1);
-        process4<false>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+        load4<FMT, false>(rows, t0 + step, t_last, o4, n16, kq, b1);
+        process4<FMT, false>(s4, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
         t0 += step;
-        if (has_tail) load4<true>(rows, t0 + step, t_last, o4, n16, kq, b0);
-        process4<false>(s4, b1, t0, t_end, kq, mag_lo, mag_hi);
+        if (has_tail) load4<FMT, true>(rows, t0 + step, t_last, o4, n16, kq, b0);
+        process4<FMT, false>(s4, b1, t0, t_end, kq, n16, mag_lo, mag_hi);
         t0 += step;
-        if (has_tail) process4<true>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+        if (has_tail) process4<FMT, true>(s4, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
       } else {
-        if (has_tail) load4<true>(rows, t0 + step, t_last, o4, n16, kq, b1);
-        process4<false>(s4, b0, t0, t_end, kq, mag_lo, mag_hi);
+        if (has_tail) load4<FMT, true>(rows, t0 + step, t_last, o4, n16, kq, b1);
+        process4<FMT, false>(s4, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
         t0 += step;
-        if (has_tail) process4<true>(s4, b1, t0, t_end, kq, mag_lo, mag_hi);
+        if (has_tail) process4<FMT, true>(s4, b1, t0, t_end, kq, n16, mag_lo, mag_hi);
       }
     }
   } else {
@@ -1015,10 +1175,17 @@ template <int ROT>
 hipError_t run_attention(const AttnDesc& d, AttnArgs& a) {
   const int int4 = d.int4 ? 1 : 0;
   const unsigned nsplit = static_cast<unsigned>(d.B * d.Hkv * a.n_hchunks * a.S);
-  if (d.int4) {
-    hipLaunchKernelGGL((attn_split_kernel<true, ROT>), dim3(nsplit), dim3(64), 0, d.stream, a);
+  const int fmt = (d.bits == 8 ? 2 : 0) + (d.G == 16 ? 1 : 0);
+  if (!d.int4) {
+    hipLaunchKernelGGL((attn_split_kernel<false, KVQ_ROT_ID, 0>), dim3(nsplit), dim3(64), 0, d.stream, a);
+  } else if (fmt == 1) {
+    hipLaunchKernelGGL((attn_split_kernel<true, ROT, 1>), dim3(nsplit), dim3(64), 0, d.stream, a);
+  } else if (fmt == 2) {
+    hipLaunchKernelGGL((attn_split_kernel<true, ROT, 2>), dim3(nsplit), dim3(64), 0, d.stream, a);
+  } else if (fmt == 3) {
+    hipLaunchKernelGGL((attn_split_kernel<true, ROT, 3>), dim3(nsplit), dim3(64), 0, d.stream, a);
   } else {
-    hipLaunchKernelGGL((attn_split_kernel<false, KVQ_ROT_ID>), dim3(nsplit), dim3(64), 0, d.stream, a);
+    hipLaunchKernelGGL((attn_split_kernel<true, ROT, 0>), dim3(nsplit), dim3(64), 0, d.stream, a);
   }
   const unsigned nc = static_cast<unsigned>(d.B * d.Hq);
   if (d.out_f32) {

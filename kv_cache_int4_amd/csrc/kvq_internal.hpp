@@ -35,7 +35,9 @@ struct AttnDesc {
   int D;
   int rotation;
   uint64_t signs[4];
-  bool int4;                  // int4 cache (true) or fp16 cache (false)
+  bool int4;                  // quantized cache (true) or fp16 cache (false)
+  int G;                      // quantized cache: group size (32 or 16)
+  int bits;                   // quantized cache: code width (4 or 8)
   const uint16_t* q;
   const uint8_t* k_codes;
   const uint16_t* k_scales;

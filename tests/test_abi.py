@@ -158,10 +158,6 @@ def test_attention_validation():
     assert call(vc=None) == INVALID
     assert call(dt=5) == INVALID
     assert call(B=0) == OK                            # nothing to do
-    for bits, G in ((4, 16), (8, 32), (8, 16)):     # attention is built for int4 in groups of 32
-        pf = K.Plan(128, G, "srft", 3, bits=bits)
-        assert L.kvq_attn_decode(pf.handle, A, A, A, A, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need,
-                                 None) == UNSUPPORTED
     p256 = K.Plan(256, 32, "srft", 3)
     assert L.kvq_attn_decode(p256.handle, A, A, A, A, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need,
                              None) == UNSUPPORTED

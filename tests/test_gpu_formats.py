@@ -1,12 +1,16 @@
 """GPU parity of the code-format variants: int4 codes in groups of 16, int8
 codes (scale = fp16(absmax / 127), two's-complement bytes) in groups of 32
-and 16, through the same encode / decode entry points and kernels as the
-int4 group-32 cache, against the CPU oracle on the same seeded inputs.
+and 16, through the same encode / decode / attention entry points and
+kernels as the int4 group-32 cache, against the CPU oracle on the same
+seeded inputs.
 
 The bars are those of the int4 cache: codes and scales bit-exact except
-within 1e-4 of a rounding boundary (mismatch fraction below 1e-5), decoded
-values within 1e-3 absolute (fp32) or half an fp16 ulp plus 1e-3 (fp16).
+within 1e-4 of a rounding boundary (mismatch fraction below 1e-5 for int4,
+1e-4 for int8 codes), decoded values within 1e-3 absolute (fp32) or half an
+fp16 ulp plus 1e-3 (fp16), attention within 2e-3 relative per (batch, head).
 """
+
+import math
 
 import numpy as np
 import pytest
@@ -16,7 +20,7 @@ import oracle as O
 import kv_cache_int4_amd as K
 from kv_cache_int4_amd import workloads as W
 from tests import parity as P
-from tests.test_gpu_parity import ROTS, check_encode, lam_per_vector, np16, say
+from tests.test_gpu_parity import ROTS, check_encode, lam_per_vector, np16, run_attn, say
 
 pytestmark = pytest.mark.gpu
 
@@ -148,3 +152,99 @@ def test_format_special_groups(fmt, D):
     assert np.array_equal(s.reshape(N, -1).view(np.uint16), scales_ref.view(np.uint16))
     assert np.array_equal(c.reshape(N, -1), codes_ref)
     assert (O.unpack_codes(codes_ref, bits) == qmin).any()
+
+
+# -------------------------------------------------------------- attention --
+
+def format_cache(plan, B, Hkv, Hq, T, Tcap, seed, plant=()):
+    """Decode-step inputs and their caches in the plan's format (tokens
+    0..T-1 encoded with kvq_encode).  plant: (b, query head, token) spots
+    whose key is made to dominate that head's scores."""
+    D = plan.D
+    k16, v16, lam_k, lam_v, q = W.decode_inputs(B, Hkv, Hq, Tcap, D, seed, "cuda")
+    rep = Hq // Hkv
+    for b, h, t in plant:
+        qv = q[b, h].float()
+        k16[b, h // rep, t] = (1200.0 / float((qv * qv).sum()) * qv).to(torch.float16)
+    kc = torch.empty((B, Hkv, Tcap, plan.code_bytes), dtype=torch.uint8, device="cuda")
+    ksc = torch.empty((B, Hkv, Tcap, D // plan.G), dtype=torch.float16, device="cuda")
+    vc, vsc = torch.empty_like(kc), torch.empty_like(ksc)
+    K.encode(plan, k16[:, :, :T], lam_k, kc, ksc, 0)
+    K.encode(plan, v16[:, :, :T], lam_v, vc, vsc, 0)
+    return q, kc, ksc, vc, vsc, lam_k, lam_v
+
+
+def oracle_attention(plan, rot, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm):
+    signs = O.plan_signs(plan.D, ROTS[rot], plan.seed)
+    return O.attention_int4(np16(q), kc.cpu().numpy(), ksc.cpu().numpy(), lam_k.cpu().numpy(),
+                            vc.cpu().numpy(), vsc.cpu().numpy(), lam_v.cpu().numpy(), L, sm, ROTS[rot], signs,
+                            plan.G, plan.bits)
+
+
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
+@pytest.mark.parametrize("rot", ["srft", "srht", "identity"])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (2, 1)])
+@pytest.mark.parametrize("L", [17, 2051])
+def test_format_attention(fmt, rot, Hq, Hkv, L):
+    bits, G = FORMATS[fmt]
+    D, B = 128, 2
+    plan = K.Plan(D, G, rot, 33, bits=bits)
+    say(f"[attn] {fmt} rot={rot} Hq={Hq} Hkv={Hkv} L={L}")
+    q, kc, ksc, vc, vsc, lam_k, lam_v = format_cache(plan, B, Hkv, Hq, L, L + 9, 13)
+    sm = 1 / math.sqrt(D)
+    ref = oracle_attention(plan, rot, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm)
+    for dt in (torch.float32, torch.float16):
+        out = run_attn(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, dt)
+        worst = P.compare_attention(np16(out), ref)
+        say(f"   {dt}: rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
+def test_format_attention_dominant_token(fmt):
+    """Planted dominant tokens (rows 1-3 of a block, the tail block, a later
+    split) in every format: the softmax maximum must cover every row."""
+    bits, G = FORMATS[fmt]
+    D, B, Hq, Hkv, L = 128, 2, 8, 2, 2051
+    plan = K.Plan(D, G, "srft", 59, bits=bits)
+    spots = [(0, 0, 5), (0, 3, 1047), (1, 5, L - 1), (1, 6, 324), (1, 1, 1601)]
+    q, kc, ksc, vc, vsc, lam_k, lam_v = format_cache(plan, B, Hkv, Hq, L, L + 5, 27, spots)
+    sm = 1 / math.sqrt(D)
+    ref = oracle_attention(plan, "srft", q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm)
+    out = run_attn(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, torch.float32)
+    worst = P.compare_attention(np16(out), ref)
+    say(f"   {fmt} dominant tokens: rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
+def test_format_attention_decode_step_full_size(fmt):
+    """The decode step at full size in every format: batch 64, Hq 8 / Hkv 2,
+    32768 cached tokens plus one appended (T=1, t0=32768); 4 seeded (b, kv
+    head) pairs checked against the oracle."""
+    bits, G = FORMATS[fmt]
+    cfg = W.CONFIGS["decode"]
+    B, Hkv, Hq, D = cfg.B, cfg.H, 8, cfg.D
+    T0 = cfg.T
+    L, Tcap = T0 + 1, T0 + 256
+    plan = K.Plan(D, G, "srft", cfg.sign_seed, bits=bits)
+    say(f"[attn-full] {fmt}: building caches")
+    k16, v16, lam_k, lam_v, q = W.decode_inputs(B, Hkv, Hq, Tcap, D, cfg.data_seed, "cuda")
+    kc = torch.empty((B, Hkv, Tcap, plan.code_bytes), dtype=torch.uint8, device="cuda")
+    ksc = torch.empty((B, Hkv, Tcap, D // G), dtype=torch.float16, device="cuda")
+    vc, vsc = torch.empty_like(kc), torch.empty_like(ksc)
+    K.encode(plan, k16[:, :, :T0], lam_k, kc, ksc, 0)
+    K.encode(plan, v16[:, :, :T0], lam_v, vc, vsc, 0)
+    K.encode(plan, k16[:, :, T0:T0 + 1], lam_k, kc, ksc, T0)
+    K.encode(plan, v16[:, :, T0:T0 + 1], lam_v, vc, vsc, T0)
+    sm = 1 / math.sqrt(D)
+    out = run_attn(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, torch.float16)
+    rng = np.random.default_rng(6)
+    rep = Hq // Hkv
+    for b, g in [(int(b), int(g)) for b, g in zip(rng.choice(B, 4, replace=False), rng.integers(0, Hkv, 4))]:
+        sl = slice(b, b + 1)
+        signs = O.plan_signs(D, O.SRFT, plan.seed)
+        ref = O.attention_int4(np16(q[sl, g * rep:(g + 1) * rep]), kc[sl, g:g + 1, :L].cpu().numpy(),
+                               ksc[sl, g:g + 1, :L].cpu().numpy(), lam_k[g:g + 1].cpu().numpy(),
+                               vc[sl, g:g + 1, :L].cpu().numpy(), vsc[sl, g:g + 1, :L].cpu().numpy(),
+                               lam_v[g:g + 1].cpu().numpy(), L, sm, O.SRFT, signs, G, bits)
+        w = P.compare_attention(np16(out[sl, g * rep:(g + 1) * rep]).astype(np.float64), ref)
+        say(f"   (b={b}, g={g}): rel {w:.2e}")
