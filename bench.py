@@ -12,7 +12,9 @@ set (about 1.8 GB) is far beyond the 256 MB Infinity Cache.  The fp16-cache
 comparator (same attention over an unquantized cache) is timed in its own
 loop right after the timed region, and so is the D=256 leg: encode and
 decode of the Gemma-3-1B-shaped prefix (212,992 vectors) with SRFT and SRHT
-(field "d256").
+(field "d256"), and the code-format variants (field "formats": int4 in groups
+of 16, int8 in groups of 32 and 16; encode and decode of the Qwen prefix and
+the decode-step attention over a cache in that format).
 
 Prints ONE JSON line.  `value` is the encode throughput (Mvec/s) over the
 timed region, measured with HIP events at the phase boundaries on the stream
@@ -40,12 +42,12 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # the kernel sources they were taken on (sha256 prefix of the listed files);
 # reported as null once those change.
 TRAFFIC = {
-    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "48c61fdbfaf66cfd",
-             "bytes": (295675.5 + 4210.5) * 2 * 1024 + (8721.7 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "26a1b9821aee5881",
-               "bytes": 57712.7 * 2 * 1024 + 32256.0 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "26a1b9821aee5881",
-               "bytes": 16456.4 * 2 * 1024 + 114794.1 * 1024},
+    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "d45627ff24ec99a2",
+             "bytes": (295697.2 + 4199.5) * 2 * 1024 + (8726.1 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "a44034939f932fd0",
+               "bytes": 57707.0 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "a44034939f932fd0",
+               "bytes": 16460.5 * 2 * 1024 + 114770.2 * 1024},
 }
 
 
@@ -219,6 +221,60 @@ def d256_leg(K, torch, stream, cfg, sets, n):
     return res
 
 
+FORMATS = (("int4-g16", 4, 16), ("int8-g32", 8, 32), ("int8-g16", 8, 16))
+
+
+def formats_leg(K, torch, stream, cfg, sets, dc, k16, v16, lam_k, lam_v, q, L, sm, n):
+    """The code-format variants (int4 in groups of 16, int8 in groups of 32
+    and 16) on the same work: encode and decode of the Qwen prefix batches,
+    and the decode-step attention over a cache in that format, each timed
+    over n launches with HIP events on the kernels' stream."""
+    D = cfg.D
+    B, Hkv, Hq = dc.B, dc.H, q.shape[1]
+    T0, Tcap = L - 1, k16.shape[2]
+    ns = len(sets)
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device=q.device)
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    res = {}
+    for name, bits, G in FORMATS:
+        plan = K.Plan(D, G, "srft", cfg.sign_seed, bits=bits)
+        cb, nsc = plan.code_bytes, D // G
+        bufs = [(torch.empty((cfg.B, cfg.H, cfg.T, cb), dtype=torch.uint8, device=q.device),
+                 torch.empty((cfg.B, cfg.H, cfg.T, nsc), dtype=torch.float16, device=q.device)) for _ in range(ns)]
+        enc = timed(lambda i: K.encode(plan, sets[i % ns][0], sets[i % ns][1], *bufs[i % ns]))
+        dec = timed(lambda i: K.decode(plan, *bufs[i % ns], sets[i % ns][1], sets[i % ns][4]))
+        del bufs
+        kc = torch.empty((B, Hkv, Tcap, cb), dtype=torch.uint8, device=q.device)
+        ksc = torch.empty((B, Hkv, Tcap, nsc), dtype=torch.float16, device=q.device)
+        vc, vsc = torch.empty_like(kc), torch.empty_like(ksc)
+        K.encode(plan, k16[:, :, :L], lam_k, kc, ksc, 0)
+        K.encode(plan, v16[:, :, :L], lam_v, vc, vsc, 0)
+        att = timed(lambda i: K.attn_decode(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, out, ws))
+        del kc, ksc, vc, vsc
+        vb = 2 * D + cb + 2 * nsc                    # bytes per vector, encode or decode
+        ab = B * Hkv * L * 2 * (cb + 2 * nsc)        # K and V codes + scales per step
+        nv = cfg.vectors
+        res[name] = {
+            "encode_us": round(enc, 2), "encode_frac_hbm": round(nv * vb / enc / 1e3 / HBM_PEAK_GBS, 4),
+            "decode_us": round(dec, 2), "decode_frac_hbm": round(nv * vb / dec / 1e3 / HBM_PEAK_GBS, 4),
+            "attn_us": round(att, 2), "attn_bytes": ab, "attn_frac_hbm": round(ab / att / 1e3 / HBM_PEAK_GBS, 4),
+        }
+    torch.cuda.synchronize()
+    return res
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -339,6 +395,8 @@ def main():
     # ---- D=256 (Gemma-3-1B-shaped prefix), both rotations, timed apart ----
     gemma = d256_leg(K, torch, stream, g_cfg, g_sets, max(10, args.steps))
     del g_sets
+    # ---- code formats (int4 G16, int8 G32 / G16), timed apart ----
+    fmts = formats_leg(K, torch, stream, cfg, sets, dc, k16, v16, lam_k, lam_v, q, L, sm, max(10, args.steps))
     if args.profile_marks:
         src = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -420,6 +478,7 @@ def main():
                       "fp16_GB_s": round(attn16_bytes / (f16_us / 1e6) / 1e9, 1),
                       "int4_over_fp16": round(attn_us / f16_us, 4)},
         "d256": gemma,
+        "formats": fmts,
     }
     print(json.dumps(res), flush=True)
 
