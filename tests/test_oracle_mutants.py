@@ -213,6 +213,7 @@ CHECKS = [
     P.check_codes_int8_exhaustive,
     P.check_compression_variants,
     P.check_attention_bruteforce_int8,
+    P.check_srft_mixed_radix,
 ]
 
 

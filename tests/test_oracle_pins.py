@@ -145,6 +145,50 @@ def test_srft_equals_explicit_dft_matrix():
     check_srft_against_dft_matrix()
 
 
+# Mixed-radix SRFT (non-power-of-two D: the pages pick SRFT over SRHT for
+# its mixed-radix sizes, abstract): the same definition at D = 6, 10, 12
+# (M = 3, 5, 6) by brute force, and at D = 80, 96 (M = 40, 48) against
+# scipy's explicit DFT matrix, the closed-form columns and orthogonality.
+
+def check_srft_mixed_radix():
+    check_srft_bruteforce(Ds=(6, 10, 12, 20))
+    check_srft_against_dft_matrix(Ds=(80, 96))
+    check_srft_one_hot(80)
+    check_srft_one_hot(96)
+    for D in (80, 96):
+        s = O.plan_signs(D, O.SRFT, 17 + D)
+        assert s.size == D // 2
+        R = O.rotation_matrix(D, O.SRFT, s)
+        assert np.max(np.abs(R @ R.T - np.eye(D))) < 1e-12
+        x = _rng(D).standard_normal((7, D))
+        assert np.max(np.abs(O.rotate_inverse(O.rotate_forward(x, O.SRFT, s), O.SRFT, s) - x)) < 1e-12
+
+
+def test_srft_mixed_radix_sizes():
+    check_srft_mixed_radix()
+
+
+def test_quantizer_on_mixed_radix_sizes():
+    """Groups of 32 at D = 96 (3 groups) and of 16 at D = 80 (5 groups): the
+    sigma/2 bound in the w domain and through orthogonality."""
+    rng = _rng(21)
+    for D, G in ((96, 32), (96, 16), (80, 16)):
+        x = (rng.standard_normal((500, D)) * 2).astype(np.float16)
+        lam = np.exp(0.3 * rng.standard_normal(D)).astype(np.float32)
+        s = O.plan_signs(D, O.SRFT, 3)
+        for bits in (4, 8):
+            codes, scales, w = O.encode(x, lam, O.SRFT, s, G, bits)
+            assert codes.shape == (500, D * bits // 8) and scales.shape == (500, D // G)
+            q = O.unpack_codes(codes, bits).astype(np.float64)
+            sig = np.repeat(scales.astype(np.float64), G, axis=-1)
+            normal = sig >= 2.0 ** -14
+            assert np.all((np.abs(w - q * sig) <= sig / 2 + np.abs(w) * 2.0 ** -23)[normal])
+            xh = O.decode(codes, scales, lam, O.SRFT, s, G, bits)
+            lhs = np.linalg.norm(x.astype(np.float64) - xh, axis=-1)
+            rhs = np.linalg.norm(sig / (2 * lam.astype(np.float64)), axis=-1)
+            assert np.all(lhs <= rhs * (1 + 1e-6) + 1e-9)
+
+
 def test_srft_one_hot_closed_form():
     check_srft_one_hot(128)
     check_srft_one_hot(256)
