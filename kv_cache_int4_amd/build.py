@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
 
-SOURCES = ["kvq_api.cpp", "kvq_codec.hip", "kvq_attn.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_codec.hip", "kvq_mixed.hip", "kvq_attn.hip"]
 
 ARCH = "gfx950"
 COMMON = [

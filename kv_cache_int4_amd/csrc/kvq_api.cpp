@@ -155,9 +155,13 @@ kvq_status kvq_plan_create_ex(int32_t D, int32_t G, int32_t bits, kvq_rotation r
     *out = nullptr;
     if (rotation != KVQ_SRFT && rotation != KVQ_SRHT && rotation != KVQ_IDENTITY)
       return fail(KVQ_ERR_INVALID, "unknown rotation %d", (int)rotation);
-    if (D != 128 && D != 256) return fail(KVQ_ERR_UNSUPPORTED, "D=%d (built: 128, 256)", (int)D);
+    if (D != 128 && D != 256 && D != 80 && D != 96)
+      return fail(KVQ_ERR_UNSUPPORTED, "D=%d (built: 80, 96, 128, 256)", (int)D);
     if (G != 32 && G != 16) return fail(KVQ_ERR_UNSUPPORTED, "G=%d (built: 32, 16)", (int)G);
+    if (D % G) return fail(KVQ_ERR_UNSUPPORTED, "G=%d does not divide D=%d", (int)G, (int)D);
     if (bits != 4 && bits != 8) return fail(KVQ_ERR_UNSUPPORTED, "bits=%d (built: 4, 8)", (int)bits);
+    if ((D == 80 || D == 96) && rotation == KVQ_SRHT)
+      return fail(KVQ_ERR_UNSUPPORTED, "SRHT needs a power-of-two D (D=%d)", (int)D);
     kvq_plan* p = new (std::nothrow) kvq_plan;
     if (!p) return fail(KVQ_ERR_INVALID, "out of host memory");
     p->D = D;

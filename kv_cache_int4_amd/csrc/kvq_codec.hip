@@ -33,27 +33,6 @@ namespace kvq {
 namespace {
 
 // One plan-independent description of a codec launch.
-// Division by a call constant d (1 <= d < 2^32) of n < 2^32 (tile and row
-// indices): with M = floor((2^64 - 1) / d) + 1 = ceil(2^64 / d), n * M / 2^64
-// exceeds n / d by less than n / 2^64 < 2^-32, while n / d is at least 1/d
-// below the next integer, so the high 64 bits of n * M are floor(n / d).
-// d = 1 uses M = 0 and returns n.
-struct FastDiv {
-  uint64_t magic;
-  uint64_t d;
-};
-
-inline FastDiv make_fastdiv(uint64_t d) {
-  FastDiv f;
-  f.d = d;
-  f.magic = d <= 1 ? 0 : (~0ull / d) + 1;
-  return f;
-}
-
-__device__ __forceinline__ uint64_t fdiv(uint64_t n, const FastDiv& f) {
-  return f.magic == 0 ? n : __umul64hi(n, f.magic);
-}
-
 struct CodecArgs {
   const uint16_t* x;          // encode / rotate input, fp16
   const uint8_t* codes_in;    // decode input
@@ -587,11 +566,10 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
             amax = fmaxf(amax, fabsf(wv));
           }
         }
-        // scale = fp16(absmax / qmax), from absmax * fp32(1/qmax): the
-        // product is within an fp32 ulp of the quotient, so the fp16 rounding
-        // differs from the exact quotient's only within ~1e-7 (relative) of
-        // an fp16 rounding midpoint
-        sc[g] = f32_to_f16_bits(amax * (kScale * (1.0f / F::QMAX)));
+        // scale = fp16(fp32(absmax / qmax)) with the IEEE fp32 quotient
+        // (a handful of instructions per group); amax * kScale is the
+        // unitary abs-max, exact where kScale is a power of two
+        sc[g] = f32_to_f16_bits((amax * kScale) / F::QMAX);
         const float sf = f16_bits_to_f32(sc[g]);
         r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
         tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);    // fp16-subnormal scale
@@ -794,7 +772,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
           amax = fmaxf(amax, fabsf(wv));
         }
       }
-      sc[g] = f32_to_f16_bits(amax * (kScale * (1.0f / F::QMAX)));
+      sc[g] = f32_to_f16_bits((amax * kScale) / F::QMAX);
       const float sf = f16_bits_to_f32(sc[g]);
       r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
       tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);
@@ -1528,11 +1506,15 @@ hipError_t decode_rot(const CodecDesc& d, bool f32) {
 }  // namespace
 
 hipError_t launch_encode(const CodecDesc& d, int mode) {
-  return d.D == 128 ? encode_rot<128>(d, mode) : encode_rot<256>(d, mode);
+  if (d.D == 128) return encode_rot<128>(d, mode);
+  if (d.D == 256) return encode_rot<256>(d, mode);
+  return launch_encode_mixed(d, mode);
 }
 
 hipError_t launch_decode(const CodecDesc& d, bool f32) {
-  return d.D == 128 ? decode_rot<128>(d, f32) : decode_rot<256>(d, f32);
+  if (d.D == 128) return decode_rot<128>(d, f32);
+  if (d.D == 256) return decode_rot<256>(d, f32);
+  return launch_decode_mixed(d, f32);
 }
 
 }  // namespace kvq

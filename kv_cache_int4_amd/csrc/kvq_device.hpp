@@ -193,6 +193,31 @@ __device__ __forceinline__ void st_stream16(void* p, const uint4& w) {
 }
 
 // ---------------------------------------------------------------------------
+// Index arithmetic
+// ---------------------------------------------------------------------------
+
+// Division by a call constant d (1 <= d < 2^32) of n < 2^32 (tile and row
+// indices): with M = floor((2^64 - 1) / d) + 1 = ceil(2^64 / d), n * M / 2^64
+// exceeds n / d by less than n / 2^64 < 2^-32, while n / d is at least 1/d
+// below the next integer, so the high 64 bits of n * M are floor(n / d).
+// d = 1 uses M = 0 and returns n.
+struct FastDiv {
+  uint64_t magic;
+  uint64_t d;
+};
+
+inline __host__ FastDiv make_fastdiv(uint64_t d) {
+  FastDiv f;
+  f.d = d;
+  f.magic = d <= 1 ? 0 : (~0ull / d) + 1;
+  return f;
+}
+
+__device__ __forceinline__ uint64_t fdiv(uint64_t n, const FastDiv& f) {
+  return f.magic == 0 ? n : __umul64hi(n, f.magic);
+}
+
+// ---------------------------------------------------------------------------
 // Quantizer helpers
 // ---------------------------------------------------------------------------
 

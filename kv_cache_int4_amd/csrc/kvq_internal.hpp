@@ -61,6 +61,9 @@ int device_cu_count();
 // mode 0 = encode (codes + scales), mode 1 = rotate (fp32 w)
 hipError_t launch_encode(const CodecDesc& d, int mode);
 hipError_t launch_decode(const CodecDesc& d, bool f32);
+// D = 80 and 96 (SRFT over the mixed-radix DFT, or no rotation)
+hipError_t launch_encode_mixed(const CodecDesc& d, int mode);
+hipError_t launch_decode_mixed(const CodecDesc& d, bool f32);
 
 // Split-K geometry of the attention kernels.
 int64_t attn_num_splits(int64_t B, int64_t Hkv, int64_t seq_len);

@@ -147,6 +147,11 @@ CONFIGS = {
     "decode": Config("gqa-decode-B64-Hq8-Hkv2-L32769-D128", 128, 64, 2, 32768, "spread", 4),
     # Mistral-7B bulk: 32 layers x {K,V}, batch 16 x 8 heads x 8192 tokens, D=128
     "mistral": Config("mistral-7b-bulk-32Lx2-B16-H8-T8192-D128", 128, 16, 8, 8192, "t3", 5),
+    # head sizes that are not powers of two (mixed-radix SRFT): the prefix
+    # shape of "qwen" (28 layers x {K,V} x 2 KV heads x 4096 tokens) at D=96
+    # and D=80
+    "d96": Config("prefix-28Lx2x2Hx4096-D96", 96, 56, 2, 4096, "spread", 6),
+    "d80": Config("prefix-28Lx2x2Hx4096-D80", 80, 56, 2, 4096, "spread", 7),
 }
 
 

@@ -14,8 +14,12 @@ units, is about 127/7 times larger on the int8 grid, and so is the expected
 rate of boundary flips (2 E|w/scale| times the relative error), which puts
 the int4 bar at 1.8e-4 for int8; 1e-4 is kept.  Smaller samples cannot
 resolve a rate of 1e-5 (the expected count is below 10); there every
-mismatch must still be a boundary case and the count may not exceed
-max(1, 3e-5 * elements), three times the expected count at the bar.
+mismatch must still be a boundary case, and the count may not exceed the
+99.9% quantile of a Poisson count whose mean is the bar times the number of
+elements: a kernel whose rate sits exactly at the bar fails a given small
+test at most once in a thousand runs.  (Flips are rare independent events,
+so their count in n elements is Poisson; a fixed multiple of the mean is
+too tight where the mean is below one.)
 """
 
 from __future__ import annotations
@@ -27,6 +31,17 @@ import oracle as O
 BOUNDARY = 1e-4
 FRACTION = 1e-5          # int4 codes
 FRACTION8 = 1e-4         # int8 codes (see above)
+
+
+def poisson_quantile(mu: float, p: float = 0.999) -> int:
+    """Smallest k with P(Poisson(mu) <= k) >= p."""
+    term = cdf = np.exp(-mu)
+    k = 0
+    while cdf < p:
+        k += 1
+        term *= mu / k
+        cdf += term
+    return k
 
 
 def requantize(w64: np.ndarray, scales16: np.ndarray, G: int = O.GROUP, bits: int = 4) -> np.ndarray:
@@ -82,7 +97,7 @@ def compare_codes(codes_gpu, scales_gpu, x16, lam, rotation, signs, G: int = O.G
     if n_el >= 1_000_000:
         assert frac < bar, f"mismatch fraction {frac:.3e} >= {bar}"
     else:
-        allowed = max(1, int(3 * bar * n_el))
+        allowed = poisson_quantile(bar * n_el)
         assert n_code_bad + n_scale_bad <= allowed, (
             f"{n_code_bad + n_scale_bad} boundary mismatches in {n_el} elements (allowed {allowed})")
     return {

@@ -87,6 +87,31 @@ def test_plan_formats(bits, G, D):
     L.kvq_plan_destroy(h)
 
 
+@pytest.mark.parametrize("D,G", [(96, 32), (96, 16), (80, 16)])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("rot", [O.SRFT, O.IDENTITY])
+def test_plan_mixed_radix_sizes(D, G, bits, rot):
+    """D = 96 and 80 take the SRFT (D/2 pair signs, the oracle's) and the
+    identity, with groups that divide D."""
+    p = K.Plan(D, G, rot, 91, bits=bits)
+    assert p.info_ex() == (D, G, bits, rot)
+    assert p.code_bytes == D * bits // 8
+    assert np.array_equal(p.signs(), O.plan_signs(D, rot, 91))
+
+
+def test_plan_mixed_radix_rejects():
+    """SRHT needs a power-of-two D; G must divide D; attention stays D=128."""
+    L = K.library()
+    h = ctypes.c_void_p()
+    assert L.kvq_plan_create(96, 32, O.SRHT, 0, ctypes.byref(h)) == UNSUPPORTED
+    assert b"SRHT" in L.kvq_last_error()
+    assert L.kvq_plan_create(80, 32, O.SRFT, 0, ctypes.byref(h)) == UNSUPPORTED
+    assert b"does not divide" in L.kvq_last_error()
+    assert L.kvq_plan_create(112, 16, O.SRFT, 0, ctypes.byref(h)) == UNSUPPORTED
+    n = ctypes.c_size_t()
+    assert L.kvq_attn_workspace_size(96, 1, 8, 100, ctypes.byref(n)) == UNSUPPORTED
+
+
 def _encode(plan, x=A, B=1, H=2, T=4, sb=1024, sh=512, st=128, lam=A, lsb=0, codes=A, scales=A,
             Tcap=8, t0=0):
     return K.library().kvq_encode(plan.handle if plan else None, x, B, H, T, sb, sh, st, lam, lsb,
