@@ -30,7 +30,8 @@
  *   - signs: bit i of the SplitMix64 stream seeded with the plan seed (bit
  *     i mod 64 of output i / 64), sign = 1 - 2 bit.
  *   - group g = output channels [32 g, 32 g + 32); scale = fp16(absmax / 7)
- *     rounded to nearest even, subnormals kept; code = clamp(rint_even(w /
+ *     (the fp32 quotient of the fp32 abs-max, rounded to nearest even to
+ *     fp16, subnormals kept); code = clamp(rint_even(w /
  *     scale), -8, 7), 0 where scale == 0; nibble = code + 8, channel 2m in
  *     the low nibble of byte m.
  *   - variants (kvq_plan_create_ex): groups of G = 16 channels ([M3] uses
@@ -92,16 +93,21 @@ const char* kvq_strerror(kvq_status s);
 /* Detail of the last failed call on this thread ("" if none). */
 const char* kvq_last_error(void);
 
-/* Create a plan: head dimension D (128 or 256), group size G (32) and the
- * rotation, with the sign vector drawn from SplitMix64(seed) [M1].  Pure host
- * work: no GPU call.  *out receives a plan the caller releases with
- * kvq_plan_destroy. */
+/* Create a plan: head dimension D, group size G (32) and the rotation, with
+ * the sign vector drawn from SplitMix64(seed) [M1].  Pure host work: no GPU
+ * call.  *out receives a plan the caller releases with kvq_plan_destroy.
+ * D = 128 or 256 take every rotation.  D = 96 and 80 (head sizes that are
+ * not powers of two, where the DFT is factored over radices 2, 3, 4 and 5;
+ * [abstract]: the SRFT is chosen because it has mixed-radix sizes) take
+ * KVQ_SRFT and KVQ_IDENTITY; KVQ_SRHT needs a power of two.  G must divide
+ * D (D = 80: G = 16).  Other values: KVQ_ERR_UNSUPPORTED. */
 kvq_status kvq_plan_create(int32_t D, int32_t G, kvq_rotation rotation, uint64_t seed,
                            kvq_plan** out);
 
 /* Create a plan with a code width and group size: bits = 4 (int4 nibbles) or
- * 8 (int8 bytes), G = 32 or 16; otherwise as kvq_plan_create, which is this
- * call with bits = 4.  KVQ_ERR_UNSUPPORTED for other widths or groups. */
+ * 8 (int8 bytes), G = 32 or 16 (dividing D); otherwise as kvq_plan_create,
+ * which is this call with bits = 4.  KVQ_ERR_UNSUPPORTED for other widths or
+ * groups. */
 kvq_status kvq_plan_create_ex(int32_t D, int32_t G, int32_t bits, kvq_rotation rotation, uint64_t seed,
                               kvq_plan** out);
 
