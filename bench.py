@@ -12,9 +12,11 @@ set (about 1.8 GB) is far beyond the 256 MB Infinity Cache.  The fp16-cache
 comparator (same attention over an unquantized cache) is timed in its own
 loop right after the timed region, and so is the D=256 leg: encode and
 decode of the Gemma-3-1B-shaped prefix (212,992 vectors) with SRFT and SRHT
-(field "d256"), and the code-format variants (field "formats": int4 in groups
+(field "d256"), the code-format variants (field "formats": int4 in groups
 of 16, int8 in groups of 32 and 16; encode and decode of the Qwen prefix and
-the decode-step attention over a cache in that format).
+the decode-step attention over a cache in that format), and the head sizes
+that are not powers of two (field "mixed_radix": encode and decode of the
+same prefix shape at D=96 and D=80 with the mixed-radix SRFT).
 
 Prints ONE JSON line.  `value` is the encode throughput (Mvec/s) over the
 timed region, measured with HIP events at the phase boundaries on the stream
@@ -275,6 +277,62 @@ def formats_leg(K, torch, stream, cfg, sets, dc, k16, v16, lam_k, lam_v, q, L, s
     return res
 
 
+MIXED = (("d96", "int4-g32", 4, 32), ("d96", "int4-g16", 4, 16), ("d80", "int4-g16", 4, 16),
+         ("d96", "int8-g32", 8, 32), ("d80", "int8-g16", 8, 16))
+
+
+def mixed_leg(K, W, torch, stream, dev, n_sets, n):
+    """Head sizes that are not powers of two (the mixed-radix SRFT): encode
+    and decode of the 28-layer prefix shape (28 layers x {K,V} x 2 KV heads x
+    4096 tokens = 458,752 vectors) at D=96 and D=80, per code format, each
+    timed over n launches with HIP events on the kernels' stream, rotating
+    over n_sets input batches."""
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    res = {"workload": "prefix shape 28 layers x {K,V} x 2 KV heads x 4096 tokens at D=96 and D=80, SRFT"}
+    for key in ("d96", "d80"):
+        cfg = W.CONFIGS[key]
+        D = cfg.D
+        sets = []
+        for i in range(n_sets):
+            c = W.Config(cfg.name, D, cfg.B, cfg.H, cfg.T, cfg.law, cfg.index + 10 * i)
+            x, lam = W.prefix_inputs(c, dev)
+            sets.append((x, lam, torch.empty_like(x)))
+        for k2, name, bits, G in MIXED:
+            if k2 != key:
+                continue
+            plan = K.Plan(D, G, "srft", cfg.sign_seed, bits=bits)
+            cb, nsc = plan.code_bytes, D // G
+            bufs = [(torch.empty((cfg.B, cfg.H, cfg.T, cb), dtype=torch.uint8, device=dev),
+                     torch.empty((cfg.B, cfg.H, cfg.T, nsc), dtype=torch.float16, device=dev))
+                    for _ in range(n_sets)]
+            enc = timed(lambda i: K.encode(plan, sets[i % n_sets][0], sets[i % n_sets][1], *bufs[i % n_sets]))
+            dec = timed(lambda i: K.decode(plan, *bufs[i % n_sets], sets[i % n_sets][1], sets[i % n_sets][2]))
+            del bufs
+            vb = 2 * D + cb + 2 * nsc                 # bytes per vector, encode or decode
+            nb = cfg.vectors * vb
+            res[f"D{D}-{name}"] = {
+                "bytes_per_call": nb,
+                "encode_us": round(enc, 2), "encode_GB_s": round(nb / enc / 1e3, 1),
+                "encode_frac_hbm": round(nb / enc / 1e3 / HBM_PEAK_GBS, 4),
+                "decode_us": round(dec, 2), "decode_GB_s": round(nb / dec / 1e3, 1),
+                "decode_frac_hbm": round(nb / dec / 1e3 / HBM_PEAK_GBS, 4),
+            }
+        del sets
+    torch.cuda.synchronize()
+    return res
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -397,6 +455,8 @@ def main():
     del g_sets
     # ---- code formats (int4 G16, int8 G32 / G16), timed apart ----
     fmts = formats_leg(K, torch, stream, cfg, sets, dc, k16, v16, lam_k, lam_v, q, L, sm, max(10, args.steps))
+    # ---- D=96 and D=80 (mixed-radix SRFT), timed apart ----
+    mixed = mixed_leg(K, W, torch, stream, dev, args.sets, max(10, args.steps))
     if args.profile_marks:
         src = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -479,6 +539,7 @@ def main():
                       "int4_over_fp16": round(attn_us / f16_us, 4)},
         "d256": gemma,
         "formats": fmts,
+        "mixed_radix": mixed,
     }
     print(json.dumps(res), flush=True)
 
