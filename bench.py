@@ -44,12 +44,12 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # the kernel sources they were taken on (sha256 prefix of the listed files);
 # reported as null once those change.
 TRAFFIC = {
-    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "d45627ff24ec99a2",
-             "bytes": (295697.2 + 4199.5) * 2 * 1024 + (8726.1 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "a44034939f932fd0",
-               "bytes": 57707.0 * 2 * 1024 + 32256.0 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "a44034939f932fd0",
-               "bytes": 16460.5 * 2 * 1024 + 114770.2 * 1024},
+    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "c29c7e311d3566ff",
+             "bytes": (295675.7 + 2119.5) * 2 * 1024 + (4366.3 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "e37aa07798ec13b5",
+               "bytes": 57715.1 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "e37aa07798ec13b5",
+               "bytes": 16454.6 * 2 * 1024 + 114764.5 * 1024},
 }
 
 

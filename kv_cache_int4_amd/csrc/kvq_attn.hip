@@ -802,9 +802,12 @@ __device__ __forceinline__ void process4(State<true>& st, const Blk4<FMT>& cur, 
   }
 }
 
-// Waves per CU the split geometry targets: the int4 kernel holds two waves
-// per SIMD (up to 256 registers), the fp16 one four.
-constexpr int kWavesPerCuInt4 = 16;
+// Waves per CU the split geometry targets.  The int4 kernel holds two waves
+// per SIMD (up to 256 registers), so eight per CU run at once: one round of
+// waves, each with a longer slice, measured faster than two rounds (fewer
+// query rotations and partials to combine).  The fp16 kernel holds four per
+// SIMD.
+constexpr int kWavesPerCuInt4 = 8;
 constexpr int kWavesPerCuF16 = 16;
 
 template <bool INT4, int ROT, int FMT>
