@@ -1062,35 +1062,60 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnArgs a, int int4) 
   const float* ml = a.part_ml + bh * a.S * 2;
   const float* acc = a.part_acc + bh * a.S * 128 + 2 * lane;
 
-  // split maxima and sums, 64 splits per pass (one per lane)
-  float m = -INFINITY;
-  for (int64_t s0 = 0; s0 < a.S; s0 += 64)
-    if (s0 + lane < a.S) m = fmaxf(m, ml[2 * (s0 + lane)]);
-  m = wave_max(m);
+  // lambda_V of the lane's channels, loaded with the partials
+  float lv0 = 1.f, lv1 = 1.f;
+  if (int4) {
+    lv0 = a.lambda_v[g * 128 + 2 * lane];
+    lv1 = a.lambda_v[g * 128 + 2 * lane + 1];
+  }
   float l = 0.f, x0 = 0.f, x1 = 0.f;
-  for (int64_t s0 = 0; s0 < a.S; s0 += 64) {
-    const int64_t sl = s0 + lane;
-    const float ms = sl < a.S ? ml[2 * sl] : -INFINITY;
-    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m);
-    if (sl < a.S) l = fmaf(w, ml[2 * sl + 1], l);
-    const int n = static_cast<int>(a.S - s0 < 64 ? a.S - s0 : 64);
-    int j = 0;
-    for (; j + 8 <= n; j += 8) {
-      float2 v[8];
+  float m = -INFINITY;
+  if (a.S <= 16) {
+    // one pass with every load issued up front: the split maxima and sums
+    // (one split per lane) and the lane's two channels of every split
+    const int S = static_cast<int>(a.S);
+    const float2 msl = lane < S ? *reinterpret_cast<const float2*>(ml + 2 * lane) : make_float2(-INFINITY, 0.f);
+    float2 v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float2*>(acc + (s0 + j + u) * 128);
+    for (int u = 0; u < 16; ++u) v[u] = u < S ? *reinterpret_cast<const float2*>(acc + u * 128) : make_float2(0.f, 0.f);
+    m = wave_max(msl.x);
+    const float w = msl.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(msl.x - m);
+    l = w * msl.y;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
-        x0 = fmaf(wu, v[u].x, x0);
-        x1 = fmaf(wu, v[u].y, x1);
-      }
+    for (int u = 0; u < 16; ++u) {
+      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+      x0 = fmaf(wu, v[u].x, x0);
+      x1 = fmaf(wu, v[u].y, x1);
     }
-    for (; j < n; ++j) {
-      const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-      const float2 v = *reinterpret_cast<const float2*>(acc + (s0 + j) * 128);
-      x0 = fmaf(wu, v.x, x0);
-      x1 = fmaf(wu, v.y, x1);
+  } else {
+    // split maxima and sums, 64 splits per pass (one per lane)
+    for (int64_t s0 = 0; s0 < a.S; s0 += 64)
+      if (s0 + lane < a.S) m = fmaxf(m, ml[2 * (s0 + lane)]);
+    m = wave_max(m);
+    for (int64_t s0 = 0; s0 < a.S; s0 += 64) {
+      const int64_t sl = s0 + lane;
+      const float ms = sl < a.S ? ml[2 * sl] : -INFINITY;
+      const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m);
+      if (sl < a.S) l = fmaf(w, ml[2 * sl + 1], l);
+      const int n = static_cast<int>(a.S - s0 < 64 ? a.S - s0 : 64);
+      int j = 0;
+      for (; j + 8 <= n; j += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float2*>(acc + (s0 + j + u) * 128);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+          x0 = fmaf(wu, v[u].x, x0);
+          x1 = fmaf(wu, v[u].y, x1);
+        }
+      }
+      for (; j < n; ++j) {
+        const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+        const float2 v = *reinterpret_cast<const float2*>(acc + (s0 + j) * 128);
+        x0 = fmaf(wu, v.x, x0);
+        x1 = fmaf(wu, v.y, x1);
+      }
     }
   }
   l = wave_sum(l);
@@ -1101,12 +1126,11 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnArgs a, int int4) 
   int k = lane;              // pair index this lane writes
   uint32_t neg0 = 0, neg1 = 0;
   if (int4) {
-    const float* lv = a.lambda_v + g * 128;
     if (ROT == KVQ_ROT_SRFT) {
       // Z_lane = (x0 + i x1) / lambda, unitary inverse 64-point DFT across
       // lanes: radix-2 decimation in frequency, output bit-reversed
-      float re = x0 * (0.125f / lv[2 * lane]);
-      float im = x1 * (0.125f / lv[2 * lane + 1]);
+      float re = x0 * (0.125f / lv0);
+      float im = x1 * (0.125f / lv1);
 #pragma unroll
       for (int hh = 32; hh >= 1; hh >>= 1) {
         const float pr = shfl_xor(re, hh), pi = shfl_xor(im, hh);
@@ -1128,8 +1152,8 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnArgs a, int int4) 
     } else if (ROT == KVQ_ROT_SRHT) {
       // H_128 on channels 2 lane + e: the stride-1 step inside the lane,
       // strides 2 .. 64 across lanes
-      float y0 = x0 * (0.0883883476483184405f / lv[2 * lane]);
-      float y1 = x1 * (0.0883883476483184405f / lv[2 * lane + 1]);
+      float y0 = x0 * (0.0883883476483184405f / lv0);
+      float y1 = x1 * (0.0883883476483184405f / lv1);
       const float t0 = y0 + y1, t1 = y0 - y1;
       y0 = t0;
       y1 = t1;
@@ -1144,8 +1168,8 @@ __global__ void __launch_bounds__(64) attn_combine_kernel(AttnArgs a, int int4) 
       neg0 = sign_bit(a.signs, 2 * lane);
       neg1 = sign_bit(a.signs, 2 * lane + 1);
     } else {
-      x0 /= lv[2 * lane];
-      x1 /= lv[2 * lane + 1];
+      x0 /= lv0;
+      x1 /= lv1;
     }
   }
   if (neg0) x0 = -x0;
