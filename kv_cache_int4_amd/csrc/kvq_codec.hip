@@ -3,9 +3,10 @@
 // Work decomposition.  A wave owns a tile of 16 KiB of fp16 input: 64 head
 // vectors of D=128 (one per lane) or 32 vectors of D=256 (a lane pair each).
 // Tiles never cross a (batch, head) row, so the lambda row is wave-uniform.
-// Waves are persistent: each walks the tiles with a stride of the grid; two
-// waves share every SIMD, so one streams its tile in while the other
-// computes.
+// The grid has one wave per tile (up to 2^30; beyond that waves walk the
+// tiles with a stride of the grid, loading the next tile while computing
+// the current one); two waves share every SIMD, so one streams its tile in
+// while the other computes.
 //
 // Hot kernels (encode128/256, decode128/256): the next tile's input goes
 // straight from HBM into LDS with direct (global -> LDS) loads while the
@@ -1389,13 +1390,14 @@ __global__ void __launch_bounds__(64, 2) decode_f32_kernel(CodecArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 
-// Persistent grid: enough waves to give every CU eight (two per SIMD), spread
-// so that every wave gets the same number of tiles.
-int64_t persistent_grid(int64_t n_tiles) {
-  const int64_t slots = static_cast<int64_t>(device_cu_count()) * 8;
-  if (n_tiles <= slots) return n_tiles;
-  const int64_t rounds = (n_tiles + slots - 1) / slots;
-  return (n_tiles + rounds - 1) / rounds;
+// One wave per tile: the dispatcher starts each wave as a slot frees up, so
+// the resident waves drift out of phase and their loads, arithmetic and
+// stores overlap better than those of a persistent grid walking the tiles
+// in lockstep (measured 5-14% faster at the prefix sizes).  Beyond 2^30
+// tiles the waves take several tiles each, with a stride of the grid.
+int64_t launch_grid(int64_t n_tiles) {
+  const int64_t cap = int64_t(1) << 30;
+  return n_tiles < cap ? n_tiles : cap;
 }
 
 template <int D>
@@ -1429,7 +1431,7 @@ hipError_t encode_dispatch(const CodecDesc& d, int mode) {
   a.w = d.w;
   if (a.n_tiles == 0) return hipSuccess;
   if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
-  const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
+  const dim3 grid(static_cast<unsigned>(launch_grid(a.n_tiles)));
   if (mode == 1) {
     // rotate only: the quantizer format plays no part
     if (D == 128) {
@@ -1454,7 +1456,7 @@ hipError_t decode_dispatch(const CodecDesc& d, bool f32) {
   a.y = d.y;
   if (a.n_tiles == 0) return hipSuccess;
   if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
-  const dim3 grid(static_cast<unsigned>(persistent_grid(a.n_tiles)));
+  const dim3 grid(static_cast<unsigned>(launch_grid(a.n_tiles)));
   if (f32) {
     hipLaunchKernelGGL((decode_f32_kernel<D, ROT, FMT>), grid, dim3(64), 0, d.stream, a);
   } else if (D == 128) {

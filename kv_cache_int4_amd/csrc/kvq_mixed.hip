@@ -10,10 +10,11 @@
 // takes G = 16 only (five groups), D = 96 takes G = 32 or 16.
 //
 // Work decomposition.  A wave owns a tile of 64 consecutive vectors of one
-// (batch, head) row, one vector per lane, and walks the tiles with a stride
-// of the grid (persistent waves, two per SIMD).  The next tile's input moves
-// from HBM straight into LDS with direct (global -> LDS) 16-byte loads while
-// the current tile computes in registers:
+// (batch, head) row, one vector per lane; the grid has one wave per tile (up
+// to 2^30, beyond which waves walk the tiles with a stride of the grid and
+// the next tile's input streams in while the current one computes).  Tile
+// input moves from HBM straight into LDS with direct (global -> LDS) 16-byte
+// loads and is computed in registers:
 //   encode: the fp16 rows (D / 8 chunks of 16 bytes each) land in a
 //           row-major LDS tile whose chunks are XOR-swizzled per row, so that
 //           each lane's read of its own row is free of bank conflicts; the
@@ -532,11 +533,11 @@ __global__ void __launch_bounds__(64, 2) mix_decode_kernel(MixArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// One wave per tile (up to 2^30 waves; beyond that they walk the tiles with
+// a stride of the grid), as for D = 128 and 256.
 int64_t mix_grid(int64_t n_tiles) {
-  const int64_t slots = static_cast<int64_t>(device_cu_count()) * 8;
-  if (n_tiles <= slots) return n_tiles;
-  const int64_t rounds = (n_tiles + slots - 1) / slots;
-  return (n_tiles + rounds - 1) / rounds;
+  const int64_t cap = int64_t(1) << 30;
+  return n_tiles < cap ? n_tiles : cap;
 }
 
 void fill_mix(MixArgs& a, const CodecDesc& d) {
