@@ -44,12 +44,12 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # the kernel sources they were taken on (sha256 prefix of the listed files);
 # reported as null once those change.
 TRAFFIC = {
-    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "c29c7e311d3566ff",
-             "bytes": (295675.7 + 2119.5) * 2 * 1024 + (4366.3 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "e37aa07798ec13b5",
-               "bytes": 57715.1 * 2 * 1024 + 32256.0 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "e37aa07798ec13b5",
-               "bytes": 16454.6 * 2 * 1024 + 114764.5 * 1024},
+    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "7c4b299e05516274",
+             "bytes": (295676.0 + 2138.5) * 2 * 1024 + (4368.1 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d10e6c8c7a7b4442",
+               "bytes": 57713.9 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d10e6c8c7a7b4442",
+               "bytes": 16454.2 * 2 * 1024 + 114780.8 * 1024},
 }
 
 
