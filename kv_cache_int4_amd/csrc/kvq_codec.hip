@@ -3,10 +3,10 @@
 // Work decomposition.  A wave owns a tile of 16 KiB of fp16 input: 64 head
 // vectors of D=128 (one per lane) or 32 vectors of D=256 (a lane pair each).
 // Tiles never cross a (batch, head) row, so the lambda row is wave-uniform.
-// The grid has one wave per tile (up to 2^30; beyond that waves walk the
-// tiles with a stride of the grid, loading the next tile while computing
-// the current one); two waves share every SIMD, so one streams its tile in
-// while the other computes.
+// The grid has one wave per tile, up to 32 waves per CU; larger calls have
+// the waves walk the tiles with a stride of the grid, loading the next tile
+// while computing the current one.  Two waves share every SIMD, so one
+// streams its tile in while the other computes.
 //
 // Hot kernels (encode128/256, decode128/256): the next tile's input goes
 // straight from HBM into LDS with direct (global -> LDS) loads while the
@@ -1393,10 +1393,11 @@ namespace {
 // One wave per tile: the dispatcher starts each wave as a slot frees up, so
 // the resident waves drift out of phase and their loads, arithmetic and
 // stores overlap better than those of a persistent grid walking the tiles
-// in lockstep (measured 5-14% faster at the prefix sizes).  Beyond 2^30
-// tiles the waves take several tiles each, with a stride of the grid.
+// in lockstep (measured 5-14% faster at the prefix sizes).  Past 32 waves
+// per CU (four times what fits at once) the waves take several tiles each,
+// with a stride of the grid, loading the next tile while computing one.
 int64_t launch_grid(int64_t n_tiles) {
-  const int64_t cap = int64_t(1) << 30;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 32;
   return n_tiles < cap ? n_tiles : cap;
 }
 

@@ -10,9 +10,10 @@
 // takes G = 16 only (five groups), D = 96 takes G = 32 or 16.
 //
 // Work decomposition.  A wave owns a tile of 64 consecutive vectors of one
-// (batch, head) row, one vector per lane; the grid has one wave per tile (up
-// to 2^30, beyond which waves walk the tiles with a stride of the grid and
-// the next tile's input streams in while the current one computes).  Tile
+// (batch, head) row, one vector per lane; the grid has one wave per tile up
+// to 32 waves per CU (larger calls have the waves walk the tiles with a
+// stride of the grid, the next tile's input streaming in while the current
+// one computes).  Tile
 // input moves from HBM straight into LDS with direct (global -> LDS) 16-byte
 // loads and is computed in registers:
 //   encode: the fp16 rows (D / 8 chunks of 16 bytes each) land in a
@@ -533,10 +534,10 @@ __global__ void __launch_bounds__(64, 2) mix_decode_kernel(MixArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-// One wave per tile (up to 2^30 waves; beyond that they walk the tiles with
-// a stride of the grid), as for D = 128 and 256.
+// One wave per tile up to 32 waves per CU; larger calls have the waves walk
+// the tiles with a stride of the grid, as for D = 128 and 256.
 int64_t mix_grid(int64_t n_tiles) {
-  const int64_t cap = int64_t(1) << 30;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 32;
   return n_tiles < cap ? n_tiles : cap;
 }
 

@@ -157,3 +157,33 @@ def test_mixed_rejections_and_empty():
     K.encode(plan, x, lam, codes, scales, 2)
     torch.cuda.synchronize()
     assert bool((codes == 0x5A).all()) and bool((scales == 1234.0).all())
+
+
+@pytest.mark.parametrize("D,G", [(96, 32), (80, 16)])
+def test_mixed_multi_tile_waves_sampled(D, G):
+    """A call with more tiles than the grid holds (B=4, H=8, T=20000: 10,016
+    tiles, over 32 waves per CU), so waves take several tiles and stream the
+    next one in while computing: 16384 seeded sample vectors checked against
+    the oracle, encode and fp16 decode."""
+    B, H, T = 4, 8, 20000
+    g = W.gen("cuda", 77, D, T)
+    std = torch.exp(0.5 * torch.randn((H, D), generator=g, device="cuda"))
+    x = (torch.randn((B, H, T, D), generator=g, device="cuda") * std[None, :, None, :]).to(torch.float16)
+    lam = torch.exp(0.3 * torch.randn((B, H, D), generator=g, device="cuda"))
+    plan = K.Plan(D, G, "srft", 4242)
+    codes = torch.empty((B, H, T, plan.code_bytes), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((B, H, T, D // G), dtype=torch.float16, device="cuda")
+    K.encode(plan, x, lam, codes, scales)
+    y = torch.empty_like(x)
+    K.decode(plan, codes, scales, lam, y)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(np.random.default_rng(5).choice(B * H * T, 16384, replace=False)).cuda()
+    xs = x.reshape(-1, D)[idx].cpu().numpy()
+    cs = codes.reshape(-1, plan.code_bytes)[idx].cpu().numpy()
+    ss = scales.reshape(-1, D // G)[idx].cpu().numpy()
+    ys = y.reshape(-1, D)[idx].cpu().numpy()
+    lv = lam.reshape(B * H, D)[(idx // T)].cpu().numpy()
+    signs = O.plan_signs(D, O.SRFT, plan.seed)
+    rep = P.compare_codes(cs, ss, xs, lv, O.SRFT, signs, G)
+    say(f"   D={D} sampled codes: {rep['code_mismatch']} / {rep['scale_mismatch']} mismatches")
+    P.compare_decode(ys, cs, ss, lv, O.SRFT, signs, G)

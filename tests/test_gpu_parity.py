@@ -256,6 +256,35 @@ def test_mistral_bulk_sampled():
         P.compare_decode(ys, cs, ss, lv, O.SRFT, signs)
 
 
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+def test_d256_multi_tile_waves_sampled(rot):
+    """D=256 with more tiles than the grid holds (B=2, H=8, T=20000: 10,000
+    tiles of 32 vectors, over 32 waves per CU), so waves take several tiles:
+    16384 seeded sample vectors checked, encode and fp16 decode."""
+    B, H, T, D = 2, 8, 20000, 256
+    g = W.gen("cuda", 78, D, T)
+    std = torch.exp(0.5 * torch.randn((H, D), generator=g, device="cuda"))
+    x = (torch.randn((B, H, T, D), generator=g, device="cuda") * std[None, :, None, :]).to(torch.float16)
+    lam = torch.exp(0.3 * torch.randn((H, D), generator=g, device="cuda"))
+    plan = K.Plan(D, 32, rot, 4343)
+    codes = torch.empty((B, H, T, D // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((B, H, T, D // 32), dtype=torch.float16, device="cuda")
+    K.encode(plan, x, lam, codes, scales)
+    y = torch.empty_like(x)
+    K.decode(plan, codes, scales, lam, y)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(np.random.default_rng(6).choice(B * H * T, 16384, replace=False)).cuda()
+    xs = x.reshape(-1, D)[idx].cpu().numpy()
+    cs = codes.reshape(-1, D // 2)[idx].cpu().numpy()
+    ss = scales.reshape(-1, D // 32)[idx].cpu().numpy()
+    ys = y.reshape(-1, D)[idx].cpu().numpy()
+    lv = lam.cpu().numpy()[((idx // T) % H).cpu().numpy()]
+    signs = O.plan_signs(D, ROTS[rot], plan.seed)
+    rep = P.compare_codes(cs, ss, xs, lv, ROTS[rot], signs)
+    say(f"   D=256 {rot} sampled codes: {rep['code_mismatch']} / {rep['scale_mismatch']} mismatches")
+    P.compare_decode(ys, cs, ss, lv, ROTS[rot], signs)
+
+
 # -------------------------------------------------------------- attention --
 
 def build_cache(plan, B, Hkv, Hq, T, Tcap, D, seed):
