@@ -612,19 +612,41 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
 // on the odd lane is the negated value; the sign is folded into that lane's
 // half of the lambda table.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void dma_tile256(const CodecArgs& a, const Tile& t, lds_u8* lds, int lane,
-                                            const uint32_t (&off4)[4]) {
+// Chunk swizzle of row r of a D=256 tile.  The SRFT lanes read one row per
+// lane pair (rows 2v + R of every v at once): the swizzle by bits 1-4 of the
+// row spreads those 32 rows over all 16 chunk columns, so each half-wave's
+// dword reads hit distinct banks.  The SRHT and unrotated lanes read
+// consecutive rows, which the swizzle by bits 0-3 spreads.
+template <int ROT>
+__device__ __forceinline__ int swz256(int r) {
+  return ROT == KVQ_ROT_SRFT ? (r >> 1) & 15 : r & 15;
+}
+
+// Slot i * 64 + lane of the LDS tile receives row r = 4 i + lane / 16
+// (vector r / 2, half r % 2), chunk (lane % 16) ^ swz256(r).  The lane's
+// source offsets repeat every eight loads; they are recomputed per call from
+// a laundered lane index (held across the transform they would spill).
+template <int ROT>
+__device__ __forceinline__ void dma_tile256(const CodecArgs& a, const Tile& t, lds_u8* lds, int lane) {
+  asm volatile("" : "+v"(lane));
+  uint32_t off8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    off8[i] = static_cast<uint32_t>((lane >> 5) * 2 * a.st + ((lane >> 4) & 1) * 256 +
+                                    16 * ((lane & 15) ^ swz256<ROT>(r)));
+  }
   const char* base = reinterpret_cast<const char*>(a.x + t.b * a.sb + t.h * a.sh + t.t_start * a.st);
   const int64_t step = 4 * a.st;        // bytes of two vectors (four rows)
   if (t.nv == 32) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      __builtin_amdgcn_global_load_lds(base + i * step + off4[i & 3], lds + 1024 * i, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(base + i * step + off8[i & 7], lds + 1024 * i, 16, 0, 0);
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (2 * i + (lane >> 5) < t.nv)
-        __builtin_amdgcn_global_load_lds(base + i * step + off4[i & 3], lds + 1024 * i, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(base + i * step + off8[i & 7], lds + 1024 * i, 16, 0, 0);
   }
 }
 
@@ -661,18 +683,12 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
 
   mask_lds[lane] = pair_mask256<ROT>(a, 0, lane);
   mask_lds[64 + lane] = pair_mask256<ROT>(a, 1, lane);
-  uint32_t off4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * i + (lane >> 4);      // row of the tile: vector r / 2, half r % 2
-    off4[i] = static_cast<uint32_t>((lane >> 5) * 2 * a.st + ((lane >> 4) & 1) * 256 + 16 * ((lane & 15) ^ (r & 15)));
-  }
   // lambda of a tile: lane l holds channels l, l + 64, l + 128, l + 192
   float lam_r[4] = {0.f, 0.f, 0.f, 0.f};
   int64_t tile = blockIdx.x;
   if (tile < a.n_tiles) {
     const Tile t = tile_info<256>(a, tile);
-    dma_tile256(a, t, (lds_u8*)lds, lane, off4);
+    dma_tile256<ROT>(a, t, (lds_u8*)lds, lane);
     const float* lr = a.lambda + t.b * a.lambda_sb + t.h * 256;
 #pragma unroll
     for (int q = 0; q < 4; ++q) lam_r[q] = lr[lane + 64 * q];
@@ -699,7 +715,8 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
       for (int R = 0; R < 2; ++R) {
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-          const uint32_t w0 = (blk_off(v2 + R, c) >> 2) + hh;
+          const int r = v2 + R;
+          const uint32_t w0 = ((r * 256 + ((c ^ swz256<ROT>(r)) << 4)) >> 2) + hh;
           p[32 * R + 2 * c] = reinterpret_cast<const uint32_t*>(lds)[w0];
           p[32 * R + 2 * c + 1] = reinterpret_cast<const uint32_t*>(lds)[w0 + 2];
         }
@@ -721,7 +738,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     const int64_t nxt = tile + gridDim.x;
     if (nxt < a.n_tiles) {
       const Tile tn = tile_info<256>(a, nxt);
-      dma_tile256(a, tn, (lds_u8*)lds, lane, off4);
+      dma_tile256<ROT>(a, tn, (lds_u8*)lds, lane);
       const float* lr = a.lambda + tn.b * a.lambda_sb + tn.h * 256;
 #pragma unroll
       for (int q = 0; q < 4; ++q) lam_r[q] = lr[lane + 64 * q];
