@@ -45,11 +45,11 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # reported as null once those change.
 TRAFFIC = {
     "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "7c4b299e05516274",
-             "bytes": (295676.0 + 2138.5) * 2 * 1024 + (4368.1 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d10e6c8c7a7b4442",
-               "bytes": 57713.9 * 2 * 1024 + 32256.0 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d10e6c8c7a7b4442",
-               "bytes": 16454.2 * 2 * 1024 + 114780.8 * 1024},
+             "bytes": (295678.2 + 2138.5) * 2 * 1024 + (4367.8 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "5c25c373ce2740c9",
+               "bytes": 57708.2 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "5c25c373ce2740c9",
+               "bytes": 16461.4 * 2 * 1024 + 114756.9 * 1024},
 }
 
 

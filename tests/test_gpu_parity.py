@@ -417,3 +417,64 @@ def test_attention_decode_step_full_size():
         ref16 = O.attention_f16(qs, k16[sl, g:g + 1].cpu().numpy(), v16[sl, g:g + 1].cpu().numpy(), L, sm)
         w2 = P.compare_attention(np16(out16[sl, g * rep:(g + 1) * rep]).astype(np.float64), ref16)
         say(f"   (b={b}, g={g}): int4 rel {w1:.2e}, fp16 rel {w2:.2e}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,L", [(4, 1, 9000), (6, 1, 5000), (2, 2, 4500)])
+def test_attention_many_splits(Hq, Hkv, L):
+    """Batch 1 with one or two kv heads: few (batch, kv head, head chunk)
+    units, so each is cut into more than 16 splits (the general merge path);
+    Hq = 6 leaves a second chunk of two heads.  int4 (SRFT) and the fp16
+    comparator against the oracle."""
+    D, B = 128, 1
+    Tcap = L + 3
+    plan = K.Plan(D, 32, "srft", 71)
+    say(f"[attn-splits] Hq={Hq} Hkv={Hkv} L={L}")
+    k16, v16, lam_k, lam_v, q, kc, ksc, vc, vsc = build_cache(plan, B, Hkv, Hq, L, Tcap, D, 29)
+    sm = 1 / math.sqrt(D)
+    signs = O.plan_signs(D, O.SRFT, plan.seed)
+    ref = O.attention_int4(np16(q), kc.cpu().numpy(), ksc.cpu().numpy(), lam_k.cpu().numpy(),
+                           vc.cpu().numpy(), vsc.cpu().numpy(), lam_v.cpu().numpy(), L, sm, O.SRFT, signs)
+    out = run_attn(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, torch.float32)
+    say(f"   int4: rel err {P.compare_attention(np16(out), ref):.2e}")
+    ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device="cuda")
+    out16 = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    K.attn_decode_f16(q, k16, v16, L, sm, out16, ws)
+    torch.cuda.synchronize()
+    ref16 = O.attention_f16(np16(q), k16.cpu().numpy(), v16.cpu().numpy(), L, sm)
+    say(f"   fp16 comparator: rel err {P.compare_attention(np16(out16), ref16):.2e}")
+
+
+def test_attention_workspace_reuse():
+    """One workspace, sized for the largest call, serves a run of calls of
+    different shapes, split counts and caches in stream order; repeating a
+    call reproduces its output bit for bit (the merge takes the splits in a
+    fixed order)."""
+    D = 128
+    plan = K.Plan(D, 32, "srft", 5)
+    sm = 1 / math.sqrt(D)
+    shapes = [(8, 8, 2, 3000), (1, 4, 1, 9000), (2, 2, 1, 40), (8, 8, 2, 3000)]
+    ws = torch.empty(K.attn_workspace_size(D, 8, 8, 9000), dtype=torch.uint8, device="cuda")
+    caches = {}
+    first = {}
+    for i, (B, Hq, Hkv, L) in enumerate(shapes):
+        say(f"[attn-reuse] call {i}: B={B} Hq={Hq} Hkv={Hkv} L={L}")
+        key = (B, Hq, Hkv, L)
+        if key not in caches:
+            caches[key] = build_cache(plan, B, Hkv, Hq, L, L + 1, D, 40 + i)
+        k16, v16, lam_k, lam_v, q, kc, ksc, vc, vsc = caches[key]
+        for rep in range(2):
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+            K.attn_decode(plan, q, kc, ksc, lam_k, vc, vsc, lam_v, L, sm, out, ws)
+            out16 = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+            K.attn_decode_f16(q, k16, v16, L, sm, out16, ws)
+            torch.cuda.synchronize()
+            if key in first:
+                assert torch.equal(out, first[key][0]) and torch.equal(out16, first[key][1])
+            else:
+                first[key] = (out, out16)
+        if i == 1:
+            signs = O.plan_signs(D, O.SRFT, plan.seed)
+            ref = O.attention_int4(np16(q), kc.cpu().numpy(), ksc.cpu().numpy(), lam_k.cpu().numpy(),
+                                   vc.cpu().numpy(), vsc.cpu().numpy(), lam_v.cpu().numpy(), L, sm, O.SRFT,
+                                   signs)
+            say(f"   int4: rel err {P.compare_attention(np16(first[key][0]), ref):.2e}")
