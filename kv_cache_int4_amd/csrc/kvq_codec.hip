@@ -194,16 +194,14 @@ __device__ __forceinline__ void forward_rotation(float (&v)[128], int lane) {
         for (int m = 0; m < 64; ++m) twiddle<128, false>(v[2 * rev4(m)], v[2 * rev4(m) + 1], m);
       }
       const float sg = (lane & 1) ? 1.f : -1.f;
-#pragma unroll
-      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sg);
+      pair_fma_all(v, sg);
     }
   } else if (ROT == KVQ_ROT_SRHT) {
     wht128(v);
     if (D == 256) {
       // H_256 [u; v] = [H u + H v; H u - H v]; the second lane holds -H v.
       const float sg = (lane & 1) ? 1.f : -1.f;
-#pragma unroll
-      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sg);
+      pair_fma_all(v, sg);
     }
   }
 }
@@ -752,8 +750,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
 #pragma unroll
         for (int m = 1; m < 64; ++m) twiddle<128, false>(v[2 * rev4(m)], v[2 * rev4(m) + 1], m);
       }
-#pragma unroll
-      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+      pair_fma_all(v, sgn);
     } else {
 #pragma unroll
       for (int k = 0; k < 64; ++k) {
@@ -761,8 +758,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
         v[2 * k + 1] = f16_bits_to_f32(p[k] >> 16);
       }
       if (kPair) {
-#pragma unroll
-        for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+        pair_fma_all(v, sgn);
       }
       if (ROT == KVQ_ROT_SRHT) wht128(v);
     }
@@ -1250,11 +1246,9 @@ __global__ void __launch_bounds__(64, 2) decode256_kernel(CodecArgs a) {
 #pragma unroll
         for (int k = 1; k < 64; ++k) twiddle<128, true>(v[2 * rev4(k)], v[2 * rev4(k) + 1], k);
       }
-#pragma unroll
-      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+      pair_fma_all(v, sgn);
     } else if (ROT == KVQ_ROT_SRHT) {
-#pragma unroll
-      for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+      pair_fma_all(v, sgn);
       wht128(v);
     }
     // the next tile's direct loads have had the transform to land
@@ -1362,8 +1356,7 @@ __global__ void __launch_bounds__(64, 2) decode_f32_kernel(CodecArgs a) {
       if (D == 256) {
         // lane 2v: A_m = Z_m + Z_{m+64}; lane 2v+1: -(Z_m - Z_{m+64}) W^-m
         const float sgn = (lane & 1) ? -1.f : 1.f;
-#pragma unroll
-        for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+        pair_fma_all(v, sgn);
         if (lane & 1) {
 #pragma unroll
           for (int m = 0; m < 64; ++m) twiddle<128, true>(v[2 * m], v[2 * m + 1], m);
@@ -1373,8 +1366,7 @@ __global__ void __launch_bounds__(64, 2) decode_f32_kernel(CodecArgs a) {
     } else if (ROT == KVQ_ROT_SRHT) {
       if (D == 256) {
         const float sgn = (lane & 1) ? -1.f : 1.f;
-#pragma unroll
-        for (int i = 0; i < 128; ++i) v[i] = pair_fma(v[i], sgn);
+        pair_fma_all(v, sgn);
       }
       wht128(v);
     }

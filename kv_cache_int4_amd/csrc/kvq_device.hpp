@@ -179,6 +179,33 @@ __device__ __forceinline__ float pair_fma(float own, float sign) {
   return fmaf(other, sign, own);
 }
 
+// The same step on eight registers, the partner read fused into the FMA as
+// its DPP operand (v_fmac_f32_dpp: v += sign * v[l ^ 1]), which the
+// compiler does not form by itself when the DPP source is the accumulator.
+// A DPP read of a register a VALU wrote in the two instructions before
+// needs two wait states: the s_nop covers the instructions ahead of the
+// block; inside it every instruction reads a register no earlier one of
+// the block writes.  Same single rounding as fmaf.
+__device__ __forceinline__ void pair_fma8(float* v, float sign) {
+  asm("s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+      : "v"(sign));
+}
+
+// pair_fma on all 128 registers of a lane's half vector.
+__device__ __forceinline__ void pair_fma_all(float (&v)[128], float sign) {
+#pragma unroll
+  for (int i = 0; i < 128; i += 8) pair_fma8(v + i, sign);
+}
+
 // Streaming 16-byte global load / store (touched once: nontemporal hint).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
