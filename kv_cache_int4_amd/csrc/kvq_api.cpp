@@ -74,6 +74,15 @@ bool product_ok(int64_t a, int64_t b, int64_t c, int64_t d) {
   return v <= (static_cast<__int128>(1) << 62);
 }
 
+// The largest element offset a strided [B, H, T, D] view reaches,
+// (B-1) sb + (H-1) sh + (T-1) st + D - 1, within [0, 2^62] (non-empty view,
+// non-negative strides).
+bool extent_ok(int64_t B, int64_t H, int64_t T, int64_t sb, int64_t sh, int64_t st, int64_t D) {
+  const __int128 e = static_cast<__int128>(B - 1) * sb + static_cast<__int128>(H - 1) * sh +
+                     static_cast<__int128>(T - 1) * st + (D - 1);
+  return e <= (static_cast<__int128>(1) << 62);
+}
+
 kvq_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -106,6 +115,7 @@ kvq_status check_x(const kvq_plan* p, const uint16_t* x, int64_t B, int64_t H, i
   if (sb % 8 || sh % 8 || st % 8)
     return fail(KVQ_ERR_ALIGN, "x strides must be multiples of 8 elements (16-byte rows)");
   if (!product_ok(B, H, T, p->D)) return fail(KVQ_ERR_INVALID, "shape too large");
+  if (!extent_ok(B, H, T, sb, sh, st, p->D)) return fail(KVQ_ERR_INVALID, "x strides reach too far");
   return KVQ_OK;
 }
 
@@ -174,8 +184,8 @@ kvq_status kvq_plan_create_ex(int32_t D, int32_t G, int32_t bits, kvq_rotation r
     uint64_t state = seed;
     for (int32_t w = 0; w * 64 < n; ++w) {
       const uint64_t word = splitmix64_next(state);
-      const int32_t bits = n - w * 64 < 64 ? n - w * 64 : 64;
-      p->sign_bits[w] = bits == 64 ? word : (word & ((1ull << bits) - 1));
+      const int32_t nb = n - w * 64 < 64 ? n - w * 64 : 64;   // signs held by this word
+      p->sign_bits[w] = nb == 64 ? word : (word & ((1ull << nb) - 1));
     }
     *out = p;
     return ok();
@@ -296,6 +306,7 @@ kvq_status kvq_decode(const kvq_plan* plan, const uint8_t* codes, const uint16_t
         return fail(KVQ_ERR_ALIGN, "fp32 y strides must be even");
     }
     if (!product_ok(B, H, Tcap, plan->D)) return fail(KVQ_ERR_INVALID, "shape too large");
+    if (!extent_ok(B, H, T, y_sb, y_sh, y_st, plan->D)) return fail(KVQ_ERR_INVALID, "y strides reach too far");
     kvq::CodecDesc d{};
     fill_signs(plan, d);
     d.codes_in = codes;

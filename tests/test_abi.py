@@ -135,6 +135,8 @@ def test_encode_validation():
     assert _encode(p, lam=A + 1) == ALIGN
     assert _encode(p, lsb=-1) == INVALID
     assert _encode(p, B=1 << 40, H=1 << 20) == INVALID  # overflowing shape
+    assert _encode(p, B=2, sb=1 << 62) == INVALID        # strides reaching past 2^62 elements
+    assert b"reach" in K.library().kvq_last_error()
     # zero work is a no-op that touches nothing (NULL pointers allowed)
     assert _encode(p, T=0, x=None, lam=None, codes=None, scales=None) == OK
     assert K.library().kvq_last_error() == b""
@@ -152,6 +154,7 @@ def test_decode_and_rotate_validation():
     assert L.kvq_decode(h, A, A, 1, 1, 8, 0, 4, A, 0, A, 1, 2048, 2048, 257, None) == ALIGN
     assert L.kvq_decode(h, None, A, 1, 1, 8, 0, 4, A, 0, A, 0, 2048, 2048, 256, None) == INVALID
     assert L.kvq_decode(h, A, A, 1, 1, 8, 0, 0, A, 0, A, 0, 2048, 2048, 256, None) == OK
+    assert L.kvq_decode(h, A, A, 2, 1, 8, 0, 4, A, 0, A, 0, 1 << 62, 2048, 256, None) == INVALID
     assert L.kvq_rotate(h, A, 1, 1, 4, 1024, 1024, 256, A, 0, None, None) == INVALID
     assert L.kvq_rotate(h, A, 1, 1, 4, 1024, 1024, 256, A, 0, A + 4, None) == ALIGN
     assert L.kvq_rotate(None, A, 1, 1, 4, 1024, 1024, 256, A, 0, A, None) == INVALID
