@@ -44,12 +44,12 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # the kernel sources they were taken on (sha256 prefix of the listed files);
 # reported as null once those change.
 TRAFFIC = {
-    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "7c4b299e05516274",
-             "bytes": (295678.2 + 2138.5) * 2 * 1024 + (4367.8 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "5c25c373ce2740c9",
-               "bytes": 57708.2 * 2 * 1024 + 32256.0 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "5c25c373ce2740c9",
-               "bytes": 16461.4 * 2 * 1024 + 114756.9 * 1024},
+    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "5ea32b42bb6f5df8",
+             "bytes": (295675.9 + 2138.5) * 2 * 1024 + (4364.1 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d7ae9b3f18317702",
+               "bytes": 57710.4 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d7ae9b3f18317702",
+               "bytes": 16460.2 * 2 * 1024 + 114741.7 * 1024},
 }
 
 
