@@ -99,12 +99,15 @@ def trace_summary(path: str) -> str:
         return "(empty)"
     key = "Dispatch_Id" if "Dispatch_Id" in rows[0] else "Correlation_Id"
     rows.sort(key=lambda r: int(r[key]))
-    marks = [i for i, r in enumerate(rows) if "sleep" in r["Kernel_Name"] or "spin" in r["Kernel_Name"]]
+    # a counter collection has a row per (dispatch, counter[, partial]): the
+    # window is taken by dispatch id, strictly between the first and the
+    # last marker dispatch
+    marks = sorted({int(r[key]) for r in rows if "sleep" in r["Kernel_Name"] or "spin" in r["Kernel_Name"]})
     if len(marks) < 2:
         raise SystemExit(f"{path}: fewer than two marker dispatches")
     lo, hi = marks[0], marks[-1]
     gk = "Grid_Size" if "Grid_Size" in rows[0] else "Grid_Size_X"
-    window = rows[lo + 1:hi]
+    window = [r for r in rows if lo < int(r[key]) < hi]
     # the calibration copy is the last kernel before the closing marker
     calib_id = max(int(r[key]) for r in window)
 
