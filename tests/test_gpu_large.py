@@ -1,7 +1,8 @@
 """GPU parity at sizes whose byte offsets pass 2^31 (and, for the codec
 input, 2^32): the codec on one head of 33.6M D=128 vectors (8.6 GB of fp16
-rows, 2.1 GB of codes) and the decode-step attention over a 33.6M-token int4
-cache.  Every address past the 32-bit range is exercised.
+rows, 2.1 GB of codes), of 16.8M D=256 vectors and of 33.6M D=96 vectors,
+and the decode-step attention over a 33.6M-token int4 cache.  Every address
+past the 32-bit range is exercised.
 
 The codec is checked on sampled vectors on both sides of those offsets and
 at the end, against the oracle (codes, scales and the fp16 decode).  The
@@ -48,37 +49,42 @@ def fill_normal(t, std, seed):
         flat[i:j] = (torch.randn((j - i, t.shape[-1]), generator=g, device="cuda") * std).to(t.dtype)
 
 
-def test_codec_past_32bit_offsets_sampled():
-    T = T_BIG
-    say(f"[large] codec: 1 x 1 x {T} x {D}")
+@pytest.mark.parametrize("Dc,G,T", [(128, 32, T_BIG), (256, 32, (1 << 24) + 100), (96, 16, T_BIG)])
+def test_codec_past_32bit_offsets_sampled(Dc, G, T):
+    """SRFT encode and fp16 decode of one head of T vectors of size Dc: the
+    input passes 2^32 bytes, the codes 2^31 (D=128, 256) or 2^30 (D=96)."""
+    say(f"[large] codec: 1 x 1 x {T} x {Dc}, G={G}")
     g = torch.Generator(device="cuda").manual_seed(3)
-    std = torch.exp(0.5 * torch.randn(D, generator=g, device="cuda"))
-    lam = torch.exp(0.3 * torch.randn((1, D), generator=g, device="cuda"))
-    x = torch.empty((1, 1, T, D), dtype=torch.float16, device="cuda")
+    std = torch.exp(0.5 * torch.randn(Dc, generator=g, device="cuda"))
+    lam = torch.exp(0.3 * torch.randn((1, Dc), generator=g, device="cuda"))
+    x = torch.empty((1, 1, T, Dc), dtype=torch.float16, device="cuda")
     fill_normal(x, std, 11)
-    plan = K.Plan(D, 32, "srft", 99)
-    codes = torch.empty((1, 1, T, D // 2), dtype=torch.uint8, device="cuda")
-    scales = torch.empty((1, 1, T, D // 32), dtype=torch.float16, device="cuda")
+    plan = K.Plan(Dc, G, "srft", 99)
+    codes = torch.empty((1, 1, T, Dc // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((1, 1, T, Dc // G), dtype=torch.float16, device="cuda")
     K.encode(plan, x, lam, codes, scales)
     y = torch.empty_like(x)
     K.decode(plan, codes, scales, lam, y)
     torch.cuda.synchronize()
     say("[large] codec: encoded and decoded; sampling")
     rng = np.random.default_rng(17)
-    # 2^23 vectors = 2^31 bytes of input, 2^24 = 2^32 bytes of input and
-    # 2^30 of codes, 2^25 = 2^31 bytes of codes
-    near = [np.arange(c - 64, c + 64) for c in (1 << 23, 1 << 24, 1 << 25)]
+    # vectors where the input passes 2^31 and 2^32 bytes and the codes 2^30
+    # and 2^31 bytes
+    marks = [c for c in ((1 << 31) // (2 * Dc), (1 << 32) // (2 * Dc), (1 << 30) // (Dc // 2),
+                         (1 << 31) // (Dc // 2)) if c + 64 <= T]
+    near = [np.arange(c - 64, c + 64) for c in marks]
     idx = np.unique(np.concatenate(near + [np.arange(T - 256, T), rng.choice(T, 4096, replace=False)]))
     it = torch.from_numpy(idx).cuda()
-    xs = np16(x.view(-1, D)[it])
-    cs = np16(codes.view(-1, D // 2)[it])
-    ss = np16(scales.view(-1, D // 32)[it])
-    ys = np16(y.view(-1, D)[it])
-    lv = np.broadcast_to(np16(lam).astype(np.float32), (len(idx), D))
-    signs = O.plan_signs(D, O.SRFT, plan.seed)
-    rep = P.compare_codes(cs, ss, xs, lv, O.SRFT, signs)
-    say(f"   {len(idx)} sampled vectors: {rep['code_mismatch']} code / {rep['scale_mismatch']} scale mismatches")
-    r = P.compare_decode(ys, cs, ss, lv, O.SRFT, signs)
+    xs = np16(x.view(-1, Dc)[it])
+    cs = np16(codes.view(-1, Dc // 2)[it])
+    ss = np16(scales.view(-1, Dc // G)[it])
+    ys = np16(y.view(-1, Dc)[it])
+    lv = np.broadcast_to(np16(lam).astype(np.float32), (len(idx), Dc))
+    signs = O.plan_signs(Dc, O.SRFT, plan.seed)
+    rep = P.compare_codes(cs, ss, xs, lv, O.SRFT, signs, G)
+    say(f"   {len(idx)} sampled vectors ({len(marks)} offset marks): {rep['code_mismatch']} code / "
+        f"{rep['scale_mismatch']} scale mismatches")
+    r = P.compare_decode(ys, cs, ss, lv, O.SRFT, signs, G)
     say(f"   fp16 decode: {r}")
 
 
