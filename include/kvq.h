@@ -44,7 +44,9 @@
  * entry point allocates, frees or synchronizes; kernels are enqueued on the
  * caller's stream (a hipStream_t passed as void*, NULL = the default stream)
  * and device faults surface at the caller's next synchronization.  fp16 values
- * are passed as uint16_t bit patterns.  Strides are in elements.
+ * are passed as uint16_t bit patterns.  Strides are in elements, non-negative,
+ * and every element a call reaches must lie within 2^62 elements of its base
+ * pointer (KVQ_ERR_INVALID otherwise); byte offsets past 2^32 are supported.
  *
  * Errors: every argument check runs on the host before anything is enqueued;
  * a failing call has no side effects and returns a kvq_status other than
