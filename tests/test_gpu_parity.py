@@ -258,10 +258,11 @@ def test_mistral_bulk_sampled():
 
 @pytest.mark.parametrize("rot", ["srft", "srht"])
 def test_d256_multi_tile_waves_sampled(rot):
-    """D=256 with more tiles than the grid holds (B=2, H=8, T=20000: 10,000
-    tiles of 32 vectors, over 32 waves per CU), so waves take several tiles:
-    16384 seeded sample vectors checked, encode and fp16 decode."""
-    B, H, T, D = 2, 8, 20000, 256
+    """D=256 with more tiles than the grid holds (B=2, H=8, T=40000: 20,000
+    tiles of 32 vectors: more than 64 waves per CU, past which the encoder's
+    grid, like the decoder's, stops at 32 per CU), so waves take several
+    tiles: 16384 seeded sample vectors checked, encode and fp16 decode."""
+    B, H, T, D = 2, 8, 40000, 256
     g = W.gen("cuda", 78, D, T)
     std = torch.exp(0.5 * torch.randn((H, D), generator=g, device="cuda"))
     x = (torch.randn((B, H, T, D), generator=g, device="cuda") * std[None, :, None, :]).to(torch.float16)
