@@ -45,11 +45,11 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # reported as null once those change.
 TRAFFIC = {
     "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "5ea32b42bb6f5df8",
-             "bytes": (295675.9 + 2138.5) * 2 * 1024 + (4364.1 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d7ae9b3f18317702",
-               "bytes": 57710.4 * 2 * 1024 + 32256.0 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d7ae9b3f18317702",
-               "bytes": 16460.2 * 2 * 1024 + 114741.7 * 1024},
+             "bytes": (295675.2 + 2138.5) * 2 * 1024 + (4365.2 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d8d7ac0efb751357",
+               "bytes": 57709.5 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "d8d7ac0efb751357",
+               "bytes": 16460.4 * 2 * 1024 + 114751.4 * 1024},
 }
 
 
