@@ -94,15 +94,41 @@ def _check(status: int) -> None:
         raise KvqError(status, library().kvq_last_error().decode())
 
 
-def _stream(t) -> int:
+def _stream(idx: int) -> int:
+    """The current HIP stream of device idx."""
     import torch
-    if t is None or not t.is_cuda:
-        return 0
-    return torch.cuda.current_stream(t.device).cuda_stream
+    return torch.cuda.current_stream(idx).cuda_stream
+
+
+def _on(idx: int, fn, *args):
+    """fn(*args) with device idx current: the library launches on the
+    current device."""
+    import torch
+    if idx == torch.cuda.current_device():
+        return fn(*args)
+    with torch.cuda.device(idx):
+        return fn(*args)
 
 
 def _ptr(t) -> int:
     return t.data_ptr() if t is not None else 0
+
+
+def _req(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _device(*ts) -> int:
+    """The one CUDA device every tensor lives on: the kernels take raw device
+    pointers, so a host tensor or a tensor on another GPU is refused here
+    rather than handed to the GPU."""
+    idx = ts[0].get_device()
+    for t in ts:
+        d = t.get_device()
+        _req(d >= 0, "every tensor must be on a GPU (got a host tensor)")
+        _req(d == idx, f"tensors on different devices: cuda:{idx} and cuda:{d}")
+    return idx
 
 
 class Plan:
@@ -187,30 +213,37 @@ def encode(plan: Plan, x, lam, codes, scales, t0: int = 0):
     Tcap = codes.shape[2]
     assert codes.dim() == 4 and tuple(codes.shape) == (B, H, Tcap, plan.code_bytes), "codes shape"
     assert scales.dim() == 4 and tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), "scales shape"
-    _check(library().kvq_encode(plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam), _lam_args(lam, H, plan.D),
-                                _ptr(codes), _ptr(scales), Tcap, t0, _stream(x)))
+    idx = _device(x, lam, codes, scales)
+    _check(_on(idx, library().kvq_encode, plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam),
+               _lam_args(lam, H, plan.D), _ptr(codes), _ptr(scales), Tcap, t0, _stream(idx)))
 
 
 def decode(plan: Plan, codes, scales, lam, y, t0: int = 0):
     """Dequantize tokens t0..t0+T-1 into y [B, H, T, D] (fp16 or fp32)."""
     import torch
     assert codes.is_contiguous() and scales.is_contiguous() and lam.is_contiguous()
+    assert codes.dtype == torch.uint8 and scales.dtype == torch.float16 and lam.dtype == torch.float32
     B, H, Tcap = codes.shape[0], codes.shape[1], codes.shape[2]
     assert codes.dim() == 4 and codes.shape[3] == plan.code_bytes, "codes shape"
     assert tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), "scales shape"
     assert y.dim() == 4 and y.shape[:2] == (B, H) and y.shape[3] == plan.D and y.stride(3) == 1
     dt = {torch.float16: _F16, torch.float32: _F32}[y.dtype]
-    _check(library().kvq_decode(plan.handle, _ptr(codes), _ptr(scales), B, H, Tcap, t0, y.shape[2],
-                                _ptr(lam), _lam_args(lam, H, plan.D), _ptr(y), dt,
-                                y.stride(0), y.stride(1), y.stride(2), _stream(y)))
+    idx = _device(codes, scales, lam, y)
+    _check(_on(idx, library().kvq_decode, plan.handle, _ptr(codes), _ptr(scales), B, H, Tcap, t0, y.shape[2],
+               _ptr(lam), _lam_args(lam, H, plan.D), _ptr(y), dt,
+               y.stride(0), y.stride(1), y.stride(2), _stream(idx)))
 
 
 def rotate(plan: Plan, x, lam, w):
     """w [B, H, T, D] fp32 = lambda * (R x) (the encoder's transform alone)."""
+    import torch
+    assert x.dtype == torch.float16 and lam.dtype == torch.float32 and w.dtype == torch.float32
+    assert lam.is_contiguous()
     B, H, T, sb, sh, st = _x_args(x, plan.D)
     assert w.is_contiguous() and tuple(w.shape) == (B, H, T, plan.D)
-    _check(library().kvq_rotate(plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam),
-                                _lam_args(lam, H, plan.D), _ptr(w), _stream(x)))
+    idx = _device(x, lam, w)
+    _check(_on(idx, library().kvq_rotate, plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam),
+               _lam_args(lam, H, plan.D), _ptr(w), _stream(idx)))
 
 
 def attn_workspace_size(D: int, B: int, Hq: int, seq_len: int) -> int:
@@ -223,25 +256,41 @@ def attn_decode(plan: Plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_
                 sm_scale: float, out, workspace):
     """Decode-step attention over the int4 cache: out [B, Hq, D]."""
     import torch
+    _req(q.dim() == 3 and q.dtype == torch.float16 and q.shape[2] == plan.D, "q must be fp16 [B, Hq, D]")
     B, Hq, D = q.shape
+    _req(k_codes.dim() == 4, "codes must be [B, Hkv, Tcap, D*bits/8]")
     Hkv, Tcap = k_codes.shape[1], k_codes.shape[2]
+    cshape, sshape = (B, Hkv, Tcap, plan.code_bytes), (B, Hkv, Tcap, D // plan.G)
+    for c, sc in ((k_codes, k_scales), (v_codes, v_scales)):
+        _req(c.dtype == torch.uint8 and tuple(c.shape) == cshape, f"codes must be uint8 {cshape}")
+        _req(sc.dtype == torch.float16 and tuple(sc.shape) == sshape, f"scales must be fp16 {sshape}")
+    for lam in (lam_k, lam_v):
+        _req(lam.dtype == torch.float32 and tuple(lam.shape) == (Hkv, D), f"lambda must be fp32 [{Hkv}, {D}]")
+    _req(tuple(out.shape) == (B, Hq, D), f"out must be [{B}, {Hq}, {D}]")
     for t in (q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out, workspace):
         assert t.is_contiguous()
     dt = {torch.float16: _F16, torch.float32: _F32}[out.dtype]
-    _check(library().kvq_attn_decode(plan.handle, _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(lam_k),
-                                     _ptr(v_codes), _ptr(v_scales), _ptr(lam_v), B, Hq, Hkv, Tcap, seq_len,
-                                     float(sm_scale), _ptr(out), dt, _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(), _stream(q)))
+    idx = _device(q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out, workspace)
+    _check(_on(idx, library().kvq_attn_decode, plan.handle, _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(lam_k),
+               _ptr(v_codes), _ptr(v_scales), _ptr(lam_v), B, Hq, Hkv, Tcap, seq_len,
+               float(sm_scale), _ptr(out), dt, _ptr(workspace),
+               workspace.numel() * workspace.element_size(), _stream(idx)))
 
 
 def attn_decode_f16(q, k, v, seq_len: int, sm_scale: float, out, workspace):
     """The same attention over an fp16 cache k, v [B, Hkv, Tcap, D]."""
     import torch
+    _req(q.dim() == 3 and q.dtype == torch.float16, "q must be fp16 [B, Hq, D]")
     B, Hq, D = q.shape
+    _req(k.dim() == 4 and k.dtype == torch.float16 and k.shape[0] == B and k.shape[3] == D,
+         "k must be fp16 [B, Hkv, Tcap, D]")
+    _req(v.dtype == torch.float16 and v.shape == k.shape, "v must match k")
     Hkv, Tcap = k.shape[1], k.shape[2]
+    _req(tuple(out.shape) == (B, Hq, D), f"out must be [{B}, {Hq}, {D}]")
     for t in (q, k, v, out, workspace):
         assert t.is_contiguous()
     dt = {torch.float16: _F16, torch.float32: _F32}[out.dtype]
-    _check(library().kvq_attn_decode_f16(D, _ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Tcap, seq_len,
-                                         float(sm_scale), _ptr(out), dt, _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(q)))
+    idx = _device(q, k, v, out, workspace)
+    _check(_on(idx, library().kvq_attn_decode_f16, D, _ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Tcap, seq_len,
+               float(sm_scale), _ptr(out), dt, _ptr(workspace),
+               workspace.numel() * workspace.element_size(), _stream(idx)))

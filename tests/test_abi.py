@@ -12,6 +12,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import oracle as O
 import kv_cache_int4_amd as K
@@ -200,3 +201,30 @@ def test_workspace_size_monotone():
     assert 0 < a < b
     with pytest.raises(K.KvqError):
         K.attn_workspace_size(64, 2, 8, 100)
+
+
+def test_binding_refuses_host_tensors():
+    """The Python binding hands raw pointers to the GPU: host tensors are
+    refused before any library call (checked here on the CPU)."""
+    p = K.Plan(128, 32, "srft", 1)
+    x = torch.zeros((1, 2, 4, 128), dtype=torch.float16)
+    lam = torch.ones((2, 128), dtype=torch.float32)
+    codes = torch.zeros((1, 2, 8, 64), dtype=torch.uint8)
+    scales = torch.zeros((1, 2, 8, 4), dtype=torch.float16)
+    with pytest.raises(ValueError, match="host tensor"):
+        K.encode(p, x, lam, codes, scales)
+    with pytest.raises(ValueError, match="host tensor"):
+        K.decode(p, codes, scales, lam, torch.zeros((1, 2, 8, 128), dtype=torch.float16))
+    with pytest.raises(ValueError, match="host tensor"):
+        K.rotate(p, x, lam, torch.zeros((1, 2, 4, 128), dtype=torch.float32))
+    q = torch.zeros((1, 4, 128), dtype=torch.float16)
+    out = torch.zeros((1, 4, 128), dtype=torch.float32)
+    ws = torch.zeros(K.attn_workspace_size(128, 1, 4, 8), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="host tensor"):
+        K.attn_decode(p, q, codes, scales, lam, codes, scales, lam, 8, 0.1, out, ws)
+    kv = torch.zeros((1, 2, 8, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="host tensor"):
+        K.attn_decode_f16(q, kv, kv, 8, 0.1, out, ws)
+    # shapes that do not match the plan are refused first
+    with pytest.raises(ValueError, match="codes must be"):
+        K.attn_decode(p, q, codes[..., :32], scales, lam, codes, scales, lam, 8, 0.1, out, ws)
