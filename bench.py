@@ -336,16 +336,15 @@ def mixed_leg(K, W, torch, stream, dev, n_sets, n):
     return res
 
 
-def graph_leg(K, torch, stream, plan, k_new, v_new, lam_k, lam_v, cache, T0, q, L, sm, out, ws, n):
+def graph_leg(K, torch, stream, plan, kv_new, lam_kv, lam_k, lam_v, cache, T0, q, L, sm, out, ws, n):
     """The decode step (append K and V, then attention) captured once in a
     HIP graph and replayed n times: us per replayed step.  Capture and
     replay go through torch's graph API; the library calls allocate,
     free, synchronize and memset nothing, so the step captures as is."""
-    kc, ks, vc, vs = cache
+    kc, ks, vc, vs, kvc, kvs = cache
 
     def step():
-        K.encode(plan, k_new, lam_k, kc, ks, T0)
-        K.encode(plan, v_new, lam_v, vc, vs, T0)
+        K.encode(plan, kv_new, lam_kv, kvc, kvs, T0)
         K.attn_decode(plan, q, kc, ks, lam_k, vc, vs, lam_v, L, sm, out, ws)
 
     side = torch.cuda.Stream()
@@ -417,16 +416,18 @@ def main():
     Tcap = T0 + 256
     aplan = K.Plan(D, 32, "srft", dc.sign_seed)
     k16, v16, lam_k, lam_v, q = W.decode_inputs(B, Hkv, Hq, Tcap, D, dc.data_seed, dev)
+    # A layer's K and V caches are one allocation [2B, Hkv, Tcap, ...], K rows
+    # first: the new token's K and V go in with one kvq_encode call over the
+    # 2B rows, lambda_K / lambda_V given per row.
     caches = []
     for _ in range(2):
-        kc = torch.empty((B, Hkv, Tcap, D // 2), dtype=torch.uint8, device=dev)
-        ks = torch.empty((B, Hkv, Tcap, D // 32), dtype=torch.float16, device=dev)
-        vc, vs = torch.empty_like(kc), torch.empty_like(ks)
-        K.encode(aplan, k16[:, :, :T0], lam_k, kc, ks, 0)
-        K.encode(aplan, v16[:, :, :T0], lam_v, vc, vs, 0)
-        caches.append((kc, ks, vc, vs))
-    k_new = k16[:, :, T0:T0 + 1]
-    v_new = v16[:, :, T0:T0 + 1]
+        kvc = torch.empty((2 * B, Hkv, Tcap, D // 2), dtype=torch.uint8, device=dev)
+        kvs = torch.empty((2 * B, Hkv, Tcap, D // 32), dtype=torch.float16, device=dev)
+        K.encode(aplan, k16[:, :, :T0], lam_k, kvc[:B], kvs[:B], 0)
+        K.encode(aplan, v16[:, :, :T0], lam_v, kvc[B:], kvs[B:], 0)
+        caches.append((kvc[:B], kvs[:B], kvc[B:], kvs[B:], kvc, kvs))
+    kv_new = torch.cat([k16[:, :, T0:T0 + 1], v16[:, :, T0:T0 + 1]]).contiguous()        # [2B, Hkv, 1, D]
+    lam_kv = torch.cat([lam_k.expand(B, Hkv, D), lam_v.expand(B, Hkv, D)]).contiguous()  # [2B, Hkv, D]
     ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     sm = 1.0 / math.sqrt(D)
@@ -438,14 +439,13 @@ def main():
 
     def run_phase(p, i):
         x, lam, codes, scales, y = sets[i % len(sets)]
-        kc, ks, vc, vs = caches[i % 2]
+        kc, ks, vc, vs, kvc, kvs = caches[i % 2]
         if p == "encode":
             K.encode(plan, x, lam, codes, scales)
         elif p == "decode":
             K.decode(plan, codes, scales, lam, y)
         elif p == "append":
-            K.encode(aplan, k_new, lam_k, kc, ks, T0)
-            K.encode(aplan, v_new, lam_v, vc, vs, T0)
+            K.encode(aplan, kv_new, lam_kv, kvc, kvs, T0)
         else:
             K.attn_decode(aplan, q, kc, ks, lam_k, vc, vs, lam_v, L, sm, out, ws)
 
@@ -489,7 +489,7 @@ def main():
     torch.cuda.synchronize()
     f16_us = e0.elapsed_time(e1) / n16 * 1e3
     # ---- the same decode step replayed from a captured HIP graph ----
-    graph_us = graph_leg(K, torch, stream, aplan, k_new, v_new, lam_k, lam_v, caches[0], T0, q, L, sm, out, ws,
+    graph_us = graph_leg(K, torch, stream, aplan, kv_new, lam_kv, lam_k, lam_v, caches[0], T0, q, L, sm, out, ws,
                          max(10, args.steps))
     # ---- D=256 (Gemma-3-1B-shaped prefix), both rotations, timed apart ----
     gemma = d256_leg(K, torch, stream, g_cfg, g_sets, max(10, args.steps))

@@ -94,3 +94,26 @@ def test_decode_step_graph_replays():
             ref = O.attention_int4(np16(q_in), kc.cpu().numpy(), ks.cpu().numpy(), lam_k.cpu().numpy(),
                                    vc.cpu().numpy(), vs.cpu().numpy(), lam_v.cpu().numpy(), L, sm, O.SRFT, signs)
             say(f"   eager step vs oracle: rel err {P.compare_attention(np16(out), ref):.2e}")
+
+
+def test_stacked_kv_append_matches_two_calls():
+    """K and V caches held as one [2B, Hkv, Tcap, ...] allocation (K rows
+    first) take the new token's K and V in one kvq_encode call over 2B rows,
+    with lambda_K / lambda_V given per row: the bytes written equal those of
+    two separate calls."""
+    D, B, Hkv, T0 = 128, 64, 2, 500
+    Tcap = T0 + 4
+    plan = K.Plan(D, 32, "srft", 11)
+    k16, v16, lam_k, lam_v, _ = W.decode_inputs(B, Hkv, 8, Tcap, D, 3, "cuda")
+    kvc = torch.full((2 * B, Hkv, Tcap, D // 2), 0x5A, dtype=torch.uint8, device="cuda")
+    kvs = torch.full((2 * B, Hkv, Tcap, D // 32), 7.0, dtype=torch.float16, device="cuda")
+    kc, ks = kvc[:B].clone(), kvs[:B].clone()
+    vc, vs = kvc[B:].clone(), kvs[B:].clone()
+    kv_new = torch.cat([k16[:, :, T0:T0 + 1], v16[:, :, T0:T0 + 1]]).contiguous()
+    lam_kv = torch.cat([lam_k.expand(B, Hkv, D), lam_v.expand(B, Hkv, D)]).contiguous()
+    K.encode(plan, kv_new, lam_kv, kvc, kvs, T0)
+    K.encode(plan, k16[:, :, T0:T0 + 1], lam_k, kc, ks, T0)
+    K.encode(plan, v16[:, :, T0:T0 + 1], lam_v, vc, vs, T0)
+    torch.cuda.synchronize()
+    assert torch.equal(kvc[:B], kc) and torch.equal(kvs[:B], ks)
+    assert torch.equal(kvc[B:], vc) and torch.equal(kvs[B:], vs)
