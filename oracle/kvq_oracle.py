@@ -21,7 +21,7 @@ What the method computes, and where it is stated
 * Compression 3.0x-3.56x (explainer, "Speichereffizienz"): 16 bits against
   4 + 16/32 bits per channel, i.e. groups of 32 with fp16 scales.
 
-Readings where the pages are silent (each listed in the design notes):
+Readings where the pages are silent:
   R1  s has one sign per complex pair (length D/2) for SRFT and one per real
       channel (length D) for SRHT.
   R2  "pack" pairs adjacent channels: z_k = x_{2k} + i x_{2k+1}; unpacking
