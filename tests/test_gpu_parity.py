@@ -1,11 +1,11 @@
 """GPU parity: libkvq (through the C ABI) against the CPU oracle on the same
 seeded inputs.
 
-Bars (per spec tolerances): rotated fp32 within 1e-5 relative per
-vector; codes and scales bit-exact except within 1e-4 of a rounding boundary
-with the mismatch fraction below 1e-5; decoded values within 1e-3 absolute
-(fp32) or half an fp16 ulp plus 1e-3 (fp16); attention within 2e-3 relative
-per (batch, head).  Output buffers carry canary bytes around the written
+Bars: rotated fp32 within 1e-5 relative per vector; codes and scales
+bit-exact except within 1e-4 of a rounding boundary with the mismatch
+fraction below 1e-5; decoded values within 1e-3 absolute (fp32) or half an
+fp16 ulp plus 1e-3 (fp16); attention within 2e-3 relative per (batch,
+head).  Output buffers carry canary bytes around the written
 region to catch stray writes.
 """
 
