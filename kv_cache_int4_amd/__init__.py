@@ -188,12 +188,16 @@ def cache_shapes(B: int, H: int, Tcap: int, D: int, G: int = GROUP, bits: int = 
     return (B, H, Tcap, D * bits // 8), (B, H, Tcap, D // G)
 
 
-def _lam_args(lam, H, D):
+def _lam_args(lam, B, H, D):
+    """lambda_sb of a [H, D] table (shared across the batch) or a [1 or B,
+    H, D] one; any other leading size would make the kernels read rows past
+    the tensor, so it is refused here."""
     if lam.dim() == 2:
-        assert tuple(lam.shape) == (H, D)
+        _req(tuple(lam.shape) == (H, D), f"lambda must be [{H}, {D}] or [1 or {B}, {H}, {D}]")
         return 0
-    assert lam.dim() == 3 and lam.shape[1:] == (H, D)
-    assert lam.stride(2) == 1 and lam.stride(1) == D
+    _req(lam.dim() == 3 and tuple(lam.shape[1:]) == (H, D) and lam.shape[0] in (1, B),
+         f"lambda must be [{H}, {D}] or [1 or {B}, {H}, {D}] (got {tuple(lam.shape)})")
+    _req(lam.stride(2) == 1 and lam.stride(1) == D, "lambda must be dense in (H, D)")
     return 0 if lam.shape[0] == 1 else lam.stride(0)
 
 
@@ -213,9 +217,10 @@ def encode(plan: Plan, x, lam, codes, scales, t0: int = 0):
     Tcap = codes.shape[2]
     assert codes.dim() == 4 and tuple(codes.shape) == (B, H, Tcap, plan.code_bytes), "codes shape"
     assert scales.dim() == 4 and tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), "scales shape"
+    lsb = _lam_args(lam, B, H, plan.D)
     idx = _device(x, lam, codes, scales)
     _check(_on(idx, library().kvq_encode, plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam),
-               _lam_args(lam, H, plan.D), _ptr(codes), _ptr(scales), Tcap, t0, _stream(idx)))
+               lsb, _ptr(codes), _ptr(scales), Tcap, t0, _stream(idx)))
 
 
 def decode(plan: Plan, codes, scales, lam, y, t0: int = 0):
@@ -228,9 +233,10 @@ def decode(plan: Plan, codes, scales, lam, y, t0: int = 0):
     assert tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), "scales shape"
     assert y.dim() == 4 and y.shape[:2] == (B, H) and y.shape[3] == plan.D and y.stride(3) == 1
     dt = {torch.float16: _F16, torch.float32: _F32}[y.dtype]
+    lsb = _lam_args(lam, B, H, plan.D)
     idx = _device(codes, scales, lam, y)
     _check(_on(idx, library().kvq_decode, plan.handle, _ptr(codes), _ptr(scales), B, H, Tcap, t0, y.shape[2],
-               _ptr(lam), _lam_args(lam, H, plan.D), _ptr(y), dt,
+               _ptr(lam), lsb, _ptr(y), dt,
                y.stride(0), y.stride(1), y.stride(2), _stream(idx)))
 
 
@@ -241,9 +247,10 @@ def rotate(plan: Plan, x, lam, w):
     assert lam.is_contiguous()
     B, H, T, sb, sh, st = _x_args(x, plan.D)
     assert w.is_contiguous() and tuple(w.shape) == (B, H, T, plan.D)
+    lsb = _lam_args(lam, B, H, plan.D)
     idx = _device(x, lam, w)
     _check(_on(idx, library().kvq_rotate, plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam),
-               _lam_args(lam, H, plan.D), _ptr(w), _stream(idx)))
+               lsb, _ptr(w), _stream(idx)))
 
 
 def attn_workspace_size(D: int, B: int, Hq: int, seq_len: int) -> int:
@@ -252,9 +259,8 @@ def attn_workspace_size(D: int, B: int, Hq: int, seq_len: int) -> int:
     return n.value
 
 
-def attn_decode(plan: Plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, seq_len: int,
-                sm_scale: float, out, workspace):
-    """Decode-step attention over the int4 cache: out [B, Hq, D]."""
+def _attn_checks(plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out):
+    """Shapes, dtypes and layouts of a decode-step attention call."""
     import torch
     _req(q.dim() == 3 and q.dtype == torch.float16 and q.shape[2] == plan.D, "q must be fp16 [B, Hq, D]")
     B, Hq, D = q.shape
@@ -267,8 +273,18 @@ def attn_decode(plan: Plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_
     for lam in (lam_k, lam_v):
         _req(lam.dtype == torch.float32 and tuple(lam.shape) == (Hkv, D), f"lambda must be fp32 [{Hkv}, {D}]")
     _req(tuple(out.shape) == (B, Hq, D), f"out must be [{B}, {Hq}, {D}]")
-    for t in (q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out, workspace):
-        assert t.is_contiguous()
+    for t in (q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out):
+        _req(t.is_contiguous(), "attention tensors must be contiguous")
+
+
+def attn_decode(plan: Plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, seq_len: int,
+                sm_scale: float, out, workspace):
+    """Decode-step attention over the int4 cache: out [B, Hq, D]."""
+    import torch
+    _attn_checks(plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out)
+    _req(workspace.is_contiguous(), "workspace must be contiguous")
+    B, Hq, D = q.shape
+    Hkv, Tcap = k_codes.shape[1], k_codes.shape[2]
     dt = {torch.float16: _F16, torch.float32: _F32}[out.dtype]
     idx = _device(q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out, workspace)
     _check(_on(idx, library().kvq_attn_decode, plan.handle, _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(lam_k),

@@ -119,6 +119,17 @@ kvq_status check_x(const kvq_plan* p, const uint16_t* x, int64_t B, int64_t H, i
   return KVQ_OK;
 }
 
+// Scales: rows of 16 bytes or more (D = 256, or groups of 16 at D = 128) are
+// moved with 16-byte accesses, the others with 8-byte (encode) or 4-byte
+// (decode) ones.
+kvq_status check_scales_align(const kvq_plan* p, const uint16_t* scales) {
+  const bool wide = (p->D == 256) || (p->D == 128 && p->G == 16);
+  if (wide && !aligned(scales, 16))
+    return fail(KVQ_ERR_ALIGN, "scales is not 16-byte aligned (D=%d, G=%d)", p->D, p->G);
+  if (!aligned(scales, 8)) return fail(KVQ_ERR_ALIGN, "scales is not 8-byte aligned");
+  return KVQ_OK;
+}
+
 std::mutex g_cu_mutex;
 int g_cu_count[64] = {0};
 
@@ -236,7 +247,7 @@ kvq_status kvq_encode(const kvq_plan* plan, const uint16_t* x, int64_t B, int64_
     if (kvq_status s = check_x(plan, x, B, H, T, x_sb, x_sh, x_st, lambda, lambda_sb)) return s;
     if (!codes || !scales) return fail(KVQ_ERR_INVALID, "codes or scales is NULL");
     if (!aligned(codes, 16)) return fail(KVQ_ERR_ALIGN, "codes is not 16-byte aligned");
-    if (!aligned(scales, 8)) return fail(KVQ_ERR_ALIGN, "scales is not 8-byte aligned");
+    if (kvq_status s = check_scales_align(plan, scales)) return s;
     if (!product_ok(B, H, Tcap, plan->D)) return fail(KVQ_ERR_INVALID, "cache shape too large");
     kvq::CodecDesc d{};
     fill_signs(plan, d);
@@ -292,10 +303,16 @@ kvq_status kvq_decode(const kvq_plan* plan, const uint8_t* codes, const uint16_t
     if (B == 0 || H == 0 || T == 0) return ok();
     if (!codes || !scales || !lambda || !y) return fail(KVQ_ERR_INVALID, "NULL pointer argument");
     if (!aligned(codes, 16)) return fail(KVQ_ERR_ALIGN, "codes is not 16-byte aligned");
-    if (!aligned(scales, 8)) return fail(KVQ_ERR_ALIGN, "scales is not 8-byte aligned");
-    if (!aligned(lambda, 4)) return fail(KVQ_ERR_ALIGN, "lambda is not 4-byte aligned");
+    if (kvq_status s = check_scales_align(plan, scales)) return s;
     if (y_sb < 0 || y_sh < 0 || y_st < 0 || lambda_sb < 0)
       return fail(KVQ_ERR_INVALID, "strides must be non-negative");
+    if (plan->D == 128 || plan->D == 256) {
+      // the decoders bring each lambda row into LDS with 16-byte direct loads
+      if (!aligned(lambda, 16)) return fail(KVQ_ERR_ALIGN, "lambda is not 16-byte aligned (D=%d decode)", plan->D);
+      if (lambda_sb % 4) return fail(KVQ_ERR_ALIGN, "lambda_sb must be a multiple of 4 (D=%d decode)", plan->D);
+    } else if (!aligned(lambda, 4)) {
+      return fail(KVQ_ERR_ALIGN, "lambda is not 4-byte aligned");
+    }
     if (y_dtype == KVQ_F16) {
       if (!aligned(y, 16)) return fail(KVQ_ERR_ALIGN, "y is not 16-byte aligned");
       if (y_sb % 8 || y_sh % 8 || y_st % 8)
@@ -337,7 +354,7 @@ namespace {
 
 kvq_status check_attn_common(int32_t D, const uint16_t* q, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tcap,
                              int64_t seq_len, void* out, kvq_dtype out_dtype, void* workspace,
-                             size_t workspace_bytes) {
+                             size_t workspace_bytes, bool check_workspace) {
   if (B < 0 || Hq < 0 || Hkv <= 0 || Tcap < 0) return fail(KVQ_ERR_INVALID, "bad shape");
   if (Hq % Hkv) return fail(KVQ_ERR_INVALID, "Hq=%lld is not a multiple of Hkv=%lld", (long long)Hq, (long long)Hkv);
   if (seq_len < 1 || seq_len > Tcap)
@@ -346,11 +363,50 @@ kvq_status check_attn_common(int32_t D, const uint16_t* q, int64_t B, int64_t Hq
   if (!q || !out) return fail(KVQ_ERR_INVALID, "q or out is NULL");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(KVQ_ERR_ALIGN, "q and out must be 16-byte aligned");
   if (!product_ok(B, Hkv, Tcap, D)) return fail(KVQ_ERR_INVALID, "shape too large");
+  if (!check_workspace) return KVQ_OK;
   const size_t need = kvq::attn_workspace_bytes(D, B, Hq, seq_len);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KVQ_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : 0);
   if (workspace && !aligned(workspace, 16)) return fail(KVQ_ERR_ALIGN, "workspace is not 16-byte aligned");
   return KVQ_OK;
+}
+
+kvq_status check_attn_plan(const kvq_plan* plan) {
+  if (plan->D != 128) return fail(KVQ_ERR_UNSUPPORTED, "attention is built for D=128 (plan D=%d)", plan->D);
+  return KVQ_OK;
+}
+
+kvq_status check_attn_cache(const uint8_t* k_codes, const uint16_t* k_scales, const float* lambda_k,
+                            const uint8_t* v_codes, const uint16_t* v_scales, const float* lambda_v) {
+  if (!k_codes || !k_scales || !lambda_k || !v_codes || !v_scales || !lambda_v)
+    return fail(KVQ_ERR_INVALID, "NULL cache pointer");
+  if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 8) || !aligned(v_scales, 8) ||
+      !aligned(lambda_k, 16) || !aligned(lambda_v, 16))
+    return fail(KVQ_ERR_ALIGN, "cache codes need 16-byte, scales 8-byte, lambda 16-byte alignment");
+  return KVQ_OK;
+}
+
+kvq::AttnDesc attn_desc(const kvq_plan* plan, const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                        const float* lambda_k, const uint8_t* v_codes, const uint16_t* v_scales,
+                        const float* lambda_v, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tcap, int64_t seq_len,
+                        float sm_scale, void* out, kvq_dtype out_dtype, void* workspace, void* stream) {
+  kvq::AttnDesc d{};
+  d.D = plan->D;
+  d.rotation = plan->rotation;
+  for (int i = 0; i < 4; ++i) d.signs[i] = plan->sign_bits[i];
+  d.int4 = true;
+  d.G = plan->G;
+  d.bits = plan->bits;
+  d.q = q;
+  d.k_codes = k_codes; d.k_scales = k_scales; d.lambda_k = lambda_k;
+  d.v_codes = v_codes; d.v_scales = v_scales; d.lambda_v = lambda_v;
+  d.B = B; d.Hq = Hq; d.Hkv = Hkv; d.Tcap = Tcap; d.seq_len = seq_len;
+  d.sm_scale = sm_scale;
+  d.out = out;
+  d.out_f32 = out_dtype == KVQ_F32;
+  d.workspace = workspace;
+  d.stream = static_cast<hipStream_t>(stream);
+  return d;
 }
 
 }  // namespace
@@ -362,32 +418,14 @@ kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q, const uint8_
                            void* stream) {
   try {
     if (kvq_status s = check_plan(plan)) return s;
-    if (plan->D != 128) return fail(KVQ_ERR_UNSUPPORTED, "attention is built for D=128 (plan D=%d)", plan->D);
+    if (kvq_status s = check_attn_plan(plan)) return s;
     if (kvq_status s = check_attn_common(plan->D, q, B, Hq, Hkv, Tcap, seq_len, out, out_dtype, workspace,
-                                         workspace_bytes))
+                                         workspace_bytes, true))
       return s;
-    if (!k_codes || !k_scales || !lambda_k || !v_codes || !v_scales || !lambda_v)
-      return fail(KVQ_ERR_INVALID, "NULL cache pointer");
-    if (!aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 8) || !aligned(v_scales, 8) ||
-        !aligned(lambda_k, 16) || !aligned(lambda_v, 16))
-      return fail(KVQ_ERR_ALIGN, "cache codes need 16-byte, scales 8-byte, lambda 16-byte alignment");
+    if (kvq_status s = check_attn_cache(k_codes, k_scales, lambda_k, v_codes, v_scales, lambda_v)) return s;
     if (B == 0 || Hq == 0) return ok();
-    kvq::AttnDesc d{};
-    d.D = plan->D;
-    d.rotation = plan->rotation;
-    for (int i = 0; i < 4; ++i) d.signs[i] = plan->sign_bits[i];
-    d.int4 = true;
-    d.G = plan->G;
-    d.bits = plan->bits;
-    d.q = q;
-    d.k_codes = k_codes; d.k_scales = k_scales; d.lambda_k = lambda_k;
-    d.v_codes = v_codes; d.v_scales = v_scales; d.lambda_v = lambda_v;
-    d.B = B; d.Hq = Hq; d.Hkv = Hkv; d.Tcap = Tcap; d.seq_len = seq_len;
-    d.sm_scale = sm_scale;
-    d.out = out;
-    d.out_f32 = out_dtype == KVQ_F32;
-    d.workspace = workspace;
-    d.stream = static_cast<hipStream_t>(stream);
+    const kvq::AttnDesc d = attn_desc(plan, q, k_codes, k_scales, lambda_k, v_codes, v_scales, lambda_v, B, Hq,
+                                      Hkv, Tcap, seq_len, sm_scale, out, out_dtype, workspace, stream);
     return hip_status(kvq::launch_attention(d), "kvq_attn_decode launch");
   } catch (...) {
     return fail(KVQ_ERR_INVALID, "internal error");
@@ -400,7 +438,7 @@ kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, 
   try {
     if (D != 128) return fail(KVQ_ERR_UNSUPPORTED, "attention is built for D=128 (D=%d)", (int)D);
     if (kvq_status s = check_attn_common(D, q, B, Hq, Hkv, Tcap, seq_len, out, out_dtype, workspace,
-                                         workspace_bytes))
+                                         workspace_bytes, true))
       return s;
     if (!k || !v) return fail(KVQ_ERR_INVALID, "k or v is NULL");
     if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_ERR_ALIGN, "k and v must be 16-byte aligned");

@@ -16,9 +16,9 @@
 // leave through coalesced 16-byte stores.  Random signs are applied as XOR
 // masks on fp16 words where each lane's masks are fixed for the kernel.
 //
-// The general kernels (rotate_kernel for the D=256 rotate-only output,
-// decode_f32_kernel for fp32 output) stage rows through registers and LDS
-// with ordinary loads.
+// The encoders also write the rotated fp32 values (rotate mode, for
+// checking the transform); decode_f32_kernel (fp32 output) stages rows
+// through registers and LDS with ordinary loads.
 //
 // Method (gist.science explainer of "When Quantization Is Free",
 // "Methodik" 1-2): sign -> FFT over the D/2 complex pairs -> pack ->
@@ -119,140 +119,6 @@ __device__ __forceinline__ Tile tile_info(const CodecArgs& a, int64_t tile) {
   const int64_t left = a.T - t.t_start;
   t.nv = static_cast<int>(left < Geo<D>::VPT ? left : Geo<D>::VPT);
   return t;
-}
-
-// Coalesced fp16 row loads of one tile into registers.
-template <int D>
-__device__ __forceinline__ void load_rows(const CodecArgs& a, const Tile& t, int lane,
-                                          uint4 (&buf)[Geo<D>::NLD]) {
-  using G = Geo<D>;
-  const int c = lane % G::CPR;
-  const int r0 = lane / G::CPR;
-  const uint16_t* base = a.x + t.b * a.sb + t.h * a.sh + (t.t_start + r0) * a.st + c * 8;
-#pragma unroll
-  for (int i = 0; i < G::NLD; ++i) {
-    const int v = i * G::RPI + r0;
-    if (v < t.nv) {
-      buf[i] = ld_stream16(base + static_cast<int64_t>(i * G::RPI) * a.st);
-    } else {
-      buf[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-// Sign-xor the staged words and scatter them into the per-lane LDS blocks.
-template <int D, int ROT>
-__device__ __forceinline__ void stage_rows(uint8_t* lds, int lane, const uint4 (&buf)[Geo<D>::NLD],
-                                           const uint4& mask) {
-  using G = Geo<D>;
-  const int c = lane % G::CPR;
-  const int r0 = lane / G::CPR;
-#pragma unroll
-  for (int i = 0; i < G::NLD; ++i) {
-    const int v = i * G::RPI + r0;
-    uint4 w = buf[i];
-    w.x ^= mask.x; w.y ^= mask.y; w.z ^= mask.z; w.w ^= mask.w;
-    if (D == 128) {
-      *reinterpret_cast<uint4*>(lds + blk_off(v, c)) = w;
-    } else if (ROT != KVQ_ROT_SRFT) {
-      *reinterpret_cast<uint4*>(lds + blk_off(2 * v + (c >> 4), c & 15)) = w;
-    } else {
-      // even pairs to lane 2v, odd pairs to lane 2v+1
-      const uint32_t off = (c & 1) * 8;
-      *reinterpret_cast<uint2*>(lds + blk_off(2 * v, c >> 1) + off) = make_uint2(w.x, w.z);
-      *reinterpret_cast<uint2*>(lds + blk_off(2 * v + 1, c >> 1) + off) = make_uint2(w.y, w.w);
-    }
-  }
-}
-
-// Each lane reads its own block and widens the 64 fp16 pairs to fp32.
-__device__ __forceinline__ void read_block(const uint8_t* lds, int lane, float (&v)[128]) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint4 w = *reinterpret_cast<const uint4*>(lds + blk_off(lane, j));
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[8 * j + 2 * e] = f16_bits_to_f32(ws[e] & 0xFFFFu);
-      v[8 * j + 2 * e + 1] = f16_bits_to_f32(ws[e] >> 16);
-    }
-  }
-}
-
-// Forward rotation of the lane's 128 values (unnormalized; the scale
-// rot_scale<D, ROT>() is applied by the caller).
-template <int D, int ROT>
-__device__ __forceinline__ void forward_rotation(float (&v)[128], int lane) {
-  if (ROT == KVQ_ROT_SRFT) {
-    fft64<false>(v);
-    if (D == 256) {
-      // radix-2 decimation in time across the lane pair: lane 2v holds the
-      // transform E of the even pairs, lane 2v+1 the (negated) transform O
-      // of the odd pairs; Z_m = E_m + W^m O_m, Z_{m+64} = E_m - W^m O_m.
-      if (lane & 1) {
-#pragma unroll
-        for (int m = 0; m < 64; ++m) twiddle<128, false>(v[2 * rev4(m)], v[2 * rev4(m) + 1], m);
-      }
-      const float sg = (lane & 1) ? 1.f : -1.f;
-      pair_fma_all(v, sg);
-    }
-  } else if (ROT == KVQ_ROT_SRHT) {
-    wht128(v);
-    if (D == 256) {
-      // H_256 [u; v] = [H u + H v; H u - H v]; the second lane holds -H v.
-      const float sg = (lane & 1) ? 1.f : -1.f;
-      pair_fma_all(v, sg);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Rotate only, D = 256 (fp32 output, for checking): w = lambda * R x
-// ---------------------------------------------------------------------------
-template <int D, int ROT>
-__global__ void __launch_bounds__(64, 2) rotate_kernel(CodecArgs a) {
-  using G = Geo<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[16384];
-  const int lane = threadIdx.x;
-  constexpr float kScale = rot_scale<D, ROT>();
-
-  // this lane's sign masks: it always stages column c of a row, i.e. the
-  // pair words 4c .. 4c+3
-  const int col = lane % G::CPR;
-  const uint4 mask = make_uint4(word_mask<D, ROT>(a.signs, 4 * col), word_mask<D, ROT>(a.signs, 4 * col + 1),
-                                word_mask<D, ROT>(a.signs, 4 * col + 2), word_mask<D, ROT>(a.signs, 4 * col + 3));
-
-  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
-    const Tile t = tile_info<D>(a, tile);
-    float v[128];
-    {
-      uint4 buf[G::NLD];
-      load_rows<D>(a, t, lane, buf);
-      stage_rows<D, ROT>(lds, lane, buf, mask);
-    }
-    __syncthreads();
-    read_block(lds, lane, v);
-    __syncthreads();
-
-    forward_rotation<D, ROT>(v, lane);
-
-    const int half = (D == 256) ? (lane & 1) : 0;
-    const float* lam = a.lambda + t.b * a.lambda_sb + t.h * D + half * 128;
-    const int vec = lane / G::L;           // vector index inside the tile
-    float* wr = a.w + ((t.row * a.T) + t.t_start + vec) * D + half * 128;
-    if (vec < t.nv) {
-#pragma unroll
-      for (int j = 0; j < 128; j += 4) {
-        float4 o;
-        o.x = v[chan_reg<ROT>(j)] * lam[j] * kScale;
-        o.y = v[chan_reg<ROT>(j + 1)] * lam[j + 1] * kScale;
-        o.z = v[chan_reg<ROT>(j + 2)] * lam[j + 2] * kScale;
-        o.w = v[chan_reg<ROT>(j + 3)] * lam[j + 3] * kScale;
-        *reinterpret_cast<float4*>(wr + j) = o;
-      }
-    }
-    __syncthreads();
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -665,7 +531,9 @@ __device__ __forceinline__ uint32_t pair_mask256(const CodecArgs& a, int h, int 
   return 0u;
 }
 
-template <int ROT, int FMT>
+// MODE 0 writes codes and scales; MODE 1 writes the rotated values w =
+// lambda * R x in fp32 (the transform of this kernel, for checking).
+template <int ROT, int MODE, int FMT>
 __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
   using F = Fmt<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
@@ -741,7 +609,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) lam_r[q] = lr[lane + 64 * q];
     }
-    if (pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
+    if (MODE == 0 && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 
     float v[128];
     if (ROT == KVQ_ROT_SRFT) {
@@ -766,6 +634,24 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     asm volatile("" ::: "memory");
     const float4* lam4 = reinterpret_cast<const float4*>(lam_lds);   // [hh * 32 + j / 4]
     const bool valid = (lane >> 1) < t.nv;
+
+    if (MODE == 1) {
+      // lane 2v + h: channels 128 h .. 128 h + 127 of vector v
+      float* wr = a.w + ((t.row * a.T) + t.t_start + (lane >> 1)) * 256 + 128 * hh;
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < 128; j += 4) {
+          const float4 l4 = lam4[32 * hh + j / 4];
+          float4 o;
+          o.x = v[chan_reg<ROT>(j)] * l4.x * kScale;
+          o.y = v[chan_reg<ROT>(j + 1)] * l4.y * kScale;
+          o.z = v[chan_reg<ROT>(j + 2)] * l4.z * kScale;
+          o.w = v[chan_reg<ROT>(j + 3)] * l4.w * kScale;
+          *reinterpret_cast<float4*>(wr + j) = o;
+        }
+      }
+      continue;
+    }
 
     float r[F::NG];
     uint32_t sc[F::NG];
@@ -812,7 +698,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
       pend_c[q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
     pend_valid = valid;
   }
-  if (pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
+  if (MODE == 0 && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1453,12 +1339,12 @@ hipError_t encode_dispatch(const CodecDesc& d, int mode) {
     if (D == 128) {
       hipLaunchKernelGGL((encode128_kernel<ROT, 1, 0>), grid, dim3(64), 0, d.stream, a);
     } else {
-      hipLaunchKernelGGL((rotate_kernel<D, ROT>), grid, dim3(64), 0, d.stream, a);
+      hipLaunchKernelGGL((encode256_kernel<ROT, 1, 0>), grid, dim3(64), 0, d.stream, a);
     }
   } else if (D == 128) {
     hipLaunchKernelGGL((encode128_kernel<ROT, 0, FMT>), grid, dim3(64), 0, d.stream, a);
   } else {
-    hipLaunchKernelGGL((encode256_kernel<ROT, FMT>), grid, dim3(64), 0, d.stream, a);
+    hipLaunchKernelGGL((encode256_kernel<ROT, 0, FMT>), grid, dim3(64), 0, d.stream, a);
   }
   return hipGetLastError();
 }

@@ -66,8 +66,12 @@ hipError_t launch_encode_mixed(const CodecDesc& d, int mode);
 hipError_t launch_decode_mixed(const CodecDesc& d, bool f32);
 
 // Split-K geometry of the attention kernels.
-int64_t attn_num_splits(int64_t B, int64_t Hkv, int64_t seq_len);
+// Workspace bytes any call with this seq_len may need (the caller-owned
+// workspace is sized by this), and bytes this call needs on the current
+// device (no more than the former).
 size_t attn_workspace_bytes(int D, int64_t B, int64_t Hq, int64_t seq_len);
+size_t attn_workspace_needed(const AttnDesc& d);
 hipError_t launch_attention(const AttnDesc& d);
+
 
 }  // namespace kvq

@@ -10,8 +10,8 @@ What the method computes, and where it is stated
 * Rotation.  The gist.science explainer ("Methodik", item 1) defines the
   sign-randomized Fourier transform as pack(F . diag(s) . x) with F the
   unitary DFT and s a fixed random sign vector; the paper's abstract names
-  the Walsh-Hadamard alternative (SRHT) and says the two are statistically
-  indistinguishable for KV quality.
+  the Walsh-Hadamard alternative (SRHT) and reports no measurable quality
+  difference between the two.
 * Order of the fused pipeline (explainer, "Methodik", item 2): sign multiply
   on load, FFT over log2(d/2) radix-2 passes (so the transform length is
   d/2 complex points), pack to a real representation, per-channel lambda
@@ -42,6 +42,8 @@ Readings where the pages are silent:
       kernel computes in: w is the float64 rotation rounded to float32, the
       quotients absmax/7 and w/scale are IEEE float32 divisions (correctly
       rounded), then rounded to fp16 / rounded half-to-even to an integer.
+      The plain definition (each exact quotient rounded once, from the
+      float64 values) is kept beside it as decide="fp64", for reporting.
 
 Signs come from SplitMix64 (G. L. Steele, D. Lea, C. H. Flood, "Fast
 splittable pseudorandom number generators", OOPSLA 2014), written here from
@@ -59,7 +61,8 @@ __all__ = [
     "SRFT", "SRHT", "IDENTITY", "HERMITIAN", "ROTATIONS", "GROUP",
     "splitmix64", "plan_signs",
     "rotate_forward", "rotate_inverse",
-    "quantize_groups", "pack_nibbles", "unpack_nibbles", "pack_codes", "unpack_codes",
+    "quantize_groups", "fp16_of_quotient", "rint_of_quotient",
+    "pack_nibbles", "unpack_nibbles", "pack_codes", "unpack_codes",
     "code_range",
     "encode", "decode", "rotate",
     "boundary_distances",
@@ -264,18 +267,68 @@ def code_range(bits: int):
     return -(1 << (bits - 1)), (1 << (bits - 1)) - 1
 
 
-def quantize_groups(w: np.ndarray, G: int = GROUP, bits: int = 4):
+def _fp16_midpoints(t: np.ndarray):
+    """The fp16 neighbours lo <= t < hi of non-negative float64 values t and
+    their midpoint, all as float64 (lo = hi = t where t is an fp16 value)."""
+    lo = t.astype(np.float16)
+    lo = np.where(lo.astype(np.float64) > t, np.nextafter(lo, np.float16(0)), lo)
+    hi = np.nextafter(lo, np.float16(np.inf))
+    return lo, hi, (lo.astype(np.float64) + hi.astype(np.float64)) / 2
+
+
+def fp16_of_quotient(a: np.ndarray, d: int) -> np.ndarray:
+    """fp16 of the exact quotient a / d (a >= 0 float64, d = 7 or 127),
+    rounded once to nearest, ties to even, subnormals kept.
+
+    numpy rounds the float64 quotient to fp16; that is one rounding of the
+    exact quotient because the float64 quotient of a float64 by a small
+    integer lands on an fp16 rounding midpoint only when the exact quotient
+    does (the midpoint m has at most 12 significant bits, so m * d is a
+    float64 value and the float64 neighbours of a / d sit at least 4/d of a
+    float64 ulp of m away)."""
+    a = np.asarray(a, dtype=np.float64)
+    q = a / float(d)
+    assert np.all(q <= 65504.0), "scale overflows fp16 (reading R11)"
+    return q.astype(np.float16)
+
+
+def rint_of_quotient(w: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """rint_half_even of the exact quotient w / s (float64 w, s > 0 an fp16
+    value): the float64 quotient is a half-integer only when the exact one
+    is (k + 1/2 times an fp16 value is a float64 value, and a float64 w next
+    to it gives a quotient at least a float64 ulp away), so rounding it is
+    one rounding of the exact quotient."""
+    return np.rint(w / s)
+
+
+def quantize_groups(w: np.ndarray, G: int = GROUP, bits: int = 4, decide: str = "fp32"):
     """Per-group abs-max scale and signed codes of the lambda-scaled rotation.
 
     Takes w (float64, last axis D) and returns
       q      int8  [..., D]     codes in [qmin, qmax] (code_range(bits))
       scale  float16 [..., D/G] one scale per group of G consecutive channels
-    Decision precision (reading DP): w is rounded to float32; the group
-    abs-max a is exact in float32; scale = fp16_RNE(fp32(a / qmax)); the code
-    is rint_half_even(fp32(w / scale)) clamped to [qmin, qmax], and 0 where
-    the scale is zero (reading R10).
+    Decision precision, decide = "fp32" (reading DP): w is rounded to
+    float32; the group abs-max a is exact in float32; scale =
+    fp16_RNE(fp32(a / qmax)); the code is rint_half_even(fp32(w / scale))
+    clamped to [qmin, qmax], and 0 where the scale is zero (reading R10).
+    decide = "fp64" takes the same decisions on the float64 values with one
+    rounding of each exact quotient: scale = fp16_RNE(a / qmax) and code =
+    rint_half_even(w / scale), the plain definition with no float32 step.
     """
     qmin, qmax = code_range(bits)
+    if decide == "fp64":
+        w64 = np.asarray(w, dtype=np.float64)
+        D = w64.shape[-1]
+        assert D % G == 0
+        wg = w64.reshape(w64.shape[:-1] + (D // G, G))
+        a = np.max(np.abs(wg), axis=-1)
+        scale = fp16_of_quotient(a, qmax)
+        s64 = scale.astype(np.float64)[..., None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            k = rint_of_quotient(wg, np.where(s64 > 0, s64, 1.0))
+        q = np.where(s64 == 0, 0.0, np.clip(k, qmin, qmax))
+        return q.reshape(w64.shape).astype(np.int8), scale
+    assert decide == "fp32", f"unknown decision precision {decide!r}"
     w32 = np.asarray(w, dtype=np.float64).astype(np.float32)
     D = w32.shape[-1]
     assert D % G == 0
@@ -340,12 +393,13 @@ def rotate(x16: np.ndarray, lam: np.ndarray, rotation: int, signs: np.ndarray) -
     return np.asarray(lam, dtype=np.float64) * rotate_forward(x, rotation, signs)
 
 
-def encode(x16, lam, rotation: int, signs: np.ndarray, G: int = GROUP, bits: int = 4):
+def encode(x16, lam, rotation: int, signs: np.ndarray, G: int = GROUP, bits: int = 4, decide: str = "fp32"):
     """The full write path: x (fp16, [..., D]) and lambda ([..., D], broadcast
     like numpy) -> (codes uint8 [..., D*bits/8], scales fp16 [..., D/G],
-    w float64)."""
+    w float64).  ``decide`` selects the decision precision of the quantizer
+    (quantize_groups)."""
     w = rotate(x16, lam, rotation, signs)
-    q, scale = quantize_groups(w, G, bits)
+    q, scale = quantize_groups(w, G, bits, decide)
     return pack_codes(q, bits), scale, w
 
 
@@ -381,10 +435,7 @@ def boundary_distances(w: np.ndarray, scale_used: np.ndarray, G: int = GROUP, bi
     a = np.max(np.abs(w.reshape(w.shape[:-1] + (D // G, G))), axis=-1)
     t = a / float(qmax)
     # fp16 neighbours of t and their midpoint
-    lo = t.astype(np.float16)
-    lo = np.where(lo.astype(np.float64) > t, np.nextafter(lo, np.float16(0)), lo)
-    hi = np.nextafter(lo, np.float16(np.inf))
-    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2
+    _, _, mid = _fp16_midpoints(t)
     with np.errstate(divide="ignore", invalid="ignore"):
         scale_dist = np.where(t > 0, np.abs(t - mid) / t, np.inf)
     return code_dist, scale_dist

@@ -7,6 +7,12 @@ sits within 1e-4 of a rounding boundary:
   * a code may differ only where w/scale lies within 1e-4 (in code units) of
     a half-integer; in a group whose scale differs, the GPU codes are checked
     against the oracle's w re-quantized with the GPU's scale.
+With no rotation (KVQ_IDENTITY) both sides hold the same float32 w = lambda
+* x and the same float32 abs-max, and both take the scale as fp16 of the
+IEEE float32 quotient, so every scale must match bit for bit; a code may
+differ only where the kernel's multiply by a reciprocal (1 ulp) instead of a
+division can move w/scale across a half-integer, i.e. within (qmax + 1) *
+2^-22 code units of one.
 The mismatch fraction (codes + scales, per element) is reported and must stay
 below 1e-5 on every sample of at least 10^6 elements (int4 codes).  For int8
 codes the bar is 1e-4: the same float32 rotation error, measured in code
@@ -15,14 +21,21 @@ rate of boundary flips (2 E|w/scale| times the relative error), which puts
 the int4 bar at 1.8e-4 for int8; 1e-4 is kept.  Smaller samples cannot
 resolve a rate of 1e-5 (the expected count is below 10); there every
 mismatch must still be a boundary case, and the count may not exceed the
-99.9% quantile of a Poisson count whose mean is the bar times the number of
-elements: a kernel whose rate sits exactly at the bar fails a given small
-test at most once in a thousand runs.  (Flips are rare independent events,
-so their count in n elements is Poisson; a fixed multiple of the mean is
-too tight where the mean is below one.)
+99% quantile of a Poisson count whose mean is the bar times the number of
+elements (flips are rare independent events, so their count in n elements
+is Poisson).
+The decisions are compared twice: against the oracle's float32 decisions
+(its reading DP, the kernel's precision; the bars above apply), and against
+the plain definition with each exact quotient rounded once (decide="fp64");
+there every mismatch must also be a boundary case and the fraction must stay
+below the bar on samples of at least 10^6 elements.  Every comparison is
+recorded in RECORDS (written out by the test session when KVQ_PARITY_REPORT
+names a file).
 """
 
 from __future__ import annotations
+
+import os
 
 import numpy as np
 
@@ -31,9 +44,21 @@ import oracle as O
 BOUNDARY = 1e-4
 FRACTION = 1e-5          # int4 codes
 FRACTION8 = 1e-4         # int8 codes (see above)
+SMALL_SAMPLE_P = 0.99    # quantile of the small-sample count rule
+ROT_NAMES = {O.SRFT: "srft", O.SRHT: "srht", O.IDENTITY: "identity"}
+
+RECORDS: list = []
 
 
-def poisson_quantile(mu: float, p: float = 0.999) -> int:
+def identity_band(bits: int) -> float:
+    """Code units within which the kernel's reciprocal multiply may flip an
+    unrotated code: |w/scale| <= qmax + 1/2, and the reciprocal (1 ulp), the
+    product and the oracle's division (half an ulp each) together move the
+    quotient by at most 2^-22 relative."""
+    return (O.code_range(bits)[1] + 1) * 2.0 ** -22
+
+
+def poisson_quantile(mu: float, p: float = SMALL_SAMPLE_P) -> int:
     """Smallest k with P(Poisson(mu) <= k) >= p."""
     term = cdf = np.exp(-mu)
     k = 0
@@ -44,16 +69,51 @@ def poisson_quantile(mu: float, p: float = 0.999) -> int:
     return k
 
 
+def _mismatches(qg, sg16, w, scales_ref, codes_ref, G, bits, decide):
+    """Scale and code mismatches of the GPU's codes qg and scales sg16 (fp16
+    bits) against the oracle's (scales_ref, codes_ref), with the boundary
+    distance of each and, in groups whose scale differs, the codes expected
+    with the GPU's scale."""
+    sr = scales_ref.view(np.uint16)
+    code_dist, scale_dist = O.boundary_distances(w, scales_ref, G, bits)
+    scale_bad = sg16 != sr
+    qr = O.unpack_codes(codes_ref, bits)
+    q_expect = qr
+    if scale_bad.any():
+        sg = sg16.view(np.float16)
+        q_alt = _requantize(w, sg, G, bits, decide)
+        bad_full = np.repeat(scale_bad, G, axis=-1)
+        q_expect = np.where(bad_full, q_alt, qr)
+        cd_alt, _ = O.boundary_distances(w, sg, G, bits)
+        code_dist = np.where(bad_full, cd_alt, code_dist)
+    code_bad = qg != q_expect
+    return scale_bad, scale_dist, code_bad, code_dist
+
+
+def _requantize(w64, scales16, G, bits, decide):
+    """Oracle codes of w with the given fp16 scales, decided in float32
+    (reading DP) or from the float64 values."""
+    qmin, qmax = O.code_range(bits)
+    s16 = np.repeat(np.asarray(scales16, dtype=np.float16), G, axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        if decide == "fp64":
+            s = s16.astype(np.float64)
+            r = O.rint_of_quotient(np.asarray(w64, dtype=np.float64), np.where(s > 0, s, 1.0))
+        else:
+            s = s16.astype(np.float32)
+            r = np.rint(np.asarray(w64, dtype=np.float64).astype(np.float32) / s)
+    q = np.where(s == 0, 0, np.clip(r, qmin, qmax))
+    return q.astype(np.int16)
+
+
 def requantize(w64: np.ndarray, scales16: np.ndarray, G: int = O.GROUP, bits: int = 4) -> np.ndarray:
     """Oracle codes of w with the given fp16 scales (the same float32 decision
     as the oracle's quantizer)."""
-    qmin, qmax = O.code_range(bits)
-    w32 = np.asarray(w64, dtype=np.float64).astype(np.float32)
-    s = np.repeat(np.asarray(scales16, dtype=np.float16).astype(np.float32), G, axis=-1)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        r = w32 / s
-    q = np.where(s == 0, np.float32(0), np.clip(np.rint(r), qmin, qmax))
-    return q.astype(np.int16)
+    return _requantize(w64, scales16, G, bits, "fp32")
+
+
+def _test_id() -> str:
+    return os.environ.get("PYTEST_CURRENT_TEST", "").rsplit(" (", 1)[0]
 
 
 def compare_codes(codes_gpu, scales_gpu, x16, lam, rotation, signs, G: int = O.GROUP, bits: int = 4):
@@ -67,47 +127,57 @@ def compare_codes(codes_gpu, scales_gpu, x16, lam, rotation, signs, G: int = O.G
     N, D = w.shape[0], w.shape[-1]
     n_el = N * D
     sg = scales_gpu.view(np.uint16)
-    sr = scales_ref.view(np.uint16)
-    code_dist_ref, scale_dist = O.boundary_distances(w, scales_ref, G, bits)
+    qg = O.unpack_codes(codes_gpu, bits)
+    bar = FRACTION if bits == 4 else FRACTION8
 
-    scale_bad = sg != sr
-    n_scale_bad = int(scale_bad.sum())
+    # the oracle's float32 decisions (reading DP): the parity bar
+    scale_bad, scale_dist, code_bad, code_dist = _mismatches(qg, sg, w, scales_ref, codes_ref, G, bits, "fp32")
+    n_scale_bad, n_code_bad = int(scale_bad.sum()), int(code_bad.sum())
+    # the plain definition, each exact quotient rounded once
+    q64, scales64 = O.quantize_groups(w, G, bits, decide="fp64")
+    codes64 = O.pack_codes(q64, bits)
+    scale_bad64, scale_dist64, code_bad64, code_dist64 = _mismatches(qg, sg, w, scales64, codes64, G, bits, "fp64")
+    n_scale_bad64, n_code_bad64 = int(scale_bad64.sum()), int(code_bad64.sum())
+    frac = (n_code_bad + n_scale_bad) / max(n_el, 1)
+    frac64 = (n_code_bad64 + n_scale_bad64) / max(n_el, 1)
+    rec = {
+        "test": _test_id(), "rotation": ROT_NAMES.get(rotation, str(rotation)), "D": D, "G": G, "bits": bits,
+        "vectors": N, "elements": n_el, "groups": N * (D // G),
+        "code_mismatch": n_code_bad, "scale_mismatch": n_scale_bad, "mismatch_frac": frac,
+        "code_mismatch_fp64": n_code_bad64, "scale_mismatch_fp64": n_scale_bad64, "mismatch_frac_fp64": frac64,
+    }
+    RECORDS.append(rec)
+
+    if rotation == O.IDENTITY:
+        assert n_scale_bad == 0, f"{n_scale_bad} scale mismatches with no rotation (must be bit-exact)"
+        band = identity_band(bits)
+        if n_code_bad:
+            assert np.all(code_dist[code_bad] <= band), (
+                f"{n_code_bad} code mismatches with no rotation, max boundary distance "
+                f"{code_dist[code_bad].max():.3e} > {band:.3e}")
     if n_scale_bad:
         assert np.all(scale_dist[scale_bad] <= BOUNDARY), (
             f"{n_scale_bad} scale mismatches, max boundary distance {scale_dist[scale_bad].max():.3e}")
-
-    qg = O.unpack_codes(codes_gpu, bits)
-    qr = O.unpack_codes(codes_ref, bits)
-    # groups with a GPU-specific scale: re-quantize with that scale
-    q_expect = qr.copy()
-    code_dist = code_dist_ref
-    if n_scale_bad:
-        q_alt = requantize(w, scales_gpu, G, bits)
-        bad_full = np.repeat(scale_bad, G, axis=-1)
-        q_expect = np.where(bad_full, q_alt, qr)
-        cd_alt, _ = O.boundary_distances(w, scales_gpu, G, bits)
-        code_dist = np.where(bad_full, cd_alt, code_dist_ref)
-    code_bad = qg != q_expect
-    n_code_bad = int(code_bad.sum())
     if n_code_bad:
         assert np.all(code_dist[code_bad] <= BOUNDARY), (
             f"{n_code_bad} code mismatches, max boundary distance {code_dist[code_bad].max():.3e}")
-    frac = (n_code_bad + n_scale_bad) / max(n_el, 1)
-    bar = FRACTION if bits == 4 else FRACTION8
+    if n_scale_bad64:
+        assert np.all(scale_dist64[scale_bad64] <= BOUNDARY), (
+            f"{n_scale_bad64} scale mismatches against the float64 decisions, max boundary distance "
+            f"{scale_dist64[scale_bad64].max():.3e}")
+    if n_code_bad64:
+        assert np.all(code_dist64[code_bad64] <= BOUNDARY), (
+            f"{n_code_bad64} code mismatches against the float64 decisions, max boundary distance "
+            f"{code_dist64[code_bad64].max():.3e}")
     if n_el >= 1_000_000:
         assert frac < bar, f"mismatch fraction {frac:.3e} >= {bar}"
+        assert frac64 < bar, f"mismatch fraction against the float64 decisions {frac64:.3e} >= {bar}"
     else:
         allowed = poisson_quantile(bar * n_el)
         assert n_code_bad + n_scale_bad <= allowed, (
             f"{n_code_bad + n_scale_bad} boundary mismatches in {n_el} elements (allowed {allowed})")
-    return {
-        "vectors": N, "elements": n_el,
-        "code_mismatch": n_code_bad, "scale_mismatch": n_scale_bad,
-        "code_mismatch_frac": n_code_bad / max(n_el, 1),
-        "scale_mismatch_frac_per_group": n_scale_bad / max(N * (D // G), 1),
-        "mismatch_frac": frac,
-        "w": w,
-    }
+    return dict(rec, code_mismatch_frac=n_code_bad / max(n_el, 1),
+                scale_mismatch_frac_per_group=n_scale_bad / max(N * (D // G), 1), w=w)
 
 
 def compare_rotation(w_gpu, x16, lam, rotation, signs, rel: float = 1e-5):

@@ -1,10 +1,10 @@
 """Synthetic quality study: reconstruction error of the quantized cache for
 the rotations and scaling schemes the pages compare.
 
-The pages report that SRFT and SRHT are statistically indistinguishable for
-KV quality (abstract), that per-token 4-bit scaling fails on models with
-outlier coordinates while per-channel plus per-group scaling recovers
-(explainer, "Methodik" 3), and describe the real-input DFT with its
+The abstract reports no measurable difference in KV quality between the
+SRFT and the SRHT; the pages also report that per-token 4-bit scaling fails
+on models with outlier coordinates while per-channel plus per-group scaling
+recovers (explainer, "Methodik" 3), and describe the real-input DFT with its
 Hermitian half spectrum unpacked to reals (explainer, "Methodik" 2).  Without
 models or evaluation text, this study measures what those choices do to the
 relative reconstruction error

@@ -161,6 +161,34 @@ def test_decode_and_rotate_validation():
     assert L.kvq_rotate(None, A, 1, 1, 4, 1024, 1024, 256, A, 0, A, None) == INVALID
 
 
+def test_decode_alignment_of_direct_loaded_rows():
+    """The D=128/256 decoders move lambda rows (and scale rows of 16 bytes
+    or more) with 16-byte direct loads: misaligned ones are refused on the
+    host, before anything is enqueued.  (No call here passes every check:
+    none reaches a launch.)"""
+    L = K.library()
+
+    def dec(plan, scales=A, lam=A, lsb=0):
+        # codes, scales, B, H, Tcap, t0, T, lam, lsb, y, dtype, y strides
+        return L.kvq_decode(plan.handle, A, scales, 2, 1, 8, 0, 4, lam, lsb, A, 0, 8 * plan.D, 8 * plan.D,
+                            plan.D, None)
+
+    for D, G in ((128, 32), (128, 16), (256, 32), (256, 16)):
+        p = K.Plan(D, G, "srft", 5)
+        assert dec(p, lam=A + 4) == ALIGN
+        assert b"lambda" in L.kvq_last_error()
+        assert dec(p, lsb=130) == ALIGN
+        assert b"lambda_sb" in L.kvq_last_error()
+        assert dec(p, scales=A + 2) == ALIGN
+    # 16-byte scale rows: an 8-byte offset is refused for decode and encode
+    for D, G in ((128, 16), (256, 32), (256, 16)):
+        p = K.Plan(D, G, "srft", 5)
+        assert dec(p, scales=A + 8) == ALIGN
+        assert b"scales" in L.kvq_last_error()
+        assert _encode(p, sb=4 * D, sh=2 * D, st=D, scales=A + 8) == ALIGN
+        assert b"scales" in K.library().kvq_last_error()
+
+
 def test_attention_validation():
     L = K.library()
     p = K.Plan(128, 32, "srft", 3)
@@ -225,6 +253,17 @@ def test_binding_refuses_host_tensors():
     kv = torch.zeros((1, 2, 8, 128), dtype=torch.float16)
     with pytest.raises(ValueError, match="host tensor"):
         K.attn_decode_f16(q, kv, kv, 8, 0.1, out, ws)
+    # a batched lambda must have 1 or B rows (others would be read past its end)
+    x3 = torch.zeros((3, 2, 4, 128), dtype=torch.float16)
+    c3 = torch.zeros((3, 2, 8, 64), dtype=torch.uint8)
+    s3 = torch.zeros((3, 2, 8, 4), dtype=torch.float16)
+    lam2 = torch.ones((2, 2, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="lambda must be"):
+        K.encode(p, x3, lam2, c3, s3)
+    with pytest.raises(ValueError, match="lambda must be"):
+        K.decode(p, c3, s3, lam2, torch.zeros((3, 2, 8, 128), dtype=torch.float16))
+    with pytest.raises(ValueError, match="lambda must be"):
+        K.rotate(p, x3, lam2, torch.zeros((3, 2, 4, 128), dtype=torch.float32))
     # shapes that do not match the plan are refused first
     with pytest.raises(ValueError, match="codes must be"):
         K.attn_decode(p, q, codes[..., :32], scales, lam, codes, scales, lam, 8, 0.1, out, ws)

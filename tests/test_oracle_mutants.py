@@ -64,7 +64,9 @@ def _inv_no_signs(y, rotation, signs):
 
 def _quant_factory(div=7.0, half_away=False, lo=-8, hi=7, strided=False, div8=127.0, lo8=-128, hi8=127,
                    half_away8=False, g16_as_32=False):
-    def q(w, G=K.GROUP, bits=4):
+    def q(w, G=K.GROUP, bits=4, decide="fp32"):
+        if decide != "fp32":
+            return _orig["quantize_groups"](w, G, bits, decide)
         if bits == 8:
             d, l, h, away = div8, lo8, hi8, half_away8
         else:
@@ -88,6 +90,16 @@ def _quant_factory(div=7.0, half_away=False, lo=-8, hi=7, strided=False, div8=12
             qq = np.swapaxes(qq, -1, -2)
         return qq.reshape(w32.shape).astype(np.int8), scale
     return q
+
+
+def _fp16_quotient_via_fp32(a, d):
+    """The quotient taken in float32 first (the DP decision) instead of once."""
+    return (np.asarray(a, dtype=np.float64).astype(np.float32) / np.float32(d)).astype(np.float16)
+
+
+def _rint_quotient_half_up(w, s):
+    """floor(w / s + 1/2): ties rounded up instead of to even."""
+    return np.floor(w / s + 0.5)
 
 
 def _pack_codes_offset8(q, bits=4):
@@ -185,6 +197,8 @@ MUTANTS = {
     "int8-offset-binary": ("pack_codes", _pack_codes_offset8),
     "int8-unpack-unsigned": ("unpack_codes", _unpack_codes_unsigned8),
     "signs-bit-order": ("plan_signs", _signs_msb_first),
+    "fp64-scale-via-fp32": ("fp16_of_quotient", _fp16_quotient_via_fp32),
+    "fp64-code-half-up": ("rint_of_quotient", _rint_quotient_half_up),
 }
 
 CHECKS = [
@@ -214,6 +228,9 @@ CHECKS = [
     P.check_compression_variants,
     P.check_attention_bruteforce_int8,
     P.check_srft_mixed_radix,
+    P.check_fp16_quotient_exact,
+    P.check_rint_quotient_exact,
+    P.check_fp64_decisions_construction,
 ]
 
 

@@ -517,6 +517,154 @@ def test_compression_matches_printed_figure():
     check_compression_figure()
 
 
+# ------------------------------------- decisions in float64 (one rounding) --
+# The plain definition of the quantizer rounds each exact quotient once:
+# scale = fp16_RNE(a / qmax), code = rint_half_even(w / scale).  The pins
+# below compute those roundings in exact rational arithmetic on the fp16
+# grid and on the integers, and construct the inputs where a float64 or
+# float32 intermediate would round twice.
+
+def _fp16_round_exact(fr: Fraction) -> Fraction:
+    """The fp16 value nearest a non-negative rational, ties to even
+    (subnormal spacing 2^-24 below 2^-14)."""
+    if fr == 0:
+        return Fraction(0)
+    e = fr.numerator.bit_length() - fr.denominator.bit_length()
+    if Fraction(2) ** e > fr:
+        e -= 1
+    e = max(e, -14)
+    ulp = Fraction(2) ** (e - 10)
+    k = fr / ulp
+    n = math.floor(k)
+    rem = k - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n * ulp
+
+
+def _rint_exact(fr: Fraction) -> int:
+    n = math.floor(fr)
+    rem = fr - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n
+
+
+def _fp16_midpoint_cases():
+    """Abs-max values a whose quotient a / qmax sits exactly on, or within
+    2^-30 (relative) of, an fp16 rounding midpoint: below, on and above it,
+    at both parities of the lower neighbour, normal and subnormal."""
+    out = []
+    for lo_bits in (0x3C00, 0x3C01, 0x4A3F, 0x4A40, 0x0200, 0x0201, 0x1C00, 0x1C01):
+        lo = Fraction(float(np.array(lo_bits, dtype=np.uint16).view(np.float16)))
+        hi = Fraction(float(np.array(lo_bits + 1, dtype=np.uint16).view(np.float16)))
+        mid = (lo + hi) / 2
+        for qmax in (7, 127):
+            for rel in (Fraction(-1, 2 ** 30), Fraction(0), Fraction(1, 2 ** 30)):
+                a = float(mid * qmax * (1 + rel))        # rounded to float64
+                out.append((a, qmax))
+    return out
+
+
+def check_fp16_quotient_exact():
+    rng = _rng(17)
+    cases = _fp16_midpoint_cases()
+    for a in np.abs(rng.standard_normal(3000) * np.exp(3 * rng.standard_normal(3000))):
+        a = min(float(a), 60000.0)
+        cases.append((float(a), 7))
+        cases.append((float(a), 127))
+    n_double = 0
+    for a, qmax in cases:
+        want = _fp16_round_exact(Fraction(a) / qmax)
+        got = O.fp16_of_quotient(np.array([a]), qmax)[0]
+        assert Fraction(float(got)) == want, (a, qmax, float(got), float(want))
+        # the float32 route rounds twice: it differs on some constructed case
+        via32 = (np.float32(a) / np.float32(qmax)).astype(np.float16)
+        n_double += Fraction(float(via32)) != want
+    assert n_double > 0
+
+
+def check_rint_quotient_exact():
+    """Ties, values 2^-45 either side of them, and the float64 neighbours of
+    exact ties."""
+    cases = []
+    for s in (1.0, 0.0137, 0.3, 3.75, 5.9, 2.0 ** -20):
+        s16 = float(np.float16(s))
+        for k in range(-9, 9):
+            t = (k + 0.5) * s16                       # exact in float64
+            for rel in (-(2.0 ** -45), 0.0, 2.0 ** -45):
+                cases.append((t * (1 + rel), s16))
+            cases.append((float(np.nextafter(t, np.inf)), s16))
+            cases.append((float(np.nextafter(t, -np.inf)), s16))
+            cases.append((k * s16, s16))
+    for w, s in cases:
+        want = _rint_exact(Fraction(w) / Fraction(s))
+        got = O.rint_of_quotient(np.array([w]), np.array([s]))[0]
+        assert got == want, (w, s, got, want)
+
+
+def check_float64_quotients_never_land_on_boundaries():
+    """The fact behind the float64 decisions: near every fp16 rounding
+    midpoint m (within 40 float64 steps of m d) the float64 quotient a / d
+    equals m only when a = m d; near every half-integer multiple of every
+    fp16 value the quotient w / s is that half-integer only when w is the
+    multiple."""
+    b = np.arange(1, 0x7BFF, dtype=np.uint16)
+    lo = b.view(np.float16).astype(np.float64)
+    hi = (b + 1).view(np.float16).astype(np.float64)
+    mid = (lo + hi) / 2
+    for d in (7.0, 127.0):
+        t = mid * d
+        for k in range(-40, 41):
+            a = t + k * np.spacing(t)
+            assert not np.any((a / d == mid) & (a != t))
+    for h in np.arange(-8, 8) + 0.5:
+        t = h * lo
+        for k in range(-4, 5):
+            w = t + k * np.spacing(t)
+            assert not np.any((w / lo == h) & (w != t))
+
+
+def check_fp64_decisions_construction():
+    """quantize_groups(decide="fp64"): exact-grid groups give the scale and
+    codes back; a group whose abs-max quotient is 2^-30 above an fp16
+    midpoint rounds up where the float32 decision (DP) rounds to even."""
+    rng = _rng(5)
+    D, G = 64, 32
+    k = rng.integers(-7, 8, D)
+    k[0], k[40] = 7, -7
+    sigma = np.float16(0.8125)
+    w = k * float(sigma)
+    q64, s64 = O.quantize_groups(w[None], G, 4, decide="fp64")
+    assert np.all(s64 == sigma) and np.array_equal(q64[0], k.astype(np.int8))
+    # abs-max 7 m (1 + 2^-30), m the midpoint of 1 and 1 + 2^-10 (1 is even)
+    m = 1 + 2.0 ** -11
+    w2 = np.zeros(G)
+    w2[0] = 7 * m * (1 + 2.0 ** -30)
+    w2[1] = 2.5 * (1 + 2.0 ** -10)                   # a code exactly at a tie with the upper scale
+    _, s_dp = O.quantize_groups(w2[None], G, 4)
+    q_64, s_64 = O.quantize_groups(w2[None], G, 4, decide="fp64")
+    assert float(s_dp[0, 0]) == 1.0
+    assert Fraction(float(s_64[0, 0])) == 1 + Fraction(1, 2 ** 10)
+    assert q_64[0, 0] == 7 and q_64[0, 1] == 2       # 2.5 -> 2 (even)
+
+
+def test_fp16_of_quotient_single_rounding():
+    check_fp16_quotient_exact()
+
+
+def test_rint_of_quotient_half_even_exact():
+    check_rint_quotient_exact()
+
+
+def test_fp64_decision_quantizer_construction():
+    check_fp64_decisions_construction()
+
+
+def test_float64_quotients_never_land_on_boundaries():
+    check_float64_quotients_never_land_on_boundaries()
+
+
 # ------------------------------------------------------------ boundaries ---
 
 def test_boundary_distances_on_constructed_values():
