@@ -184,6 +184,23 @@ kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q,
                            float sm_scale, void* out, kvq_dtype out_dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode-step attention that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Arguments, checks
+ * and results are those of kvq_attn_decode without the workspace.  The
+ * split-K partial results go to a buffer the library keeps in device memory,
+ * 16 MiB on each GPU it runs on (held until the process ends).  A call whose
+ * partials need more (about B * Hq * splits * (D + 2) * 4 bytes, splits <=
+ * 16 at the decode-step shapes) returns KVQ_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on one GPU shares that GPU's buffer: calls that
+ * overlap on one GPU (on different streams or threads) race, and the caller
+ * must order them. */
+kvq_status kvq_attn_decode_noalloc(const kvq_plan* plan, const uint16_t* q,
+                                   const uint8_t* k_codes, const uint16_t* k_scales, const float* lambda_k,
+                                   const uint8_t* v_codes, const uint16_t* v_scales, const float* lambda_v,
+                                   int64_t B, int64_t Hq, int64_t Hkv, int64_t Tcap, int64_t seq_len,
+                                   float sm_scale, void* out, kvq_dtype out_dtype, void* stream);
+
 /* The same attention over an unquantized fp16 cache k, v [B, Hkv, Tcap, D]
  * (dense): the fp16 comparator the pages measure the int4 cache against. */
 kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -19,7 +19,7 @@ import os
 __all__ = [
     "KvqError", "Plan", "SRFT", "SRHT", "IDENTITY", "GROUP",
     "library", "library_path", "encode", "decode", "rotate",
-    "attn_workspace_size", "attn_decode", "attn_decode_f16",
+    "attn_workspace_size", "attn_decode", "attn_decode_noalloc", "attn_decode_f16",
     "cache_shapes",
 ]
 
@@ -78,6 +78,8 @@ def library() -> ctypes.CDLL:
         "kvq_attn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            _i64, _i64, _i64, _i64, _i64, _f32, _vp, ctypes.c_int,
                                            _vp, _sz, _vp]),
+        "kvq_attn_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                   _i64, _i64, _i64, _i64, _i64, _f32, _vp, ctypes.c_int, _vp]),
         "kvq_attn_decode_f16": (ctypes.c_int, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
                                                _vp, ctypes.c_int, _vp, _sz, _vp]),
     }
@@ -291,6 +293,21 @@ def attn_decode(plan: Plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_
                _ptr(v_codes), _ptr(v_scales), _ptr(lam_v), B, Hq, Hkv, Tcap, seq_len,
                float(sm_scale), _ptr(out), dt, _ptr(workspace),
                workspace.numel() * workspace.element_size(), _stream(idx)))
+
+
+def attn_decode_noalloc(plan: Plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, seq_len: int,
+                        sm_scale: float, out):
+    """attn_decode with no workspace: the partials go to the library's
+    per-GPU buffer (calls that overlap on one GPU race)."""
+    import torch
+    _attn_checks(plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out)
+    B, Hq, D = q.shape
+    Hkv, Tcap = k_codes.shape[1], k_codes.shape[2]
+    dt = {torch.float16: _F16, torch.float32: _F32}[out.dtype]
+    idx = _device(q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out)
+    _check(_on(idx, library().kvq_attn_decode_noalloc, plan.handle, _ptr(q), _ptr(k_codes), _ptr(k_scales),
+               _ptr(lam_k), _ptr(v_codes), _ptr(v_scales), _ptr(lam_v), B, Hq, Hkv, Tcap, seq_len,
+               float(sm_scale), _ptr(out), dt, _stream(idx)))
 
 
 def attn_decode_f16(q, k, v, seq_len: int, sm_scale: float, out, workspace):

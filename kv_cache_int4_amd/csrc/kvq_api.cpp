@@ -432,6 +432,36 @@ kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q, const uint8_
   }
 }
 
+kvq_status kvq_attn_decode_noalloc(const kvq_plan* plan, const uint16_t* q, const uint8_t* k_codes,
+                                   const uint16_t* k_scales, const float* lambda_k, const uint8_t* v_codes,
+                                   const uint16_t* v_scales, const float* lambda_v, int64_t B, int64_t Hq,
+                                   int64_t Hkv, int64_t Tcap, int64_t seq_len, float sm_scale, void* out,
+                                   kvq_dtype out_dtype, void* stream) {
+  try {
+    if (kvq_status s = check_plan(plan)) return s;
+    if (kvq_status s = check_attn_plan(plan)) return s;
+    // the workspace checks of the common validation are replaced by the
+    // size check against the per-GPU buffer below
+    if (kvq_status s = check_attn_common(plan->D, q, B, Hq, Hkv, Tcap, seq_len, out, out_dtype, nullptr, 0,
+                                         /*check_workspace=*/false))
+      return s;
+    if (kvq_status s = check_attn_cache(k_codes, k_scales, lambda_k, v_codes, v_scales, lambda_v)) return s;
+    if (B == 0 || Hq == 0) return ok();
+    kvq::AttnDesc d = attn_desc(plan, q, k_codes, k_scales, lambda_k, v_codes, v_scales, lambda_v, B, Hq, Hkv,
+                                Tcap, seq_len, sm_scale, out, out_dtype, nullptr, stream);
+    const size_t need = kvq::attn_workspace_needed(d);
+    if (need > kvq::kAttnScratchBytes)
+      return fail(KVQ_ERR_WORKSPACE, "the call needs %zu bytes of split-K partials; the per-GPU buffer holds %zu",
+                  need, kvq::kAttnScratchBytes);
+    void* ws = nullptr;
+    if (kvq_status s = hip_status(kvq::attn_scratch(&ws), "kvq_attn_decode_noalloc buffer address")) return s;
+    d.workspace = ws;
+    return hip_status(kvq::launch_attention(d), "kvq_attn_decode_noalloc launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INVALID, "internal error");
+  }
+}
+
 kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                                int64_t Hq, int64_t Hkv, int64_t Tcap, int64_t seq_len, float sm_scale, void* out,
                                kvq_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {

@@ -73,5 +73,10 @@ size_t attn_workspace_bytes(int D, int64_t B, int64_t Hq, int64_t seq_len);
 size_t attn_workspace_needed(const AttnDesc& d);
 hipError_t launch_attention(const AttnDesc& d);
 
+// Size of the per-GPU buffer that stands in for the workspace of
+// kvq_attn_decode_noalloc, and its device address on the current device
+// (looked up once per device).
+constexpr size_t kAttnScratchBytes = static_cast<size_t>(16) << 20;
+hipError_t attn_scratch(void** ptr);
 
 }  // namespace kvq

@@ -223,6 +223,26 @@ def test_attention_validation():
     assert L.kvq_attn_decode_f16(128, A, None, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need, None) == INVALID
 
 
+def test_noalloc_attention_validation():
+    """kvq_attn_decode_noalloc runs the checks of kvq_attn_decode, and refuses
+    a call whose partials exceed its per-GPU buffer, on the host (fake
+    pointers: nothing here reaches a launch)."""
+    L = K.library()
+    p = K.Plan(128, 32, "srft", 3)
+
+    def call(B=64, Hq=8, Hkv=2, Tcap=33024, L_=32769, kc=A, q=A):
+        return L.kvq_attn_decode_noalloc(p.handle, q, kc, A, A, A, A, A, B, Hq, Hkv, Tcap, L_, 0.088, A, 0, None)
+
+    assert call(Hq=6, Hkv=4) == INVALID
+    assert call(L_=0) == INVALID
+    assert call(kc=A + 4) == ALIGN
+    assert call(q=None) == INVALID
+    assert call(B=0) == OK
+    assert L.kvq_attn_decode_noalloc(None, A, A, A, A, A, A, A, 1, 1, 1, 8, 4, 0.1, A, 0, None) == INVALID
+    assert call(B=4096, Hq=32, Hkv=8, Tcap=300, L_=256) == WORKSPACE
+    assert b"per-GPU buffer" in L.kvq_last_error()
+
+
 def test_workspace_size_monotone():
     a = K.attn_workspace_size(128, 2, 8, 100)
     b = K.attn_workspace_size(128, 2, 8, 100000)
