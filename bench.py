@@ -71,6 +71,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bulk", action="store_true", help="skip the Mistral-shaped bulk leg (39 GB of HBM)")
     ap.add_argument("--sets", type=int, default=4, help="prefix batches rotated over")
     ap.add_argument("--profile-marks", action="store_true",
                     help="bracket the timed steps with marker kernels and add a calibration copy "
@@ -146,13 +147,37 @@ def trace_summary(path: str) -> str:
     return "\n".join(out)
 
 
+def host_info() -> dict:
+    """CPU model and core counts of the host the oracle runs on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "cpus_allowed": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
 def cpu_baseline(n_vec: int = 458752):
-    """The CPU oracle as it stands on the Qwen prefix workload (by default all
-    458,752 vectors of one step's encode and decode, about 10 s of
-    single-threaded numpy)."""
+    """The CPU oracle as it stands, pinned to one host core (numpy with one
+    BLAS/OpenMP thread; pocketfft is single-threaded): encode and decode of
+    the Qwen prefix workload (by default all 458,752 vectors of one step),
+    and the decode-step attention over the int4 cache for one sequence of
+    the batch of 64 (D=128, 8 query heads over 2 KV heads, 32769 tokens),
+    extrapolated to the batch.  About 5-10 s of work."""
     import numpy as np
     import oracle as O
     from kv_cache_int4_amd import workloads as W
+    host = host_info()
+    pinned = None
+    if hasattr(os, "sched_setaffinity"):
+        allowed = sorted(os.sched_getaffinity(0))
+        pinned = allowed[0]
+        os.sched_setaffinity(0, {pinned})
     cfg = W.CONFIGS["qwen"]
     T = 4096
     nb = min(cfg.B, max(1, -(-n_vec // (cfg.H * T))))
@@ -165,14 +190,146 @@ def cpu_baseline(n_vec: int = 458752):
     t1 = time.perf_counter()
     O.decode(codes, scales, lv, O.SRFT, signs)
     t2 = time.perf_counter()
+    # decode-step attention, one sequence: its K and V caches encoded by the
+    # oracle, then attention over all 32769 tokens (timed), times 64
+    dc = W.CONFIGS["decode"]
+    L = dc.T + 1
+    k16, v16, lam_k, lam_v, q = W.decode_inputs(1, dc.H, dc.Hq, L, dc.D, dc.data_seed)
+    ks = O.plan_signs(dc.D, O.SRFT, dc.sign_seed)
+    kc, ksc, _ = O.encode(k16.numpy(), lam_k.numpy()[None, :, None, :], O.SRFT, ks)
+    vc, vsc, _ = O.encode(v16.numpy(), lam_v.numpy()[None, :, None, :], O.SRFT, ks)
+    t3 = time.perf_counter()
+    O.attention_int4(q.numpy(), kc, ksc, lam_k.numpy(), vc, vsc, lam_v.numpy(), L, 1 / math.sqrt(dc.D), O.SRFT,
+                     ks)
+    t4 = time.perf_counter()
+    if pinned is not None:
+        os.sched_setaffinity(0, set(allowed))
     return {
         "value": n_vec / (t1 - t0) / 1e6,
         "unit": "Mvec/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{n_vec} vectors of the Qwen2.5-1.5B prefix workload (D=128, SRFT), "
-                  f"numpy float64 oracle; encode {(t1 - t0):.2f} s, decode {(t2 - t1):.2f} s",
+        "sample": f"{n_vec} vectors of the Qwen2.5-1.5B prefix workload (D=128, SRFT), numpy float64 oracle "
+                  f"pinned to host core {pinned}: encode {(t1 - t0):.2f} s, decode {(t2 - t1):.2f} s; "
+                  f"decode-step attention over the int4 cache for 1 of the 64 sequences "
+                  f"({(t4 - t3):.2f} s), times 64",
         "decode_Mvec_s": n_vec / (t2 - t1) / 1e6,
+        "attn_us_per_step_extrapolated": round((t4 - t3) * 64 * 1e6, 1),
+        "host": host,
+    }
+
+
+def timed_loop(torch, stream, fn, n, warm=3):
+    """Microseconds per call of fn(i) over n back-to-back calls, with HIP
+    events on the kernels' stream."""
+    for i in range(warm):
+        fn(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def small_leg(K, W, torch, stream, dev, n):
+    """The single-K-tensor round trip (2 KV heads x 256 tokens, D=128, 512
+    vectors): launch-latency bound, reported as microseconds per call."""
+    cfg = W.CONFIGS["small"]
+    x, lam = W.prefix_inputs(cfg, dev)
+    plan = K.Plan(cfg.D, 32, "srft", cfg.sign_seed)
+    B, H, T, D = x.shape
+    codes = torch.empty((B, H, T, D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((B, H, T, D // 32), dtype=torch.float16, device=dev)
+    y = torch.empty_like(x)
+    enc = timed_loop(torch, stream, lambda i: K.encode(plan, x, lam, codes, scales), n)
+    dec = timed_loop(torch, stream, lambda i: K.decode(plan, codes, scales, lam, y), n)
+    rt = timed_loop(torch, stream, lambda i: (K.encode(plan, x, lam, codes, scales),
+                                              K.decode(plan, codes, scales, lam, y)), n)
+    return {"workload": "single K tensor, 2 KV heads x 256 tokens, D=128, SRFT (512 vectors)",
+            "encode_us": round(enc, 2), "decode_us": round(dec, 2), "round_trip_us": round(rt, 2)}
+
+
+def mistral_leg(K, W, torch, stream, dev, n_rep):
+    """The Mistral-7B-shaped bulk path: 64 full-size calls (32 layers x {K,V};
+    each B=16, H=8, T=8192, D=128, Student-t(3) values: 1,048,576 vectors and
+    268 MB of fp16 per call, 17.2 GB in all), encoded into 64 caches, then the
+    whole cache decoded back to fp16 with 64 calls.  Each pass of 64 calls is
+    timed with HIP events, n_rep times; the caches and outputs (39 GB in all)
+    stay in HBM."""
+    cfg = W.CONFIGS["mistral"]
+    D, B, H, T = cfg.D, cfg.B, cfg.H, cfg.T
+    plan = K.Plan(D, 32, "srft", cfg.sign_seed)
+    xs, lams, cs, ss, ys = [], [], [], [], []
+    for call in range(64):
+        layer, kv = divmod(call, 2)
+        # the batch of 16 sequences as 16 x 8 heads of the law, seeded per call
+        xs.append(W.student_t3(B * H, T, D, cfg.data_seed, dev, layer, kv).view(B, H, T, D))
+        lams.append(W.lognormal_lambda((H, D), cfg.lambda_seed, dev, 0.3, layer, kv))
+        cs.append(torch.empty((B, H, T, D // 2), dtype=torch.uint8, device=dev))
+        ss.append(torch.empty((B, H, T, D // 32), dtype=torch.float16, device=dev))
+        ys.append(torch.empty((B, H, T, D), dtype=torch.float16, device=dev))
+    torch.cuda.synchronize()
+    nvec = 64 * B * H * T
+    nbytes = nvec * (2 * D + D // 2 + 2 * (D // 32))
+
+    def enc_all(_):
+        for c in range(64):
+            K.encode(plan, xs[c], lams[c], cs[c], ss[c])
+
+    def dec_all(_):
+        for c in range(64):
+            K.decode(plan, cs[c], ss[c], lams[c], ys[c])
+
+    enc = timed_loop(torch, stream, enc_all, n_rep, warm=1)
+    dec = timed_loop(torch, stream, dec_all, n_rep, warm=1)
+    res = {
+        "workload": "Mistral-7B-shaped bulk path: 64 calls (32 layers x {K,V}) of B=16, H=8, T=8192, D=128, "
+                    "Student-t(3), SRFT, group 32; encode all, then decode the whole cache",
+        "vectors": nvec, "bytes_per_pass": nbytes,
+        "encode_ms_per_64_calls": round(enc / 1e3, 4), "encode_frac_hbm": round(nbytes / enc / 1e3 / HBM_PEAK_GBS, 4),
+        "encode_Gvec_s": round(nvec / enc / 1e3, 2),
+        "decode_ms_per_64_calls": round(dec / 1e3, 4), "decode_frac_hbm": round(nbytes / dec / 1e3 / HBM_PEAK_GBS, 4),
+        "decode_Gvec_s": round(nvec / dec / 1e3, 2),
+    }
+    del xs, cs, ss, ys
+    torch.cuda.synchronize()
+    return res
+
+
+def attn256_leg(K, W, torch, stream, dev, n):
+    """The decode step at Gemma-3 1B's head shape: batch 64, 4 query heads
+    over 1 KV head, D=256, 32768 cached tokens; append one token (K and V in
+    one call over the stacked [2B, 1, Tcap] caches), then int4 attention over
+    32769 tokens, against the same attention over the fp16 cache."""
+    dc = W.CONFIGS["decode256"]
+    B, Hkv, Hq, D, T0 = dc.B, dc.H, dc.Hq, dc.D, dc.T
+    L, Tcap = T0 + 1, T0 + 256
+    plan = K.Plan(D, 32, "srft", dc.sign_seed)
+    k16, v16, lam_k, lam_v, q = W.decode_inputs(B, Hkv, Hq, Tcap, D, dc.data_seed, dev)
+    kvc = torch.empty((2 * B, Hkv, Tcap, D // 2), dtype=torch.uint8, device=dev)
+    kvs = torch.empty((2 * B, Hkv, Tcap, D // 32), dtype=torch.float16, device=dev)
+    K.encode(plan, k16[:, :, :T0], lam_k, kvc[:B], kvs[:B], 0)
+    K.encode(plan, v16[:, :, :T0], lam_v, kvc[B:], kvs[B:], 0)
+    kv_new = torch.cat([k16[:, :, T0:T0 + 1], v16[:, :, T0:T0 + 1]]).contiguous()
+    lam_kv = torch.cat([lam_k.expand(B, Hkv, D), lam_v.expand(B, Hkv, D)]).contiguous()
+    ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    sm = 1.0 / math.sqrt(D)
+    app = timed_loop(torch, stream, lambda i: K.encode(plan, kv_new, lam_kv, kvc, kvs, T0), n)
+    att = timed_loop(torch, stream, lambda i: K.attn_decode(plan, q, kvc[:B], kvs[:B], lam_k, kvc[B:], kvs[B:],
+                                                            lam_v, L, sm, out, ws), n)
+    f16 = timed_loop(torch, stream, lambda i: K.attn_decode_f16(q, k16, v16, L, sm, out, ws), max(5, n // 2))
+    ab = B * Hkv * L * 2 * (D // 2 + 2 * (D // 32))
+    fb = B * Hkv * L * 2 * 2 * D
+    return {
+        "workload": "decode step at Gemma-3-1B head shape: batch 64, Hq 4 / Hkv 1, D=256, 32768 cached tokens + 1 "
+                    "appended, SRFT, group 32",
+        "append_us": round(app, 2), "int4_attn_us": round(att, 2), "int4_us_per_step": round(app + att, 2),
+        "int4_attn_bytes": ab, "int4_attn_frac_hbm": round(ab / att / 1e3 / HBM_PEAK_GBS, 4),
+        "fp16_us_per_step": round(f16, 2), "fp16_frac_hbm": round(fb / f16 / 1e3 / HBM_PEAK_GBS, 4),
+        "int4_over_fp16": round((app + att) / f16, 4),
     }
 
 
@@ -498,6 +655,14 @@ def main():
     fmts = formats_leg(K, torch, stream, cfg, sets, dc, k16, v16, lam_k, lam_v, q, L, sm, max(10, args.steps))
     # ---- D=96 and D=80 (mixed-radix SRFT), timed apart ----
     mixed = mixed_leg(K, W, torch, stream, dev, args.sets, max(10, args.steps))
+    # ---- D=256 decode step (Gemma-3 1B head shape), timed apart ----
+    att256 = attn256_leg(K, W, torch, stream, dev, max(10, args.steps))
+    # ---- the 512-vector round trip (latency) ----
+    small = small_leg(K, W, torch, stream, dev, max(20, args.steps))
+    # ---- Mistral-7B-shaped bulk encode and full-cache decode ----
+    del sets
+    torch.cuda.empty_cache()
+    mistral = None if args.no_bulk else mistral_leg(K, W, torch, stream, dev, 3)
     if args.profile_marks:
         src = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -580,8 +745,11 @@ def main():
                       "int4_over_fp16": round(attn_us / f16_us, 4),
                       "graph_us_per_step": round(graph_us, 2)},
         "d256": gemma,
+        "attention_d256": att256,
         "formats": fmts,
         "mixed_radix": mixed,
+        "small_round_trip": small,
+        "mistral_bulk": mistral,
     }
     print(json.dumps(res), flush=True)
 

@@ -133,38 +133,52 @@ kvq_status kvq_plan_info_ex(const kvq_plan* plan, int32_t* D, int32_t* G, int32_
  * [H,D] table across the batch), quantize per group and write token t0 + t of
  *   codes  uint8 [B, H, Tcap, D*bits/8]  (dense, 16-byte aligned; D/2 bytes
  *                                         for int4)
- *   scales fp16  [B, H, Tcap, D/G]       (dense, 8-byte aligned).
- * Requires 0 <= t0, t0 + T <= Tcap.  B, H or T of 0 is a no-op. */
+ *   scales fp16  [B, H, Tcap, D/G]       (dense; 16-byte aligned at D = 256
+ *                                         and at D = 128 with G = 16, else
+ *                                         8-byte aligned).
+ * Requires 0 <= t0, t0 + T <= Tcap.  B, H or T of 0 is a no-op.  The caller
+ * owns every buffer; nothing is allocated or synchronized. */
 kvq_status kvq_encode(const kvq_plan* plan, const uint16_t* x, int64_t B, int64_t H, int64_t T,
                       int64_t x_sb, int64_t x_sh, int64_t x_st,
                       const float* lambda, int64_t lambda_sb,
                       uint8_t* codes, uint16_t* scales, int64_t Tcap, int64_t t0,
                       void* stream);
 
-/* Decode (the inverse of kvq_encode up to quantization): for tokens
+/* Decode, the read side of [M1]/[M2] (the inverse of kvq_encode up to
+ * quantization; R is orthogonal, so its inverse is R^T [M1]): for tokens
  * t0 .. t0+T-1 of codes/scales [B,H,Tcap,...] compute
  *   x^[j] = (R^T ( (q . scale) / lambda ))[j]
  * and write it to y (fp16 rounded to nearest even, or fp32) at
- * y + b*y_sb + h*y_sh + t*y_st + j; fp16 rows must be 16-byte aligned. */
+ * y + b*y_sb + h*y_sh + t*y_st + j; fp16 rows must be 16-byte aligned, fp32
+ * rows 8-byte aligned.  At D = 128 and 256 lambda must be 16-byte aligned
+ * with lambda_sb a multiple of 4, and scales aligned as for kvq_encode.
+ * Requires 0 <= t0, t0 + T <= Tcap; B, H or T of 0 is a no-op. */
 kvq_status kvq_decode(const kvq_plan* plan, const uint8_t* codes, const uint16_t* scales,
                       int64_t B, int64_t H, int64_t Tcap, int64_t t0, int64_t T,
                       const float* lambda, int64_t lambda_sb,
                       void* y, kvq_dtype y_dtype, int64_t y_sb, int64_t y_sh, int64_t y_st,
                       void* stream);
 
-/* Rotate only (test hook sharing the encoder's transform): w[b,h,t,:] =
- * lambda . (R x[b,h,t,:]) in fp32, w dense [B, H, T, D]. */
+/* Rotate only, [M1] followed by the lambda rescale of [M2] (a test hook
+ * running the encoder's own transform): w[b,h,t,:] = lambda . (R x[b,h,t,:])
+ * in fp32, w dense [B, H, T, D] and 16-byte aligned; x and lambda as for
+ * kvq_encode. */
 kvq_status kvq_rotate(const kvq_plan* plan, const uint16_t* x, int64_t B, int64_t H, int64_t T,
                       int64_t x_sb, int64_t x_sh, int64_t x_st,
                       const float* lambda, int64_t lambda_sb, float* w, void* stream);
 
 /* Bytes of device workspace kvq_attn_decode and kvq_attn_decode_f16 need for
- * this shape (split-K partial results). */
+ * this shape: the split-K partial results of the decode-step attention
+ * (the pages give no workspace; it is this library's split of the read
+ * across the GPU).  D = 128 or 256, else KVQ_ERR_UNSUPPORTED.  The size
+ * covers any split count a call with this seq_len may use; the workspace
+ * is caller-owned and may be reused across calls in stream order. */
 kvq_status kvq_attn_workspace_size(int32_t D, int64_t B, int64_t Hq, int64_t seq_len,
                                    size_t* bytes);
 
 /* Decode-step attention over the int4 cache (the read path fused with
- * attention; the pages time it only end to end [abstract]): for each batch b
+ * attention; the abstract reports its decode latency against fp16 on
+ * Gemma-3 1B, head size 256, and Qwen2.5-1.5B, head size 128): for each batch b
  * and query head h, with kv head g = h / (Hq / Hkv),
  *   out[b,h,:] = sum_t softmax_t(sm_scale q[b,h,:] . k^[b,g,t,:]) v^[b,g,t,:]
  * over t < seq_len, where k^ and v^ are the decoded cache rows
@@ -174,9 +188,10 @@ kvq_status kvq_attn_workspace_size(int32_t D, int64_t B, int64_t Hq, int64_t seq
  * rotated basis (q . k^ = ((R q) / lambda_k) . (lambda_k R k^)) and the
  * value average is rotated back once per head.  Requires Hq % Hkv == 0,
  * 1 <= seq_len <= Tcap, and a workspace of kvq_attn_workspace_size bytes.
- * Built for D = 128, every code width and group size of the plan (codes
- * [B, Hkv, Tcap, D*bits/8], scales [B, Hkv, Tcap, D/G]); a D = 256 plan
- * returns KVQ_ERR_UNSUPPORTED. */
+ * Built for D = 128 and 256, every rotation, code width and group size of
+ * the plan (codes [B, Hkv, Tcap, D*bits/8] 16-byte aligned, scales
+ * [B, Hkv, Tcap, D/G] 8-byte aligned, lambda 16-byte aligned); plans at D =
+ * 96 or 80 return KVQ_ERR_UNSUPPORTED. */
 kvq_status kvq_attn_decode(const kvq_plan* plan, const uint16_t* q,
                            const uint8_t* k_codes, const uint16_t* k_scales, const float* lambda_k,
                            const uint8_t* v_codes, const uint16_t* v_scales, const float* lambda_v,
@@ -202,7 +217,9 @@ kvq_status kvq_attn_decode_noalloc(const kvq_plan* plan, const uint16_t* q,
                                    float sm_scale, void* out, kvq_dtype out_dtype, void* stream);
 
 /* The same attention over an unquantized fp16 cache k, v [B, Hkv, Tcap, D]
- * (dense): the fp16 comparator the pages measure the int4 cache against. */
+ * (dense, 16-byte aligned): the fp16 cache the abstract compares the int4
+ * cache with.  Takes the head size D (128 or 256) instead of a plan, since
+ * no quantizer is involved; otherwise as kvq_attn_decode. */
 kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                int64_t B, int64_t Hq, int64_t Hkv, int64_t Tcap, int64_t seq_len,
                                float sm_scale, void* out, kvq_dtype out_dtype,

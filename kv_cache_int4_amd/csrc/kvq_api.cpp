@@ -372,7 +372,8 @@ kvq_status check_attn_common(int32_t D, const uint16_t* q, int64_t B, int64_t Hq
 }
 
 kvq_status check_attn_plan(const kvq_plan* plan) {
-  if (plan->D != 128) return fail(KVQ_ERR_UNSUPPORTED, "attention is built for D=128 (plan D=%d)", plan->D);
+  if (plan->D != 128 && plan->D != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "attention is built for D=128 and 256 (plan D=%d)", plan->D);
   return KVQ_OK;
 }
 
@@ -466,7 +467,7 @@ kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, 
                                int64_t Hq, int64_t Hkv, int64_t Tcap, int64_t seq_len, float sm_scale, void* out,
                                kvq_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    if (D != 128) return fail(KVQ_ERR_UNSUPPORTED, "attention is built for D=128 (D=%d)", (int)D);
+    if (D != 128 && D != 256) return fail(KVQ_ERR_UNSUPPORTED, "attention is built for D=128 and 256 (D=%d)", (int)D);
     if (kvq_status s = check_attn_common(D, q, B, Hq, Hkv, Tcap, seq_len, out, out_dtype, workspace,
                                          workspace_bytes, true))
       return s;

@@ -118,6 +118,7 @@ class Config:
     T: int
     law: str
     index: int      # seeds: data = index, lambda = 100 + index, signs = 1000 + index
+    Hq: int = 0     # decode steps: query heads (H is then the KV head count)
 
     @property
     def vectors(self) -> int:
@@ -144,7 +145,10 @@ CONFIGS = {
     # Gemma-3-1B prefix: 26 layers x {K,V} x 1 KV head x 4096 tokens, D=256
     "gemma": Config("gemma-3-1b-prefix-26Lx2x1Hx4096-D256", 256, 52, 1, 4096, "spread", 3),
     # decode step: batch 64, Hq 8 / Hkv 2, 32768 cached tokens, D=128
-    "decode": Config("gqa-decode-B64-Hq8-Hkv2-L32769-D128", 128, 64, 2, 32768, "spread", 4),
+    "decode": Config("gqa-decode-B64-Hq8-Hkv2-L32769-D128", 128, 64, 2, 32768, "spread", 4, 8),
+    # the same decode step at Gemma-3 1B's head shape: batch 64, Hq 4 / Hkv 1,
+    # 32768 cached tokens, D=256 (the same cache bytes per step as "decode")
+    "decode256": Config("gqa-decode-B64-Hq4-Hkv1-L32769-D256", 256, 64, 1, 32768, "spread", 8, 4),
     # Mistral-7B bulk: 32 layers x {K,V}, batch 16 x 8 heads x 8192 tokens, D=128
     "mistral": Config("mistral-7b-bulk-32Lx2-B16-H8-T8192-D128", 128, 16, 8, 8192, "t3", 5),
     # head sizes that are not powers of two (mixed-radix SRFT): the prefix

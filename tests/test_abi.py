@@ -101,7 +101,7 @@ def test_plan_mixed_radix_sizes(D, G, bits, rot):
 
 
 def test_plan_mixed_radix_rejects():
-    """SRHT needs a power-of-two D; G must divide D; attention stays D=128."""
+    """SRHT needs a power-of-two D; G must divide D; attention is built for D = 128 and 256 only."""
     L = K.library()
     h = ctypes.c_void_p()
     assert L.kvq_plan_create(96, 32, O.SRHT, 0, ctypes.byref(h)) == UNSUPPORTED
@@ -215,10 +215,15 @@ def test_attention_validation():
     assert call(vc=None) == INVALID
     assert call(dt=5) == INVALID
     assert call(B=0) == OK                            # nothing to do
+    # head sizes with attention kernels: 128 and 256 (the mixed-radix sizes have none)
     p256 = K.Plan(256, 32, "srft", 3)
-    assert L.kvq_attn_decode(p256.handle, A, A, A, A, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need,
+    assert L.kvq_attn_decode(p256.handle, A, A, A, A, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, 0,
+                             None) == WORKSPACE
+    p96 = K.Plan(96, 32, "srft", 3)
+    assert L.kvq_attn_decode(p96.handle, A, A, A, A, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need,
                              None) == UNSUPPORTED
-    assert L.kvq_attn_decode_f16(256, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need, None) == UNSUPPORTED
+    assert L.kvq_attn_decode_f16(96, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need, None) == UNSUPPORTED
+    assert L.kvq_attn_decode_f16(256, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, 0, None) == WORKSPACE
     assert L.kvq_attn_decode_f16(128, A, A, A, 1, 3, 2, 8, 4, 0.1, A, 0, A, need, None) == INVALID
     assert L.kvq_attn_decode_f16(128, A, None, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need, None) == INVALID
 
@@ -247,8 +252,12 @@ def test_workspace_size_monotone():
     a = K.attn_workspace_size(128, 2, 8, 100)
     b = K.attn_workspace_size(128, 2, 8, 100000)
     assert 0 < a < b
+    # D=256 partials are twice as wide
+    assert K.attn_workspace_size(256, 2, 8, 100000) > b
     with pytest.raises(K.KvqError):
         K.attn_workspace_size(64, 2, 8, 100)
+    with pytest.raises(K.KvqError):
+        K.attn_workspace_size(96, 2, 8, 100)
 
 
 def test_binding_refuses_host_tensors():
