@@ -441,6 +441,21 @@ MIXED = (("d96", "int4-g32", 4, 32), ("d96", "int4-g16", 4, 16), ("d80", "int4-g
          ("d96", "int8-g32", 8, 32), ("d80", "int8-g16", 8, 16))
 
 
+def mfma_leg(K, torch, stream, cfg, sets, n):
+    """The D=128 SRFT encoder with its DFT on the matrix cores (plan option)
+    against the VALU encoder, on the same Qwen prefix batches, each timed
+    over n launches with HIP events on the kernels' stream."""
+    D = cfg.D
+    ns = len(sets)
+    nbytes = cfg.vectors * (2 * D + D // 2 + 2 * (D // 32))
+    res = {"workload": "Qwen2.5-1.5B-shaped prefix encode (458,752 vectors, D=128, SRFT, group 32)"}
+    for name, mfma in (("valu_fft", False), ("mfma_dft", True)):
+        plan = K.Plan(D, 32, "srft", cfg.sign_seed, mfma=mfma)
+        us = timed_loop(torch, stream, lambda i: K.encode(plan, *sets[i % ns][:4]), n)
+        res[name] = {"encode_us": round(us, 2), "encode_frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def mixed_leg(K, W, torch, stream, dev, n_sets, n):
     """Head sizes that are not powers of two (the mixed-radix SRFT): encode
     and decode of the 28-layer prefix shape (28 layers x {K,V} x 2 KV heads x
@@ -653,6 +668,8 @@ def main():
     del g_sets
     # ---- code formats (int4 G16, int8 G32 / G16), timed apart ----
     fmts = formats_leg(K, torch, stream, cfg, sets, dc, k16, v16, lam_k, lam_v, q, L, sm, max(10, args.steps))
+    # ---- the encoder with its DFT on the matrix cores, timed apart ----
+    mfma = mfma_leg(K, torch, stream, cfg, sets, max(10, args.steps))
     # ---- D=96 and D=80 (mixed-radix SRFT), timed apart ----
     mixed = mixed_leg(K, W, torch, stream, dev, args.sets, max(10, args.steps))
     # ---- D=256 decode step (Gemma-3 1B head shape), timed apart ----
@@ -748,6 +765,7 @@ def main():
         "attention_d256": att256,
         "formats": fmts,
         "mixed_radix": mixed,
+        "mfma_rotation": mfma,
         "small_round_trip": small,
         "mistral_bulk": mistral,
     }

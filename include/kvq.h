@@ -113,6 +113,25 @@ kvq_status kvq_plan_create(int32_t D, int32_t G, kvq_rotation rotation, uint64_t
 kvq_status kvq_plan_create_ex(int32_t D, int32_t G, int32_t bits, kvq_rotation rotation, uint64_t seed,
                               kvq_plan** out);
 
+/* Plan options (bits of kvq_plan_create_opt's options). */
+typedef enum {
+  /* D = 128 SRFT: kvq_encode and kvq_rotate take the 64-point DFT on the
+   * matrix cores, factored as 8 x 8 (the explainer's "Begruendung" for the
+   * SRFT and its AMX path, "Methodik" 1 and 4: DFTs as small dense matrix
+   * products).  Same codes and scales up to the boundary cases of a
+   * different fp32 rounding order; decode and attention are unchanged. */
+  KVQ_OPT_MFMA_ROTATION = 1
+} kvq_option;
+
+/* Create a plan with options: kvq_plan_create_ex plus a set of kvq_option
+ * bits (0 = none).  KVQ_ERR_INVALID for unknown bits, KVQ_ERR_UNSUPPORTED
+ * for an option the plan's D or rotation has no kernel for. */
+kvq_status kvq_plan_create_opt(int32_t D, int32_t G, int32_t bits, kvq_rotation rotation, uint64_t seed,
+                               uint32_t options, kvq_plan** out);
+
+/* Read back a plan's option bits. */
+kvq_status kvq_plan_options(const kvq_plan* plan, uint32_t* options);
+
 /* Release a plan (NULL is a no-op).  Work already enqueued does not use the
  * plan object: its constants travel with each launch. */
 void kvq_plan_destroy(kvq_plan* plan);

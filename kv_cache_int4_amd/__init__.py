@@ -17,7 +17,7 @@ import ctypes
 import os
 
 __all__ = [
-    "KvqError", "Plan", "SRFT", "SRHT", "IDENTITY", "GROUP",
+    "KvqError", "Plan", "OPT_MFMA_ROTATION", "SRFT", "SRHT", "IDENTITY", "GROUP",
     "library", "library_path", "encode", "decode", "rotate",
     "attn_workspace_size", "attn_decode", "attn_decode_noalloc", "attn_decode_f16",
     "cache_shapes",
@@ -64,6 +64,9 @@ def library() -> ctypes.CDLL:
         "kvq_last_error": (ctypes.c_char_p, []),
         "kvq_plan_create": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _u64, ctypes.POINTER(_vp)]),
         "kvq_plan_create_ex": (ctypes.c_int, [_i32, _i32, _i32, ctypes.c_int, _u64, ctypes.POINTER(_vp)]),
+        "kvq_plan_create_opt": (ctypes.c_int, [_i32, _i32, _i32, ctypes.c_int, _u64, ctypes.c_uint32,
+                                               ctypes.POINTER(_vp)]),
+        "kvq_plan_options": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_uint32)]),
         "kvq_plan_destroy": (None, [_vp]),
         "kvq_plan_signs": (ctypes.c_int, [_vp, _vp, _i64]),
         "kvq_plan_info": (ctypes.c_int, [_vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
@@ -133,18 +136,24 @@ def _device(*ts) -> int:
     return idx
 
 
+OPT_MFMA_ROTATION = 1
+
+
 class Plan:
     """Head dimension D, group G, rotation ("srft" | "srht" | "identity"),
-    the seed of the sign vector and the code width (4: int4 nibbles, 8: int8
-    bytes)."""
+    the seed of the sign vector, the code width (4: int4 nibbles, 8: int8
+    bytes) and, for D=128 SRFT plans, mfma=True to run the encoder's DFT on
+    the matrix cores."""
 
-    def __init__(self, D: int = 128, G: int = GROUP, rotation="srft", seed: int = 0, bits: int = 4):
+    def __init__(self, D: int = 128, G: int = GROUP, rotation="srft", seed: int = 0, bits: int = 4,
+                 mfma: bool = False):
         L = library()
         rot = _ROT_NAMES[rotation] if isinstance(rotation, str) else int(rotation)
         h = _vp()
-        _check(L.kvq_plan_create_ex(D, G, bits, rot, seed & ((1 << 64) - 1), ctypes.byref(h)))
+        opts = OPT_MFMA_ROTATION if mfma else 0
+        _check(L.kvq_plan_create_opt(D, G, bits, rot, seed & ((1 << 64) - 1), opts, ctypes.byref(h)))
         self._h = h
-        self.D, self.G, self.rotation, self.seed, self.bits = D, G, rot, seed, bits
+        self.D, self.G, self.rotation, self.seed, self.bits, self.mfma = D, G, rot, seed, bits, mfma
 
     @property
     def code_bytes(self) -> int:

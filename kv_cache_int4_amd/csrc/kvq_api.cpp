@@ -22,6 +22,7 @@ struct kvq_plan {
   int32_t G;
   int32_t bits;
   int32_t rotation;
+  uint32_t options;        // KVQ_OPT_* bits
   uint64_t seed;
   uint64_t sign_bits[4];   // bit i of word i / 64 = 1 for sign -1
 };
@@ -98,6 +99,7 @@ void fill_signs(const kvq_plan* p, kvq::CodecDesc& d) {
   d.G = p->G;
   d.bits = p->bits;
   d.rotation = p->rotation;
+  d.options = p->options;
   for (int i = 0; i < 4; ++i) d.signs[i] = p->sign_bits[i];
 }
 
@@ -169,6 +171,23 @@ const char* kvq_strerror(kvq_status s) {
 
 const char* kvq_last_error(void) { return g_last_error.c_str(); }
 
+kvq_status kvq_plan_create_opt(int32_t D, int32_t G, int32_t bits, kvq_rotation rotation, uint64_t seed,
+                               uint32_t options, kvq_plan** out) {
+  try {
+    if (!out) return fail(KVQ_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (options & ~static_cast<uint32_t>(KVQ_OPT_MFMA_ROTATION))
+      return fail(KVQ_ERR_INVALID, "unknown option bits 0x%x", options);
+    if ((options & KVQ_OPT_MFMA_ROTATION) && !(D == 128 && rotation == KVQ_SRFT))
+      return fail(KVQ_ERR_UNSUPPORTED, "the matrix-core rotation is built for D=128 SRFT plans");
+    if (kvq_status s = kvq_plan_create_ex(D, G, bits, rotation, seed, out)) return s;
+    (*out)->options = options;
+    return ok();
+  } catch (...) {
+    return fail(KVQ_ERR_INVALID, "internal error");
+  }
+}
+
 kvq_status kvq_plan_create_ex(int32_t D, int32_t G, int32_t bits, kvq_rotation rotation, uint64_t seed,
                               kvq_plan** out) {
   try {
@@ -189,6 +208,7 @@ kvq_status kvq_plan_create_ex(int32_t D, int32_t G, int32_t bits, kvq_rotation r
     p->G = G;
     p->bits = bits;
     p->rotation = rotation;
+    p->options = 0;
     p->seed = seed;
     std::memset(p->sign_bits, 0, sizeof(p->sign_bits));
     const int32_t n = sign_count(p);
@@ -223,6 +243,13 @@ kvq_status kvq_plan_signs(const kvq_plan* plan, int8_t* host_signs, int64_t n) {
 
 kvq_status kvq_plan_info(const kvq_plan* plan, int32_t* D, int32_t* G, int32_t* rotation) {
   return kvq_plan_info_ex(plan, D, G, nullptr, rotation);
+}
+
+kvq_status kvq_plan_options(const kvq_plan* plan, uint32_t* options) {
+  if (kvq_status s = check_plan(plan)) return s;
+  if (!options) return fail(KVQ_ERR_INVALID, "options is NULL");
+  *options = plan->options;
+  return ok();
 }
 
 kvq_status kvq_plan_info_ex(const kvq_plan* plan, int32_t* D, int32_t* G, int32_t* bits, int32_t* rotation) {

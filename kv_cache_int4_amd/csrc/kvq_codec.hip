@@ -238,7 +238,7 @@ struct Fmt {
   static constexpr int CW = 128 * BITS / 32;    // code words per lane (16 or 32)
   static constexpr int CB = 4 * CW;             // code bytes per lane (64 or 128)
   static constexpr int SB = 2 * NG;             // scale bytes per lane (8 or 16)
-  static constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
+  static constexpr int IQMAX = BITS == 4 ? 7 : 127;
 };
 
 // Codes of group g (G channels) from w and r = 1 / scale: int4 as pair
@@ -432,9 +432,9 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
           }
         }
         // scale = fp16(fp32(absmax / qmax)) with the IEEE fp32 quotient
-        // (a handful of instructions per group); amax * kScale is the
+        // (div_by: three instructions per group); amax * kScale is the
         // unitary abs-max, exact where kScale is a power of two
-        sc[g] = f32_to_f16_bits((amax * kScale) / F::QMAX);
+        sc[g] = f32_to_f16_bits(div_by<F::IQMAX>(amax * kScale));
         const float sf = f16_bits_to_f32(sc[g]);
         r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
         tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);    // fp16-subnormal scale
@@ -460,6 +460,392 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
     }
   }
   if (MODE == 0 && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
+}
+
+// ---------------------------------------------------------------------------
+// D = 128 SRFT encode with the DFT on the matrix cores (a plan option).
+//
+// The 64-point DFT of pairs z_k, k = 8a + b, to frequencies m = c + 8d
+// factors as Z_{c+8d} = sum_b W_64^{b(c+8d)} sum_a W_8^{ac} z_{8a+b}:
+//   stage 1: for each b, an 8-point DFT over a: Y_b[c] = sum_a W_8^{ac}
+//            z_{8a+b}, one v_mfma_f32_16x16x32_f16 per b over 16 vectors:
+//            A = [F_hi | F_lo] (the real 16x16 form of the DFT, split into
+//            fp16 halves), B = the exact fp16 pairs twice, so F z is exact
+//            to about 2^-22;
+//   stage 2: for each c, Z_{c+8d} = sum_b G_c[d][b] Y_b[c] with G_c =
+//            W_64^{b(c+8d)} (twiddles and the 8-point DFT over b in one
+//            matrix), four v_mfma_f32_16x16x4_f32 per c on the fp32 Y.
+// Columns are 16 vectors; lane (v, r) = lane v + 16 r.  After stage 1 the
+// lane holds Y_b[c] for c in {2r, 2r+1}; stage 2 needs, for each c, the
+// values of every b, so Y passes through LDS (into the rows of the tile the
+// group has just read) in two halves of c.  After stage 2 lane (v, r) holds
+// Z_m for m = 16 r .. 16 r + 15 of vector v: output channels 32 r .. 32 r +
+// 31, exactly one group of 32 (two of 16), so lambda, the abs-max, the scale
+// and the codes are the lane's own work, and the lane's 16 code bytes are
+// chunk r of row v: a group of 16 vectors stores 1 KiB of codes with one
+// coalesced instruction.
+// ---------------------------------------------------------------------------
+typedef _Float16 mf_half8 __attribute__((ext_vector_type(8)));
+typedef float mf_float4 __attribute__((ext_vector_type(4)));
+
+// fp16 bits of a double below 65504 in magnitude, rounded to nearest even,
+// subnormals kept (compile time).
+constexpr uint32_t mf_f16_bits(double x) {
+  if (x == 0.0) return 0u;
+  const uint32_t sgn = x < 0 ? 0x8000u : 0u;
+  double m = x < 0 ? -x : x;
+  int e = 0;
+  while (m >= 2.0) { m /= 2.0; ++e; }
+  while (m < 1.0) { m *= 2.0; --e; }
+  if (e < -14) {                           // subnormal: multiples of 2^-24
+    double f = x < 0 ? -x : x;
+    for (int i = 0; i < 24; ++i) f *= 2.0;
+    uint32_t q = static_cast<uint32_t>(f);
+    const double rem = f - q;
+    if (rem > 0.5 || (rem == 0.5 && (q & 1u))) ++q;
+    return sgn | q;                        // q = 1024 is the smallest normal
+  }
+  // m in [1, 2): 10 fraction bits, round half to even
+  double f = (m - 1.0) * 1024.0;
+  uint32_t q = static_cast<uint32_t>(f);
+  const double rem = f - q;
+  if (rem > 0.5 || (rem == 0.5 && (q & 1u))) ++q;
+  if (q == 1024u) { q = 0; ++e; }
+  return sgn | (static_cast<uint32_t>(e + 15) << 10) | q;
+}
+
+constexpr double mf_f16_value(uint32_t h) {
+  if ((h & 0x7FFFu) == 0) return 0.0;
+  if (((h >> 10) & 31u) == 0) {            // subnormal
+    double v = (h & 1023u);
+    for (int i = 0; i < 24; ++i) v /= 2.0;
+    return (h & 0x8000u) ? -v : v;
+  }
+  const int e = static_cast<int>((h >> 10) & 31u) - 15;
+  double v = 1.0 + (h & 1023u) / 1024.0;
+  for (int i = 0; i < e; ++i) v *= 2.0;
+  for (int i = 0; i > e; --i) v /= 2.0;
+  return (h & 0x8000u) ? -v : v;
+}
+
+// Per-lane matrix operands of the two stages (lane l: row l % 16, k-slice
+// l / 16), without the plan's signs: stage 1 as fp16 pairs, stage 2 as fp32.
+struct MfTables {
+  uint32_t a1[64][4];
+  float a2[64][32];      // [c * 4 + kc]
+};
+
+constexpr MfTables make_mf_tables() {
+  MfTables t{};
+  // cos, sin (2 pi e / 64) rounded once to float, quarter turns exact
+  constexpr TwTable tw = make_twiddles(64);
+  for (int l = 0; l < 64; ++l) {
+    const int rr = l & 15, r = l >> 4, eo = rr & 1, c = rr >> 1;
+    // stage 1, row rr = 2 c + eo, k = 2 a + ei: [[cos, sin], [-sin, cos]]
+    // of theta = 2 pi a c / 8; hi (r < 2) or lo (r >= 2) fp16 half
+    for (int u = 0; u < 4; ++u) {
+      uint32_t w = 0;
+      for (int h = 0; h < 2; ++h) {
+        const int k = 8 * (r & 1) + 2 * u + h, aa = k >> 1, ei = k & 1;
+        // the table's fp32 value split into fp16 hi + lo: W_8^{ac} to about
+        // 2^-22 (the fp32 rounding of the entry, 2^-24, is the larger error)
+        const int e = 8 * ((aa * c) & 7);
+        const double cs = tw.c[e], sn = tw.s[e];
+        const double f = eo == 0 ? (ei == 0 ? cs : sn) : (ei == 0 ? -sn : cs);
+        const uint32_t hi = mf_f16_bits(f);
+        const uint32_t bits = r < 2 ? hi : mf_f16_bits(f - mf_f16_value(hi));
+        w |= bits << (16 * h);
+      }
+      t.a1[l][u] = w;
+    }
+    // stage 2 for c, k = 4 kc + r <-> (b = 2 kc + r / 2, ei = r % 2), row
+    // rr = 2 d + eo: W_64^{b (c + 8 d)} in real form
+    for (int cc = 0; cc < 8; ++cc)
+      for (int kc = 0; kc < 4; ++kc) {
+        const int d = rr >> 1, b = 2 * kc + (r >> 1), ei = r & 1;
+        const int e = (b * (cc + 8 * d)) & 63;
+        const float cs = tw.c[e], sn = tw.s[e];
+        t.a2[l][4 * cc + kc] = eo == 0 ? (ei == 0 ? cs : sn) : (ei == 0 ? -sn : cs);
+      }
+  }
+  return t;
+}
+
+__constant__ MfTables kMfTab = make_mf_tables();
+
+// LDS byte offset of 16-byte slot q (0..15) of the 256-byte staging row of
+// vector v16 (one of the 16 vectors of a group), inside the group's 4 KiB:
+// the slot index is XOR-swizzled with the row.
+__device__ __forceinline__ uint32_t mf_slot(int v16, int q) {
+  return static_cast<uint32_t>(v16 * 256 + ((q ^ v16) << 4));
+}
+
+
+// Quantize the lane's 32 channels w (one group of 32 or two of 16) with the
+// reciprocal scales rr into code words cw (16 bytes int4, 32 bytes int8).
+template <int FMT, bool CLAMP>
+__device__ __forceinline__ void mf_quant(const float (&w)[32], const float (&rr)[2], uint32_t* cw) {
+  using F = Fmt<FMT>;
+#pragma unroll
+  for (int q = 0; q < F::BITS; ++q) {
+    uint32_t by[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (F::BITS == 4) {
+        const int j = 8 * q + 2 * e;
+        const float rg = rr[j / F::G];
+        const uint32_t lo = CLAMP ? quant_bits(w[j], rg) : __builtin_bit_cast(uint32_t, fmaf(w[j], rg, kMagic));
+        const uint32_t hi =
+            CLAMP ? quant_bits(w[j + 1], rg) : __builtin_bit_cast(uint32_t, fmaf(w[j + 1], rg, kMagic));
+        by[e] = pair_byte(lo, hi);
+      } else {
+        const int j = 4 * q + e;
+        const float rg = rr[j / F::G];
+        by[e] = CLAMP ? quant_bits8(w[j], rg) : __builtin_bit_cast(uint32_t, fmaf(w[j], rg, kMagic8));
+      }
+    }
+    cw[q] = pack4(by[0], by[1], by[2], by[3]) ^ (F::BITS == 8 ? 0x80808080u : 0u);
+  }
+}
+
+// The lambda row of a tile (512 bytes) by one direct load of 16 bytes per
+// lane, into the LDS the caller passes (a plain pointer, as for the tile:
+// the waits for both are explicit).
+__device__ __forceinline__ void mf_dma_lambda(const CodecArgs& a, const Tile& t, uint8_t* lds, int lane) {
+  const float* gl = a.lambda + t.b * a.lambda_sb + t.h * 128 + 4 * lane;
+  if (lane < 32) __builtin_amdgcn_global_load_lds(gl, lds, 16, 0, 0);
+}
+
+// Eight 16-byte LDS reads of the lambda row (channels 32 r ..), issued and
+// waited for in one assembly block: written as plain loads, the compiler
+// would wait for every direct load in flight (it tracks the direct load that
+// filled the row, not the group's own wait).
+struct MfLam {
+  float4 v[8];
+};
+
+__device__ __forceinline__ MfLam mf_read_lambda_blk(const float* lam_lds, int r) {
+  typedef __attribute__((address_space(3))) const float lds_f;
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_f*)lam_lds)) + 128u * r;
+  MfLam o;
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  f4v x0, x1, x2, x3, x4, x5, x6, x7;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:16\n\t"
+      "ds_read_b128 %2, %8 offset:32\n\t"
+      "ds_read_b128 %3, %8 offset:48\n\t"
+      "ds_read_b128 %4, %8 offset:64\n\t"
+      "ds_read_b128 %5, %8 offset:80\n\t"
+      "ds_read_b128 %6, %8 offset:96\n\t"
+      "ds_read_b128 %7, %8 offset:112\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(x4), "=v"(x5), "=v"(x6), "=v"(x7)
+      : "v"(addr)
+      : "memory");
+  const f4v xs[8] = {x0, x1, x2, x3, x4, x5, x6, x7};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o.v[i] = make_float4(xs[i][0], xs[i][1], xs[i][2], xs[i][3]);
+  return o;
+}
+
+template <int MODE, int FMT>
+__global__ void __launch_bounds__(64, 2) encode128_mfma_kernel(CodecArgs a) {
+  using F = Fmt<FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
+  __shared__ __attribute__((aligned(16))) float lam_lds[128];
+  const int lane = threadIdx.x;
+  const int v16 = lane & 15;               // column: vector of the group
+  const int r = lane >> 4;                 // row group / k-slice
+  const int a0 = 4 * (r & 1);              // stage 1 reads pairs 8 a + b, a = a0 .. a0 + 3
+  constexpr float kScale = 0.125f;         // 1 / sqrt(64): the transforms are unnormalized
+
+  // stage 1 matrices, one per b: the table's halves with the sign of pair
+  // 8 a + b (exact); this lane's a = a0 + u for dword u
+  uint4 a1s;
+  {
+    const uint4* t1 = reinterpret_cast<const uint4*>(kMfTab.a1[lane]);
+    a1s = *t1;
+  }
+  const uint32_t sw = static_cast<uint32_t>(a.signs[0] >> (32 * (r & 1)));   // bits 8 u + b
+  mf_half8 A1[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    uint32_t d[4] = {a1s.x, a1s.y, a1s.z, a1s.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) d[u] ^= ((sw >> (8 * u + b)) & 1u) * 0x80008000u;
+    A1[b] = __builtin_bit_cast(mf_half8, make_uint4(d[0], d[1], d[2], d[3]));
+  }
+  float A2[32];
+  {
+    const float4* t2 = reinterpret_cast<const float4*>(kMfTab.a2[lane]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 x = t2[i];
+      A2[4 * i] = x.x; A2[4 * i + 1] = x.y; A2[4 * i + 2] = x.z; A2[4 * i + 3] = x.w;
+    }
+  }
+  uint32_t off4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rw = 4 * i + (lane >> 4);
+    off4[i] = static_cast<uint32_t>((lane >> 4) * 2 * a.st + 16 * ((lane & 15) ^ (rw & 15)));
+  }
+
+  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    const Tile t = tile_info<128>(a, tile);
+    // lambda first, then the tile's rows: loads complete in issue order, so
+    // group g (rows 16 g .., loads 4 g .. 4 g + 3) can start once all but the
+    // 12 - 4 g youngest loads are back, while later groups still stream in.
+    // Codes and scales are stored after the last group, so that no store
+    // sits among the loads (a partial tile, whose loads are predicated, and
+    // the rotate mode wait for everything instead).
+    mf_dma_lambda(a, t, reinterpret_cast<uint8_t*>(lam_lds), lane);
+    dma_tile128(a, t, lds, lane, off4);
+    const bool staged = MODE == 0 && t.nv == 64;
+    const int64_t cell0 = t.row * a.Tcap + a.t0 + t.t_start;   // wave-uniform
+    uint4 out_c[4][F::BITS / 4];
+    uint32_t out_s[4];
+
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (16 * g >= t.nv) break;                      // wave-uniform
+      asm volatile("" ::: "memory");                  // one group at a time
+      if (!staged) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if (g == 0) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else if (g == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (g == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int v = 16 * g + v16;                     // vector of the tile
+      uint8_t* stage = lds + 4096 * g;                // this group's rows, free after stage 1
+
+      // ---- stage 1: 8-point DFTs over a, one MFMA per b; operand dword u
+      // is pair 8 (a0 + u) + b of row v ----
+      float Y[8][4];                                  // [b][(c = 2r re, im, c = 2r+1 re, im)]
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k = 8 * (a0 + u) + b;
+          w[u] = *reinterpret_cast<const uint32_t*>(lds + blk_off(v, k >> 2) + 4 * (k & 3));
+        }
+        const mf_half8 B1 = __builtin_bit_cast(mf_half8, make_uint4(w[0], w[1], w[2], w[3]));
+        const mf_float4 y =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[b], B1, (mf_float4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Y[b][e] = y[e];
+      }
+
+      // ---- exchange: stage 2 for c needs Y_b[c] of every b, held by row
+      // group c / 2.  Two halves of c (row groups 0-1, then 2-3) pass
+      // through the group's 4 KiB (its rows, read above; a wave's LDS
+      // operations run in order): row v16, 16-byte slot ((c / 2) % 2) * 8 + b
+      // (XOR v16) holds Y_b[c], Y_b[c + 1] of the c pair ----
+      float Z[8][4];                                  // [c][(d = 2r re, im, d = 2r+1 re, im)]
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if ((r >> 1) == h) {
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+            *reinterpret_cast<float4*>(stage + mf_slot(v16, 8 * (r & 1) + b)) =
+                make_float4(Y[b][0], Y[b][1], Y[b][2], Y[b][3]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // B of stage 2 for c, k-chunk kc: Y_b[c] component e, b = 2 kc + r / 2, e = r % 2
+#pragma unroll
+        for (int cl = 0; cl < 4; ++cl) {
+          const int c = 4 * h + cl;
+          float bq[4];
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            const int b = 2 * kc + (r >> 1);
+            bq[kc] = *reinterpret_cast<const float*>(stage + mf_slot(v16, 8 * (cl >> 1) + b) + 8 * (cl & 1) +
+                                                     4 * (r & 1));
+          }
+          mf_float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A2[4 * c + kc], bq[kc], acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Z[c][e] = acc[e];
+        }
+        // the next half's writes follow these reads in LDS order
+      }
+
+      // Z[c][2 dd + e] = Z_m, m = c + 8 (2 r + dd): output channel
+      // j = 2 m + e = 32 r + 16 dd + 2 c + e; local index jl = j - 32 r
+      const bool valid = v < t.nv;
+      float w[32];
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) w[16 * dd + 2 * c + e] = Z[c][2 * dd + e];
+      {
+        // lambda of channels 32 r .. 32 r + 31, read in one block that waits
+        // for its own reads (the direct load that filled the row has landed:
+        // the group's wait above covers it)
+        const MfLam l4 = mf_read_lambda_blk(lam_lds, r);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          w[4 * q] *= l4.v[q].x; w[4 * q + 1] *= l4.v[q].y; w[4 * q + 2] *= l4.v[q].z; w[4 * q + 3] *= l4.v[q].w;
+        }
+      }
+      if (MODE == 1) {
+        float* wr = a.w + ((t.row * a.T) + t.t_start + v) * 128 + 32 * r;
+        if (valid) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            *reinterpret_cast<float4*>(wr + 4 * q) =
+                make_float4(w[4 * q] * kScale, w[4 * q + 1] * kScale, w[4 * q + 2] * kScale, w[4 * q + 3] * kScale);
+        }
+        continue;
+      }
+      // ---- scale(s) and codes of the lane's 32 channels ----
+      constexpr int NGL = 32 / F::G;                  // groups per lane: 1 or 2
+      float rr[2] = {0.f, 0.f};
+      uint32_t sc[2] = {0u, 0u};
+      bool tiny = false;
+#pragma unroll
+      for (int gg = 0; gg < NGL; ++gg) {
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < F::G; ++j) amax = fmaxf(amax, fabsf(w[F::G * gg + j]));
+        sc[gg] = f32_to_f16_bits(div_by<F::IQMAX>(amax * kScale));
+        const float sf = f16_bits_to_f32(sc[gg]);
+        rr[gg] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
+        tiny |= (sc[gg] != 0u) && (sc[gg] < 0x0400u);
+      }
+      uint32_t cw[F::BITS];                           // 16 (int4) or 32 (int8) code bytes
+      if (__builtin_amdgcn_ballot_w64(tiny && valid) == 0) mf_quant<FMT, false>(w, rr, cw);
+      else mf_quant<FMT, true>(w, rr, cw);
+#pragma unroll
+      for (int q = 0; q < F::BITS / 4; ++q)
+        out_c[g][q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+      out_s[g] = sc[0] | (sc[1] << 16);
+    }
+    if (MODE == 0) {
+      // codes: row v, bytes r * CB / 4 ..; scales: entries v * NG + r * NGL ..
+      constexpr int NGL = 32 / F::G;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int v = 16 * g + v16;
+        if (v < t.nv) {
+          char* cb = reinterpret_cast<char*>(a.codes + (cell0 + v) * F::CB) + r * (F::CB / 4);
+#pragma unroll
+          for (int q = 0; q < F::BITS / 4; ++q) *reinterpret_cast<uint4*>(cb + 16 * q) = out_c[g][q];
+          uint16_t* sp = a.scales + (cell0 + v) * F::NG + r * NGL;
+          if (NGL == 1) *sp = static_cast<uint16_t>(out_s[g]);
+          else *reinterpret_cast<uint32_t*>(sp) = out_s[g];
+        }
+      }
+    }
+    // the tile's rows served as staging: every LDS access of this tile is
+    // done before the next tile's direct loads write them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -672,7 +1058,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
           amax = fmaxf(amax, fabsf(wv));
         }
       }
-      sc[g] = f32_to_f16_bits((amax * kScale) / F::QMAX);
+      sc[g] = f32_to_f16_bits(div_by<F::IQMAX>(amax * kScale));
       const float sf = f16_bits_to_f32(sc[g]);
       r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
       tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);
@@ -1334,6 +1720,14 @@ hipError_t encode_dispatch(const CodecDesc& d, int mode) {
   if (a.n_tiles == 0) return hipSuccess;
   if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
   const dim3 grid(static_cast<unsigned>(launch_grid(a.n_tiles, true)));
+  if (D == 128 && ROT == KVQ_ROT_SRFT && (d.options & kOptMfmaRotation)) {
+    if (mode == 1) {
+      hipLaunchKernelGGL((encode128_mfma_kernel<1, 0>), grid, dim3(64), 0, d.stream, a);
+    } else {
+      hipLaunchKernelGGL((encode128_mfma_kernel<0, FMT>), grid, dim3(64), 0, d.stream, a);
+    }
+    return hipGetLastError();
+  }
   if (mode == 1) {
     // rotate only: the quantizer format plays no part
     if (D == 128) {

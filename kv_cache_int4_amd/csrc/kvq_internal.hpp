@@ -9,12 +9,17 @@ namespace kvq {
 
 enum { KVQ_ROT_SRFT = 0, KVQ_ROT_SRHT = 1, KVQ_ROT_ID = 2 };
 
+// Plan options (kvq_plan_create_opt): the SRFT's DFT of the D = 128 encoder
+// on the matrix cores.
+constexpr uint32_t kOptMfmaRotation = 1u;
+
 // A validated codec call (encode, rotate or decode).
 struct CodecDesc {
   int D;
   int G;                      // group size: 32 or 16
   int bits;                   // code width: 4 or 8
   int rotation;
+  uint32_t options;           // plan options (kOptMfmaRotation)
   uint64_t signs[4];          // sign bits, bit i of word i / 64
   const uint16_t* x;          // encode / rotate input
   const uint8_t* codes_in;    // decode input

@@ -83,7 +83,7 @@ struct MFmt {
   static constexpr int CW = CB / 4;                     // code words
   static constexpr int SB = 2 * NG;                     // scale bytes
   static constexpr int WPG = CW / NG;                   // code words per group
-  static constexpr float QMAX = BITS == 4 ? 7.f : 127.f;
+  static constexpr int IQMAX = BITS == 4 ? 7 : 127;
   // direct loads of a tile's codes: 16-byte slots where CB allows, else
   // dwords (CB = 40); NU slots per vector, as many loads per lane
   static constexpr int CU = CB % 16 == 0 ? 16 : 4;
@@ -322,7 +322,7 @@ __global__ void __launch_bounds__(64, 2) mix_encode_kernel(MixArgs a) {
         }
         // scale = fp16(fp32(absmax / qmax)) of the unitary values kScale *
         // wv, with the IEEE fp32 quotient
-        sc[g] = f32_to_f16_bits((amax * kScale) / F::QMAX);
+        sc[g] = f32_to_f16_bits(div_by<F::IQMAX>(amax * kScale));
         const float sf = f16_bits_to_f32(sc[g]);
         r[g] = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
         tiny |= (sc[g] != 0u) && (sc[g] < 0x0400u);     // fp16-subnormal scale

@@ -88,6 +88,27 @@ def test_plan_formats(bits, G, D):
     L.kvq_plan_destroy(h)
 
 
+def test_plan_options():
+    """KVQ_OPT_MFMA_ROTATION is accepted for D=128 SRFT plans of every format
+    and refused elsewhere; unknown option bits are invalid."""
+    L = K.library()
+    h = ctypes.c_void_p()
+    for bits, G in ((4, 32), (4, 16), (8, 32), (8, 16)):
+        assert L.kvq_plan_create_opt(128, G, bits, O.SRFT, 7, 1, ctypes.byref(h)) == OK
+        o = ctypes.c_uint32()
+        assert L.kvq_plan_options(h, ctypes.byref(o)) == OK and o.value == 1
+        L.kvq_plan_destroy(h)
+    assert L.kvq_plan_create_opt(256, 32, 4, O.SRFT, 7, 1, ctypes.byref(h)) == UNSUPPORTED
+    assert L.kvq_plan_create_opt(128, 32, 4, O.SRHT, 7, 1, ctypes.byref(h)) == UNSUPPORTED
+    assert L.kvq_plan_create_opt(96, 32, 4, O.SRFT, 7, 1, ctypes.byref(h)) == UNSUPPORTED
+    assert L.kvq_plan_create_opt(128, 32, 4, O.SRFT, 7, 2, ctypes.byref(h)) == INVALID
+    assert L.kvq_plan_create_opt(128, 32, 4, O.SRFT, 7, 0, None) == INVALID
+    p = K.Plan(128, 32, "srft", 7, mfma=True)
+    assert np.array_equal(p.signs(), O.plan_signs(128, O.SRFT, 7))
+    o = ctypes.c_uint32()
+    assert L.kvq_plan_options(K.Plan(128, 32, "srft", 7).handle, ctypes.byref(o)) == OK and o.value == 0
+
+
 @pytest.mark.parametrize("D,G", [(96, 32), (96, 16), (80, 16)])
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("rot", [O.SRFT, O.IDENTITY])
