@@ -320,7 +320,44 @@ __device__ __forceinline__ void store_lane_codes(char* cbase, char* sbase, int l
     *reinterpret_cast<uint4*>(cbase + static_cast<uint32_t>(lane * F::CB + 16 * q)) = c[q];
 }
 
-template <int ROT, int MODE, int FMT>
+// The same stores with the code rows turned around in LDS first (lds: at
+// least 64 * CB free bytes), so that every store instruction writes 1 KiB of
+// consecutive rows: row r goes to LDS row r with its NC = CB / 16 chunks
+// XOR-swizzled by (r NC / 16) mod NC (16 consecutive lanes then hit 16
+// distinct four-bank groups, both when a lane writes its row and when lanes
+// read chunk L mod NC of row L / NC); lane L stores chunk L mod NC of row
+// 64 i / NC + L / NC with instruction i.  Rows at or past nv are not stored.
+// One wave: its LDS reads follow its LDS writes in order.  The lane index
+// is laundered so that the addresses are formed here, not hoisted out of
+// the tile loop (where they would hold registers across the transform).
+template <typename F>
+__device__ __forceinline__ void store_codes_staged(char* cbase, char* sbase, int lane, int nv, uint8_t* lds,
+                                                   const uint4 (&c)[F::CB / 16], const uint32_t (&sw)[F::NG / 2]) {
+  constexpr int NC = F::CB / 16;
+  asm volatile("" : "+v"(lane));
+  const int sw_w = (lane * NC / 16) % NC;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) *reinterpret_cast<uint4*>(lds + lane * F::CB + 16 * (q ^ sw_w)) = c[q];
+  if (lane < nv) {
+    if (F::NG == 4) {
+      *reinterpret_cast<uint2*>(sbase + static_cast<uint32_t>(lane * F::SB)) = make_uint2(sw[0], sw[1]);
+    } else {
+      *reinterpret_cast<uint4*>(sbase + static_cast<uint32_t>(lane * F::SB)) =
+          make_uint4(sw[0], sw[1 % (F::NG / 2)], sw[2 % (F::NG / 2)], sw[3 % (F::NG / 2)]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int row = 64 / NC * i + lane / NC;
+    const int q = lane % NC;
+    const uint4 w = *reinterpret_cast<const uint4*>(lds + row * F::CB + 16 * (q ^ ((row * NC / 16) % NC)));
+    if (row < nv) *reinterpret_cast<uint4*>(cbase + static_cast<uint32_t>(1024 * i + 16 * lane)) = w;
+  }
+}
+
+// ONE: the grid has a wave per tile (no prefetch; the codes leave through
+// the free tile buffer).
+template <int ROT, int MODE, int FMT, bool ONE>
 __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
   using F = Fmt<FMT>;
   // separate LDS objects, so that reads of the masks and of lambda need not
@@ -380,14 +417,14 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
     // the tile is in registers: the buffer takes the next one
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t nxt = tile + gridDim.x;
-    if (nxt < a.n_tiles) {
+    if (!ONE && nxt < a.n_tiles) {
       const Tile tn = tile_info<128>(a, nxt);
       dma_tile128(a, tn, lds, lane, off4);
       const float* lr = a.lambda + tn.b * a.lambda_sb + tn.h * 128;
       lam_r0 = lr[lane];
       lam_r1 = lr[lane + 64];
     }
-    if (MODE == 0 && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
+    if (MODE == 0 && !ONE && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 
     float v[128];
     rotate_packed<ROT>(p, v);
@@ -457,9 +494,20 @@ __global__ void __launch_bounds__(64, 2) encode128_kernel(CodecArgs a) {
       for (int q = 0; q < F::CB / 16; ++q)
         pend_c[q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
       pend_valid = valid;
+      if (ONE) {
+        // the input tile is in registers and its LDS buffer is free: int8
+        // code rows (128 bytes) leave through it in 1 KiB stores (measured
+        // 11-13% faster); int4 rows (64 bytes) stream as well from the lane
+        if (F::CB == 128) {
+          store_codes_staged<F>(pend_cbase, pend_sbase, lane, t.nv, lds, pend_c, pend_s);
+        } else if (valid) {
+          store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
+        }
+        pend_valid = false;
+      }
     }
   }
-  if (MODE == 0 && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
+  if (MODE == 0 && !ONE && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -919,7 +967,7 @@ __device__ __forceinline__ uint32_t pair_mask256(const CodecArgs& a, int h, int 
 
 // MODE 0 writes codes and scales; MODE 1 writes the rotated values w =
 // lambda * R x in fp32 (the transform of this kernel, for checking).
-template <int ROT, int MODE, int FMT>
+template <int ROT, int MODE, int FMT, bool ONE>
 __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
   using F = Fmt<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
@@ -988,14 +1036,14 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     // the tile is in registers: the buffer takes the next one
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t nxt = tile + gridDim.x;
-    if (nxt < a.n_tiles) {
+    if (!ONE && nxt < a.n_tiles) {
       const Tile tn = tile_info<256>(a, nxt);
       dma_tile256<ROT>(a, tn, (lds_u8*)lds, lane);
       const float* lr = a.lambda + tn.b * a.lambda_sb + tn.h * 256;
 #pragma unroll
       for (int q = 0; q < 4; ++q) lam_r[q] = lr[lane + 64 * q];
     }
-    if (MODE == 0 && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
+    if (MODE == 0 && !ONE && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 
     float v[128];
     if (ROT == KVQ_ROT_SRFT) {
@@ -1083,8 +1131,18 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     for (int q = 0; q < F::CB / 16; ++q)
       pend_c[q] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
     pend_valid = valid;
+    if (ONE) {
+      // int8 half-vector code rows (row = lane) leave through the free tile
+      // buffer in 1 KiB stores, int4 rows from the lane
+      if (F::CB == 128) {
+        store_codes_staged<F>(pend_cbase, pend_sbase, lane, 2 * t.nv, lds, pend_c, pend_s);
+      } else if (valid) {
+        store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
+      }
+      pend_valid = false;
+    }
   }
-  if (MODE == 0 && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
+  if (MODE == 0 && !ONE && pend_valid) store_lane_codes<F>(pend_cbase, pend_sbase, lane, pend_c, pend_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1728,17 +1786,26 @@ hipError_t encode_dispatch(const CodecDesc& d, int mode) {
     }
     return hipGetLastError();
   }
+  const bool one = grid.x >= a.n_tiles;   // a wave per tile
   if (mode == 1) {
     // rotate only: the quantizer format plays no part
     if (D == 128) {
-      hipLaunchKernelGGL((encode128_kernel<ROT, 1, 0>), grid, dim3(64), 0, d.stream, a);
+      hipLaunchKernelGGL((encode128_kernel<ROT, 1, 0, false>), grid, dim3(64), 0, d.stream, a);
     } else {
-      hipLaunchKernelGGL((encode256_kernel<ROT, 1, 0>), grid, dim3(64), 0, d.stream, a);
+      hipLaunchKernelGGL((encode256_kernel<ROT, 1, 0, false>), grid, dim3(64), 0, d.stream, a);
     }
   } else if (D == 128) {
-    hipLaunchKernelGGL((encode128_kernel<ROT, 0, FMT>), grid, dim3(64), 0, d.stream, a);
+    if (one) {
+      hipLaunchKernelGGL((encode128_kernel<ROT, 0, FMT, true>), grid, dim3(64), 0, d.stream, a);
+    } else {
+      hipLaunchKernelGGL((encode128_kernel<ROT, 0, FMT, false>), grid, dim3(64), 0, d.stream, a);
+    }
   } else {
-    hipLaunchKernelGGL((encode256_kernel<ROT, 0, FMT>), grid, dim3(64), 0, d.stream, a);
+    if (one) {
+      hipLaunchKernelGGL((encode256_kernel<ROT, 0, FMT, true>), grid, dim3(64), 0, d.stream, a);
+    } else {
+      hipLaunchKernelGGL((encode256_kernel<ROT, 0, FMT, false>), grid, dim3(64), 0, d.stream, a);
+    }
   }
   return hipGetLastError();
 }

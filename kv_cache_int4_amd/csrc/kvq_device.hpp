@@ -272,13 +272,18 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 // the exact residual a - Q * q1.  Three instructions where a division takes
 // about ten; the result equals the IEEE quotient for every fp32 a (checked
 // on the host over every value of the subnormal range and of whole binades,
-// and the method scales exactly between binades).
+// and the method scales exactly between binades).  The quotient is held
+// opaque in a register: otherwise the compiler fuses the last fused
+// multiply-add with a following conversion to fp16 (v_fma_mixlo_f16), which
+// rounds once to fp16 where the scale is fp16 of the rounded fp32 quotient.
 template <int Q>
 __device__ __forceinline__ float div_by(float a) {
   constexpr float c = 1.0f / static_cast<float>(Q);
   const float q1 = __fmul_rn(a, c);
   const float r = fmaf(-q1, static_cast<float>(Q), a);
-  return fmaf(r, c, q1);
+  float q = fmaf(r, c, q1);
+  asm("" : "+v"(q));
+  return q;
 }
 
 // 1.5 * 2^23 + 8: adding it to w*r leaves rint_even(w*r) + 8 in the low

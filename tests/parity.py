@@ -149,7 +149,14 @@ def compare_codes(codes_gpu, scales_gpu, x16, lam, rotation, signs, G: int = O.G
     RECORDS.append(rec)
 
     if rotation == O.IDENTITY:
-        assert n_scale_bad == 0, f"{n_scale_bad} scale mismatches with no rotation (must be bit-exact)"
+        if n_scale_bad:
+            amax = np.abs(w.reshape(N, D // G, G)).max(-1).astype(np.float32)
+            sr = scales_ref.reshape(N, D // G).view(np.uint16)
+            cases = [f"(vector {i}, group {j}: absmax {amax[i, j]!r} = 0x{amax[i, j].view(np.uint32):08x}, "
+                     f"gpu 0x{sg.reshape(N, -1)[i, j]:04x}, oracle 0x{sr[i, j]:04x})"
+                     for i, j in np.argwhere(scale_bad.reshape(N, -1))[:4]]
+            raise AssertionError(f"{n_scale_bad} scale mismatches with no rotation (must be bit-exact): "
+                                 + ", ".join(cases))
         band = identity_band(bits)
         if n_code_bad:
             assert np.all(code_dist[code_bad] <= band), (
