@@ -219,18 +219,23 @@ def cpu_baseline(n_vec: int = 458752):
     }
 
 
-def timed_loop(torch, stream, fn, n, warm=3):
+def timed_loop(torch, stream, fn, n, warm=3, reps=3):
     """Microseconds per call of fn(i) over n back-to-back calls, with HIP
-    events on the kernels' stream."""
+    events on the kernels' stream: the median of reps such windows (a window
+    of a few hundred microseconds moves by 5-10% with the clock the power
+    manager picks for it)."""
     for i in range(warm):
         fn(i)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(n):
-        fn(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n * 1e3
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / n * 1e3)
+    return sorted(out)[len(out) // 2]
 
 
 def small_leg(K, W, torch, stream, dev, n):
@@ -358,15 +363,7 @@ def d256_leg(K, torch, stream, cfg, sets, n):
     ns = len(sets)
 
     def timed(fn):
-        for i in range(3):
-            fn(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n * 1e3
+        return timed_loop(torch, stream, fn, n)
 
     res = {"workload": "Gemma-3-1B-shaped prefix (26 layers x {K,V} x 1 KV head x 4096 tokens, D=256, "
                        "group 32)", "vectors": cfg.vectors, "bytes_per_call": nbytes}
@@ -399,15 +396,7 @@ def formats_leg(K, torch, stream, cfg, sets, dc, k16, v16, lam_k, lam_v, q, L, s
     ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device=q.device)
 
     def timed(fn):
-        for i in range(3):
-            fn(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n * 1e3
+        return timed_loop(torch, stream, fn, n)
 
     res = {}
     for name, bits, G in FORMATS:
@@ -464,15 +453,7 @@ def mixed_leg(K, W, torch, stream, dev, n_sets, n):
     over n_sets input batches."""
 
     def timed(fn):
-        for i in range(3):
-            fn(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n * 1e3
+        return timed_loop(torch, stream, fn, n)
 
     res = {"workload": "prefix shape 28 layers x {K,V} x 2 KV heads x 4096 tokens at D=96 and D=80, SRFT"}
     for key in ("d96", "d80"):
@@ -530,16 +511,7 @@ def graph_leg(K, torch, stream, plan, kv_new, lam_kv, lam_k, lam_v, cache, T0, q
     with torch.cuda.graph(g):
         step()
     torch.cuda.synchronize()
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(n):
-        g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n * 1e3
+    return timed_loop(torch, stream, lambda i: g.replay(), n)
 
 
 def log(msg):
@@ -649,17 +621,8 @@ def main():
     ms = {p: events[j].elapsed_time(events[j + 1]) / args.steps for j, p in enumerate(phases)}
 
     # ---- fp16-cache comparator, same shape ----
-    for _ in range(3):
-        K.attn_decode_f16(q, k16, v16, L, sm, out, ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n16 = max(5, args.steps // 2)
-    e0.record(stream)
-    for _ in range(n16):
-        K.attn_decode_f16(q, k16, v16, L, sm, out, ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    f16_us = e0.elapsed_time(e1) / n16 * 1e3
+    f16_us = timed_loop(torch, stream, lambda i: K.attn_decode_f16(q, k16, v16, L, sm, out, ws),
+                        max(5, args.steps // 2))
     # ---- the same decode step replayed from a captured HIP graph ----
     graph_us = graph_leg(K, torch, stream, aplan, kv_new, lam_kv, lam_k, lam_v, caches[0], T0, q, L, sm, out, ws,
                          max(10, args.steps))

@@ -1231,8 +1231,8 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)"
 //         (high nibble); one fma_mix removes the bias.
 //   int8: the byte with its top bit flipped is q + 128 (v_cvt_f32_ubyte),
 //         one fma removes the bias.
-template <typename F, int DPG>
-__device__ __forceinline__ void dequant_lane(const uint32_t (&cw)[F::CW], const uint32_t* s16, const float4* rl4,
+template <typename F, int DPG, typename Words>
+__device__ __forceinline__ void dequant_lane(const Words& cw, const uint32_t* s16, const float4* rl4,
                                              uint32_t magic, float (&v)[128]) {
   typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -1279,7 +1279,22 @@ __device__ __forceinline__ void dequant_lane(const uint32_t (&cw)[F::CW], const 
   }
 }
 
-template <int ROT, int FMT>
+// A lane's code words, read from the tile's LDS rows as they are used (the
+// decoders with a wave per tile: the buffer takes no next tile, and the
+// words need not all be held in registers at once).
+template <typename F>
+struct LdsWords {
+  const uint8_t* base;
+  int lane;
+  __device__ __forceinline__ uint32_t operator[](int d) const {
+    const uint4 w = *reinterpret_cast<const uint4*>(base + code_off_f<F>(lane, d / 4));
+    return (d % 4) == 0 ? w.x : (d % 4) == 1 ? w.y : (d % 4) == 2 ? w.z : w.w;
+  }
+};
+
+// ONE: the grid has a wave per tile (no prefetch; codes read from LDS as
+// the dequantization uses them).
+template <int ROT, int FMT, bool ONE>
 __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
   using F = Fmt<FMT>;
   using L = DecIn<F>;
@@ -1298,11 +1313,13 @@ __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
   __syncthreads();
   for (; tile < a.n_tiles; tile += gridDim.x) {
     const Tile t = tile_info<128>(a, tile);
-    uint32_t cw[F::CW];
+    uint32_t cw[ONE ? 1 : F::CW];
+    if (!ONE) {
 #pragma unroll
-    for (int q = 0; q < F::CB / 16; ++q) {
-      const uint4 w = *reinterpret_cast<const uint4*>(lds + L::kCodes + code_off_f<F>(lane, q));
-      cw[4 * q] = w.x; cw[4 * q + 1] = w.y; cw[4 * q + 2] = w.z; cw[4 * q + 3] = w.w;
+      for (int q = 0; q < F::CB / 16; ++q) {
+        const uint4 w = *reinterpret_cast<const uint4*>(lds + L::kCodes + code_off_f<F>(lane, q));
+        cw[4 * q] = w.x; cw[4 * q + 1] = w.y; cw[4 * q + 2] = w.z; cw[4 * q + 3] = w.w;
+      }
     }
     uint32_t s16[F::NG];
     if (F::SB == 8) {
@@ -1320,13 +1337,18 @@ __global__ void __launch_bounds__(64, 2) decode128_kernel(CodecArgs a) {
     const float l1 = reinterpret_cast<const float*>(lds + L::kLam)[lane + 64];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t nxt = tile + gridDim.x;
-    if (nxt < a.n_tiles) dma_codes128<F>(a, tile_info<128>(a, nxt), (lds_u8*)lds, lane);
+    if (!ONE && nxt < a.n_tiles) dma_codes128<F>(a, tile_info<128>(a, nxt), (lds_u8*)lds, lane);
     reinterpret_cast<float*>(work + kDecRl)[lane] = kScale * __builtin_amdgcn_rcpf(l0);
     reinterpret_cast<float*>(work + kDecRl)[lane + 64] = kScale * __builtin_amdgcn_rcpf(l1);
     lds_sync();
 
     float v[128];
-    dequant_lane<F, F::CW / F::NG>(cw, s16, reinterpret_cast<const float4*>(work + kDecRl), magic, v);
+    if (ONE) {
+      const LdsWords<F> words{lds + L::kCodes, lane};
+      dequant_lane<F, F::CW / F::NG>(words, s16, reinterpret_cast<const float4*>(work + kDecRl), magic, v);
+    } else {
+      dequant_lane<F, F::CW / F::NG>(cw, s16, reinterpret_cast<const float4*>(work + kDecRl), magic, v);
+    }
 
     if (ROT == KVQ_ROT_SRFT) fft64<true>(v);
     else if (ROT == KVQ_ROT_SRHT) wht128(v);
@@ -1823,7 +1845,11 @@ hipError_t decode_dispatch(const CodecDesc& d, bool f32) {
   if (f32) {
     hipLaunchKernelGGL((decode_f32_kernel<D, ROT, FMT>), grid, dim3(64), 0, d.stream, a);
   } else if (D == 128) {
-    hipLaunchKernelGGL((decode128_kernel<ROT, FMT>), grid, dim3(64), 0, d.stream, a);
+    if (grid.x >= a.n_tiles) {   // a wave per tile
+      hipLaunchKernelGGL((decode128_kernel<ROT, FMT, true>), grid, dim3(64), 0, d.stream, a);
+    } else {
+      hipLaunchKernelGGL((decode128_kernel<ROT, FMT, false>), grid, dim3(64), 0, d.stream, a);
+    }
   } else {
     hipLaunchKernelGGL((decode256_kernel<ROT, FMT>), grid, dim3(64), 0, d.stream, a);
   }
