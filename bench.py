@@ -238,9 +238,29 @@ def timed_loop(torch, stream, fn, n, warm=3, reps=3):
     return sorted(out)[len(out) // 2]
 
 
+def graph_loop(torch, stream, fn, n_calls=20, reps=10):
+    """GPU microseconds per call of fn(): n_calls calls captured in one HIP
+    graph, replayed reps times (the median replay), so that the host's own
+    per-call work does not pace the launches."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_calls):
+            fn()
+    torch.cuda.synchronize()
+    return timed_loop(torch, stream, lambda i: g.replay(), 1, warm=2, reps=reps) / n_calls
+
+
 def small_leg(K, W, torch, stream, dev, n):
     """The single-K-tensor round trip (2 KV heads x 256 tokens, D=128, 512
-    vectors): launch-latency bound, reported as microseconds per call."""
+    vectors): latency bound, reported as microseconds per call, both as
+    back-to-back calls from Python (paced by the host's per-call work) and
+    from a captured graph (the GPU's time per call, launch gaps included)."""
     cfg = W.CONFIGS["small"]
     x, lam = W.prefix_inputs(cfg, dev)
     plan = K.Plan(cfg.D, 32, "srft", cfg.sign_seed)
@@ -252,8 +272,14 @@ def small_leg(K, W, torch, stream, dev, n):
     dec = timed_loop(torch, stream, lambda i: K.decode(plan, codes, scales, lam, y), n)
     rt = timed_loop(torch, stream, lambda i: (K.encode(plan, x, lam, codes, scales),
                                               K.decode(plan, codes, scales, lam, y)), n)
+    enc_g = graph_loop(torch, stream, lambda: K.encode(plan, x, lam, codes, scales))
+    dec_g = graph_loop(torch, stream, lambda: K.decode(plan, codes, scales, lam, y))
+    rt_g = graph_loop(torch, stream, lambda: (K.encode(plan, x, lam, codes, scales),
+                                              K.decode(plan, codes, scales, lam, y)), n_calls=10)
     return {"workload": "single K tensor, 2 KV heads x 256 tokens, D=128, SRFT (512 vectors)",
-            "encode_us": round(enc, 2), "decode_us": round(dec, 2), "round_trip_us": round(rt, 2)}
+            "encode_us": round(enc, 2), "decode_us": round(dec, 2), "round_trip_us": round(rt, 2),
+            "graph_encode_us": round(enc_g, 2), "graph_decode_us": round(dec_g, 2),
+            "graph_round_trip_us": round(rt_g, 2)}
 
 
 def mistral_leg(K, W, torch, stream, dev, n_rep):
@@ -323,6 +349,7 @@ def attn256_leg(K, W, torch, stream, dev, n):
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     sm = 1.0 / math.sqrt(D)
     app = timed_loop(torch, stream, lambda i: K.encode(plan, kv_new, lam_kv, kvc, kvs, T0), n)
+    app_g = graph_loop(torch, stream, lambda: K.encode(plan, kv_new, lam_kv, kvc, kvs, T0))
     att = timed_loop(torch, stream, lambda i: K.attn_decode(plan, q, kvc[:B], kvs[:B], lam_k, kvc[B:], kvs[B:],
                                                             lam_v, L, sm, out, ws), n)
     f16 = timed_loop(torch, stream, lambda i: K.attn_decode_f16(q, k16, v16, L, sm, out, ws), max(5, n // 2))
@@ -331,7 +358,8 @@ def attn256_leg(K, W, torch, stream, dev, n):
     return {
         "workload": "decode step at Gemma-3-1B head shape: batch 64, Hq 4 / Hkv 1, D=256, 32768 cached tokens + 1 "
                     "appended, SRFT, group 32",
-        "append_us": round(app, 2), "int4_attn_us": round(att, 2), "int4_us_per_step": round(app + att, 2),
+        "append_us": round(app, 2), "append_graph_us": round(app_g, 2), "int4_attn_us": round(att, 2),
+        "int4_us_per_step": round(app + att, 2),
         "int4_attn_bytes": ab, "int4_attn_frac_hbm": round(ab / att / 1e3 / HBM_PEAK_GBS, 4),
         "fp16_us_per_step": round(f16, 2), "fp16_frac_hbm": round(fb / f16 / 1e3 / HBM_PEAK_GBS, 4),
         "int4_over_fp16": round((app + att) / f16, 4),
@@ -624,6 +652,7 @@ def main():
     f16_us = timed_loop(torch, stream, lambda i: K.attn_decode_f16(q, k16, v16, L, sm, out, ws),
                         max(5, args.steps // 2))
     # ---- the same decode step replayed from a captured HIP graph ----
+    append_g = graph_loop(torch, stream, lambda: K.encode(aplan, kv_new, lam_kv, caches[0][4], caches[0][5], T0))
     graph_us = graph_leg(K, torch, stream, aplan, kv_new, lam_kv, lam_k, lam_v, caches[0], T0, q, L, sm, out, ws,
                          max(10, args.steps))
     # ---- D=256 (Gemma-3-1B-shaped prefix), both rotations, timed apart ----
@@ -723,7 +752,7 @@ def main():
                       "fp16_us_per_step": round(f16_us, 2),
                       "fp16_GB_s": round(attn16_bytes / (f16_us / 1e6) / 1e9, 1),
                       "int4_over_fp16": round(attn_us / f16_us, 4),
-                      "graph_us_per_step": round(graph_us, 2)},
+                      "graph_us_per_step": round(graph_us, 2), "append_graph_us": round(append_g, 2)},
         "d256": gemma,
         "attention_d256": att256,
         "formats": fmts,

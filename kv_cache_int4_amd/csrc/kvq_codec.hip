@@ -1744,6 +1744,355 @@ __global__ void __launch_bounds__(64, 2) decode_f32_kernel(CodecArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small calls: one wave per vector, its transform spread over the 64 lanes.
+// A call of a few thousand vectors (the append of one token per sequence of
+// a decode step, a short prompt) is bound by latency, not bandwidth: the tile
+// kernels run a vector's whole transform in one lane (about 1.7k dependent
+// instructions).  Here lane l holds complex pair l (and pair l + 64 at
+// D = 256), the transform runs as radix-2 steps across the lanes (a
+// cross-lane read and a few operations per step), the group abs-max is a
+// cross-lane reduction, and each lane quantizes and stores its own channels.
+// Same arithmetic contract as the tile kernels: fp32 transform, sigma =
+// fp16 of the fp32 quotient, magic-number rounding with the clamp.
+// ---------------------------------------------------------------------------
+__constant__ TwTable kSmTw = make_twiddles(128);
+
+__device__ __forceinline__ float xlane(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Bit reversal of a 6-bit index.
+__device__ __forceinline__ int brev6(int l) { return static_cast<int>(__builtin_bitreverse32(l) >> 26); }
+
+// N complex values per lane: the unnormalized 64-point DFT across the lanes,
+// as radix-2 steps over the lane index.  Forward (kernel exp(-2 pi i / 64)):
+// decimation in frequency, lane l starts with element l and ends with
+// frequency bitrev(l).  INV: the steps in the opposite order with conjugate
+// twiddles, each the inverse of the forward step times 2, so frequency
+// bitrev(l) in lane l goes to 64 times element l of the inverse transform,
+// i.e. the conjugate-kernel DFT in natural order.
+template <bool INV, int N>
+__device__ __forceinline__ void dft64_lanes(float (&re)[N], float (&im)[N], int lane) {
+#pragma unroll
+  for (int st = 0; st < 6; ++st) {
+    const int h = INV ? (1 << st) : (32 >> st);
+    const bool bot = (lane & h) != 0;
+    const int e = (lane & (h - 1)) * (32 / h);        // W_64^e on the pair's upper element
+    const float sgn = bot ? -1.f : 1.f;
+    const float c = bot ? kSmTw.c[2 * e] : 1.f;
+    const float sn = bot ? (INV ? -kSmTw.s[2 * e] : kSmTw.s[2 * e]) : 0.f;
+    if (INV) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) {            // (re + i im)(c + i s) on the upper lane
+        const float r2 = fmaf(re[n], c, im[n] * sn);
+        const float i2 = fmaf(im[n], c, -(re[n] * sn));
+        re[n] = r2;
+        im[n] = i2;
+      }
+    }
+    float pr[N], pi[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      pr[n] = xlane(re[n], h);
+      pi[n] = xlane(im[n], h);
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) {                // lower lane x + p, upper lane p - x
+      re[n] = fmaf(re[n], sgn, pr[n]);
+      im[n] = fmaf(im[n], sgn, pi[n]);
+    }
+    if (!INV) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) {            // (re + i im)(c - i s) on the upper lane
+        const float r2 = fmaf(re[n], c, im[n] * sn);
+        const float i2 = fmaf(im[n], c, -(re[n] * sn));
+        re[n] = r2;
+        im[n] = i2;
+      }
+    }
+  }
+}
+
+// Sylvester Walsh-Hadamard steps over the lane bits (channel bits 1..6 when
+// lane l holds channels 2l, 2l+1): the lower lane keeps x + p, the upper p - x.
+template <int N>
+__device__ __forceinline__ void wht_lanes(float (&v)[N], int lane) {
+#pragma unroll
+  for (int h = 1; h < 64; h *= 2) {
+    const float sgn = (lane & h) ? -1.f : 1.f;
+    float p[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) p[n] = xlane(v[n], h);
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] = fmaf(v[n], sgn, p[n]);
+  }
+}
+
+// Where a lane's NC = D / 64 values live after the forward transform.
+// SRFT: lane l holds Z_m, m = bitrev(l) (D = 128: channels 2m, 2m+1;
+// D = 256: Z_2m, Z_2m+1, channels 4m .. 4m+3), all in one group; the lanes
+// of a group share the low log2(D / G) lane bits.  SRHT and no rotation:
+// channels 2l, 2l+1 (and 128 + 2l, 129 + 2l), in one group per half; the
+// lanes of a group share the high lane bits.
+template <int D, int ROT, int G>
+struct SmallLayout {
+  static constexpr int NC = D / 64;
+  static constexpr bool FREQ = ROT == KVQ_ROT_SRFT;
+  static constexpr int SLOTS = FREQ ? 1 : D / 128;      // groups per lane
+  static constexpr int PER_SLOT = NC / SLOTS;
+  __device__ static int chan(int lane, int j) {
+    if (FREQ) return NC * brev6(lane) + j;
+    return 128 * (j / 2) + 2 * lane + (j & 1);
+  }
+  // the smallest and largest lane-index XOR that stays in the group
+  static constexpr int MASK_LO = FREQ ? D / G : 1;
+  static constexpr int MASK_HI = FREQ ? 32 : G / 4;
+  // a lane of each group, the one that stores the scale
+  __device__ static bool rep(int lane) { return FREQ ? lane < D / G : (lane % (G / 2)) == 0; }
+};
+
+template <int D, int ROT>
+__device__ __forceinline__ uint32_t small_pair_mask(const uint64_t (&s)[4], int k) {
+  if (ROT == KVQ_ROT_SRFT) return sign_bit(s, k) ? 0x80008000u : 0u;
+  if (ROT == KVQ_ROT_SRHT) return (sign_bit(s, 2 * k) << 15) | (sign_bit(s, 2 * k + 1) << 31);
+  return 0u;
+}
+
+// Forward transform of one vector: lane l loads pair words l (and l + 64),
+// applies the signs and leaves its NC values in SmallLayout order,
+// unnormalized.
+template <int D, int ROT>
+__device__ __forceinline__ void small_forward(const CodecArgs& a, const uint16_t* xr, int lane, float (&v)[D / 64]) {
+  constexpr int NP = D / 128;
+  float re[NP], im[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int k = lane + 64 * j;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(xr + 2 * k) ^ small_pair_mask<D, ROT>(a.signs, k);
+    re[j] = f16_bits_to_f32(w & 0xFFFFu);
+    im[j] = f16_bits_to_f32(w >> 16);
+  }
+  if (ROT == KVQ_ROT_SRFT) {
+    if (D == 256) {
+      // first radix-2 step of the 128-point DIF, inside the lane: u = A + B,
+      // w = (A - B) W_128^l; the 64-point transforms of u and w are the even
+      // and the odd frequencies
+      const float c = kSmTw.c[lane], sn = kSmTw.s[lane];
+      const float ur = re[0] + re[NP - 1], ui = im[0] + im[NP - 1];
+      const float dr = re[0] - re[NP - 1], di = im[0] - im[NP - 1];
+      re[0] = ur;
+      im[0] = ui;
+      re[NP - 1] = fmaf(dr, c, di * sn);
+      im[NP - 1] = fmaf(di, c, -(dr * sn));
+    }
+    dft64_lanes<false, NP>(re, im, lane);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      v[2 * j] = re[j];
+      v[2 * j + 1] = im[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      v[2 * j] = re[j];
+      v[2 * j + 1] = im[j];
+    }
+    if (ROT == KVQ_ROT_SRHT) {
+      if (D == 256) {                       // channel bit 7: the two halves
+        const float a0 = v[0], a1 = v[1];
+        v[0] = a0 + v[2];
+        v[1] = a1 + v[3];
+        v[2] = a0 - v[2];
+        v[3] = a1 - v[3];
+      }
+#pragma unroll
+      for (int j = 0; j < D / 64; j += 2) { // channel bit 0, inside the lane
+        const float a0 = v[j];
+        v[j] = a0 + v[j + 1];
+        v[j + 1] = a0 - v[j + 1];
+      }
+      wht_lanes<D / 64>(v, lane);
+    }
+  }
+}
+
+template <int D, int ROT, int FMT, int MODE>
+__global__ void __launch_bounds__(64) encode_small_kernel(CodecArgs a) {
+  using F = Fmt<FMT>;
+  using Lay = SmallLayout<D, ROT, F::G>;
+  constexpr int NC = Lay::NC;
+  constexpr float kScale = rot_scale<D, ROT>();
+  constexpr int CBV = D * F::BITS / 8;           // code bytes per vector
+  constexpr int NGV = D / F::G;                  // groups per vector
+  const int lane = threadIdx.x;
+  const int64_t vi = blockIdx.x;
+  const int64_t t = vi % a.T;
+  const int64_t bh = vi / a.T;
+  const int64_t h = bh % a.H;
+  const int64_t b = bh / a.H;
+  const uint16_t* xr = a.x + b * a.sb + h * a.sh + t * a.st;
+  const float* lr = a.lambda + b * a.lambda_sb + h * D;
+
+  float v[NC];
+  small_forward<D, ROT>(a, xr, lane, v);
+  float wv[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) wv[j] = v[j] * lr[Lay::chan(lane, j)];
+  if (MODE == 1) {
+    float* wr = a.w + ((b * a.H + h) * a.T + t) * D;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) wr[Lay::chan(lane, j)] = wv[j] * kScale;
+    return;
+  }
+  const int64_t cell = (b * a.H + h) * a.Tcap + a.t0 + t;
+  uint8_t* cr = a.codes + cell * CBV;
+  uint16_t* sr = a.scales + cell * NGV;
+  uint32_t byte[NC];
+#pragma unroll
+  for (int sl = 0; sl < Lay::SLOTS; ++sl) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = sl * Lay::PER_SLOT; j < (sl + 1) * Lay::PER_SLOT; ++j) amax = fmaxf(amax, fabsf(wv[j]));
+#pragma unroll
+    for (int m = Lay::MASK_LO; m <= Lay::MASK_HI; m *= 2) amax = fmaxf(amax, xlane(amax, m));
+    const uint32_t sc = f32_to_f16_bits(div_by<F::IQMAX>(amax * kScale));
+    const float sf = f16_bits_to_f32(sc);
+    const float r = sf > 0.f ? kScale * __builtin_amdgcn_rcpf(sf) : 0.f;
+    const int j0 = sl * Lay::PER_SLOT;
+    if (Lay::rep(lane)) sr[Lay::chan(lane, j0) / F::G] = static_cast<uint16_t>(sc);
+#pragma unroll
+    for (int j = j0; j < j0 + Lay::PER_SLOT; ++j)
+      byte[j] = F::BITS == 4 ? quant_bits(wv[j], r) : ((quant_bits8(wv[j], r) & 0xFFu) ^ 0x80u);
+  }
+  // the lane's channels are consecutive in runs of two (four for SRFT at
+  // D = 256): int4 one byte per two channels, int8 one per channel
+#pragma unroll
+  for (int j = 0; j < NC; j += (Lay::FREQ ? NC : 2)) {
+    const int ch = Lay::chan(lane, j);
+    if (F::BITS == 4) {
+      if (Lay::FREQ && NC == 4) {
+        const uint32_t lo = pair_byte(byte[0], byte[1]) & 0xFFu, hi = pair_byte(byte[2], byte[3]) & 0xFFu;
+        *reinterpret_cast<uint16_t*>(cr + ch / 2) = static_cast<uint16_t>(lo | (hi << 8));
+      } else {
+        cr[ch / 2] = static_cast<uint8_t>(pair_byte(byte[j], byte[j + 1]) & 0xFFu);
+      }
+    } else {
+      if (Lay::FREQ && NC == 4) {
+        *reinterpret_cast<uint32_t*>(cr + ch) = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
+      } else {
+        *reinterpret_cast<uint16_t*>(cr + ch) = static_cast<uint16_t>(byte[j] | (byte[j + 1] << 8));
+      }
+    }
+  }
+}
+
+template <int D, int ROT, int FMT, bool F32>
+__global__ void __launch_bounds__(64) decode_small_kernel(CodecArgs a) {
+  using F = Fmt<FMT>;
+  using Lay = SmallLayout<D, ROT, F::G>;
+  constexpr int NC = Lay::NC;
+  constexpr int NP = D / 128;
+  constexpr float kScale = rot_scale<D, ROT>();
+  constexpr int CBV = D * F::BITS / 8;
+  constexpr int NGV = D / F::G;
+  const int lane = threadIdx.x;
+  const int64_t vi = blockIdx.x;
+  const int64_t t = vi % a.T;
+  const int64_t bh = vi / a.T;
+  const int64_t h = bh % a.H;
+  const int64_t b = bh / a.H;
+  const float* lr = a.lambda + b * a.lambda_sb + h * D;
+  const int64_t cell = (b * a.H + h) * a.Tcap + a.t0 + t;
+  const uint8_t* cr = a.codes_in + cell * CBV;
+  const uint16_t* sr = a.scales_in + cell * NGV;
+
+  // codes of the lane's channels, as signed integers
+  int q[NC];
+#pragma unroll
+  for (int j = 0; j < NC; j += (Lay::FREQ ? NC : 2)) {
+    const int ch = Lay::chan(lane, j);
+    const int run = Lay::FREQ ? NC : 2;
+    if (F::BITS == 4) {
+      uint32_t bytes = run == 4 ? *reinterpret_cast<const uint16_t*>(cr + ch / 2) : cr[ch / 2];
+#pragma unroll
+      for (int u = 0; u < run; ++u) q[j + u] = static_cast<int>((bytes >> (4 * u)) & 0xFu) - 8;
+    } else {
+      const uint32_t bytes = run == 4 ? *reinterpret_cast<const uint32_t*>(cr + ch)
+                                      : *reinterpret_cast<const uint16_t*>(cr + ch);
+#pragma unroll
+      for (int u = 0; u < run; ++u) q[j + u] = static_cast<int>(static_cast<int8_t>((bytes >> (8 * u)) & 0xFFu));
+    }
+  }
+  float v[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int ch = Lay::chan(lane, j);
+    const float sg = f16_bits_to_f32(sr[ch / F::G]);
+    v[j] = static_cast<float>(q[j]) * sg * (kScale * __builtin_amdgcn_rcpf(lr[ch]));
+  }
+  // inverse transform: lane l ends with channels 2l, 2l+1 (and 128 + 2l,
+  // 129 + 2l)
+  float o[NC];
+  if (ROT == KVQ_ROT_SRFT) {
+    float re[NP], im[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      re[j] = v[2 * j];
+      im[j] = v[2 * j + 1];
+    }
+    dft64_lanes<true, NP>(re, im, lane);
+    if (D == 256) {
+      // the inverse of the first radix-2 step: A = U + W V, B = U - W V,
+      // W = conj(W_128^l)
+      const float c = kSmTw.c[lane], sn = -kSmTw.s[lane];
+      const float wr = fmaf(re[NP - 1], c, im[NP - 1] * sn), wi = fmaf(im[NP - 1], c, -(re[NP - 1] * sn));
+      const float ur = re[0], ui = im[0];
+      re[0] = ur + wr;
+      im[0] = ui + wi;
+      re[NP - 1] = ur - wr;
+      im[NP - 1] = ui - wi;
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      o[2 * j] = re[j];
+      o[2 * j + 1] = im[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) o[j] = v[j];
+    if (ROT == KVQ_ROT_SRHT) {
+      if (D == 256) {
+        const float a0 = o[0], a1 = o[1];
+        o[0] = a0 + o[2];
+        o[1] = a1 + o[3];
+        o[2] = a0 - o[2];
+        o[3] = a1 - o[3];
+      }
+#pragma unroll
+      for (int j = 0; j < NC; j += 2) {
+        const float a0 = o[j];
+        o[j] = a0 + o[j + 1];
+        o[j + 1] = a0 - o[j + 1];
+      }
+      wht_lanes<NC>(o, lane);
+    }
+  }
+  // signs, then the row: pair k = lane + 64 j at element 2 k
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int k = lane + 64 * j;
+    const uint32_t m = small_pair_mask<D, ROT>(a.signs, k);
+    const float y0 = (m & 0x8000u) ? -o[2 * j] : o[2 * j];
+    const float y1 = (m & 0x80000000u) ? -o[2 * j + 1] : o[2 * j + 1];
+    if (F32) {
+      float* yr = static_cast<float*>(a.y) + b * a.sb + h * a.sh + t * a.st;
+      *reinterpret_cast<float2*>(yr + 2 * k) = make_float2(y0, y1);
+    } else {
+      uint16_t* yr = static_cast<uint16_t*>(a.y) + b * a.sb + h * a.sh + t * a.st;
+      *reinterpret_cast<uint32_t*>(yr + 2 * k) = pack_f16x2(y0, y1);
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1789,6 +2138,15 @@ void fill_common(CodecArgs& a, const CodecDesc& d) {
 // Format index of a call: 2 * (bits == 8) + (G == 16).
 int format_of(const CodecDesc& d) { return (d.bits == 8 ? 2 : 0) + (d.G == 16 ? 1 : 0); }
 
+// Calls of at most this many vectors take the one-wave-per-vector kernels
+// (measured from graph replays on an MI355X: at 256-2048 vectors they take
+// 3-4 us where the tile kernels take 6-7.5, and they stop winning near 6k
+// vectors at D = 128, 8k at D = 256).
+template <int D>
+constexpr int64_t small_limit() {
+  return D == 128 ? 4096 : 8192;
+}
+
 template <int D, int ROT, int FMT>
 hipError_t encode_dispatch(const CodecDesc& d, int mode) {
   CodecArgs a{};
@@ -1798,6 +2156,17 @@ hipError_t encode_dispatch(const CodecDesc& d, int mode) {
   a.scales = d.scales;
   a.w = d.w;
   if (a.n_tiles == 0) return hipSuccess;
+  const int64_t n_vec = d.B * d.H * d.T;
+  if (d.options == 0 && n_vec <= small_limit<D>()) {
+    if (mode == 1) {
+      hipLaunchKernelGGL((encode_small_kernel<D, ROT, 0, 1>), dim3(static_cast<unsigned>(n_vec)), dim3(64), 0,
+                         d.stream, a);
+    } else {
+      hipLaunchKernelGGL((encode_small_kernel<D, ROT, FMT, 0>), dim3(static_cast<unsigned>(n_vec)), dim3(64), 0,
+                         d.stream, a);
+    }
+    return hipGetLastError();
+  }
   if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
   const dim3 grid(static_cast<unsigned>(launch_grid(a.n_tiles, true)));
   if (D == 128 && ROT == KVQ_ROT_SRFT && (d.options & kOptMfmaRotation)) {
@@ -1840,6 +2209,17 @@ hipError_t decode_dispatch(const CodecDesc& d, bool f32) {
   a.scales_in = d.scales_in;
   a.y = d.y;
   if (a.n_tiles == 0) return hipSuccess;
+  const int64_t n_vec = d.B * d.H * d.T;
+  if (n_vec <= small_limit<D>()) {
+    if (f32) {
+      hipLaunchKernelGGL((decode_small_kernel<D, ROT, FMT, true>), dim3(static_cast<unsigned>(n_vec)), dim3(64), 0,
+                         d.stream, a);
+    } else {
+      hipLaunchKernelGGL((decode_small_kernel<D, ROT, FMT, false>), dim3(static_cast<unsigned>(n_vec)), dim3(64),
+                         0, d.stream, a);
+    }
+    return hipGetLastError();
+  }
   if (a.n_tiles >= (int64_t(1) << 32)) return hipErrorInvalidValue;   // index math is 32-bit exact
   const dim3 grid(static_cast<unsigned>(launch_grid(a.n_tiles, false)));
   if (f32) {

@@ -20,7 +20,7 @@ import oracle as O
 import kv_cache_int4_amd as K
 from kv_cache_int4_amd import workloads as W
 from tests import parity as P
-from tests.test_gpu_parity import ROTS, check_encode, lam_per_vector, np16, run_attn, say
+from tests.test_gpu_parity import batch_for, ROTS, check_encode, lam_per_vector, np16, run_attn, say
 
 pytestmark = pytest.mark.gpu
 
@@ -59,13 +59,15 @@ def decode_both(plan, rot, codes_d, scales_d, c, s, lam, B, H, T, t0=0):
 @pytest.mark.parametrize("fmt", sorted(FORMATS))
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("rot", ["srft", "srht", "identity"])
-@pytest.mark.parametrize("T", [63, 130])
-def test_format_ragged_offsets_strides(fmt, D, rot, T):
+@pytest.mark.parametrize("T,path", [(63, "lanes"), (130, "lanes"), (130, "tiles")])
+def test_format_ragged_offsets_strides(fmt, D, rot, T, path):
     """Ragged tails, a write offset inside a larger cache, strided input rows
-    and a lambda table shared across the batch."""
+    and a lambda table shared across the batch; on the one-wave-per-vector
+    path (small calls) and on the tile path."""
     bits, G = FORMATS[fmt]
     g = W.gen("cpu", 91, D, T)
-    B, H = 3, 2
+    H = 2
+    B = batch_for(path, H, T)
     base = torch.randn((B, H, T + 5, D + 24), generator=g).to(torch.float16) * 3
     x = base[:, :, 2:2 + T, 8:8 + D]
     lam = torch.exp(0.3 * torch.randn((H, D), generator=g))

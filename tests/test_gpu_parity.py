@@ -145,14 +145,26 @@ def test_gemma_prefix_full(rot):
     say(f"   decode fp16: {r}")
 
 
+# Calls of a few thousand vectors or fewer run one wave per vector, larger
+# ones the tile kernels: batch sizes that put a call on either path.
+PATH_VECTORS = 8200
+
+
+def batch_for(path: str, H: int, T: int) -> int:
+    return 3 if path == "lanes" else PATH_VECTORS // (H * T) + 1
+
+
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("rot", ["srft", "srht", "identity"])
-@pytest.mark.parametrize("T", [1, 63, 65, 130])
-def test_ragged_tokens_offsets_strides(D, rot, T):
+@pytest.mark.parametrize("T,path", [(1, "lanes"), (63, "lanes"), (65, "lanes"), (130, "lanes"), (1, "tiles"),
+                                    (63, "tiles"), (130, "tiles")])
+def test_ragged_tokens_offsets_strides(D, rot, T, path):
     """Ragged tails, a write offset inside a larger cache, strided input rows
-    and a lambda table shared across the batch."""
+    and a lambda table shared across the batch; on the one-wave-per-vector
+    path (small calls) and on the tile path."""
     g = W.gen("cpu", 77, D, T)
-    B, H = 3, 2
+    H = 2
+    B = batch_for(path, H, T)
     base = torch.randn((B, H, T + 5, D + 24), generator=g).to(torch.float16) * 3
     x = base[:, :, 2:2 + T, 8:8 + D]            # strides (H*(T+5)*(D+24), ...), row stride D+24
     lam = torch.exp(0.3 * torch.randn((H, D), generator=g))
