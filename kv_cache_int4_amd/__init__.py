@@ -100,8 +100,13 @@ def _check(status: int) -> None:
 
 
 def _stream(idx: int) -> int:
-    """The current HIP stream of device idx."""
+    """The current HIP stream of device idx (torch's raw-handle getter where
+    it has one: a call costs a fraction of building a Stream object, which
+    matters for calls of a few microseconds)."""
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(idx)
     return torch.cuda.current_stream(idx).cuda_stream
 
 
