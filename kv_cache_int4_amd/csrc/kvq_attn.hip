@@ -20,10 +20,10 @@
 //               streams its slice of the cache 32 tokens at a time:
 //                 QK (int4): v_mfma_i32_16x16x64_i8, rows = 16 tokens,
 //                   columns = (channel group, head) pairs, so every lane
-//                   holds useful scores.  The codes enter as unsigned
-//                   nibbles (n = q + 8, one AND and one shift per word); the
-//                   -8 offset is the accumulator's initial value, and the
-//                   group scale multiplies the exact integer result.
+//                   holds useful scores.  The codes enter as signed bytes
+//                   16 q (each nibble moved to the top of its byte, top bit
+//                   flipped: a shift and one bit operation per word), and
+//                   the group scale multiplies the exact integer result.
 //                 QK (fp16): v_mfma_f32_16x16x32_f16 on the fp16 keys.
 //                 softmax: online, base 2, exact running maximum.
 //                 PV: v_mfma_f32_16x16x32_f16.  For the int4 cache the rows
@@ -68,13 +68,10 @@ constexpr int kBlk = 32;              // tokens per inner step
 // per channel, q~ ~= s (Q1 + Q2 / 256 + Q3 / 65536):
 //   [0, 384 NH)        limbs Q1, Q2, Q3, 128 NH bytes each, channel order
 //   [384 NH, 400 NH)   s[4 NH] f32, one per 32-channel group
-//   [400 NH, 448 NH)   sums of Q1, Q2, Q3 per group, i32[3][4 NH]
-//   [448 NH, 544 NH)   groups of 16: sums per 16 channels, i32[3][8 NH]
 template <int NH>
 struct Rec {
   static constexpr int S = 384 * NH;
-  static constexpr int SUM = 400 * NH;
-  static constexpr int SUM16 = 448 * NH;
+  static constexpr int BYTES = 400 * NH;
 };
 
 __constant__ TwTable kTw64Const = make_twiddles(64);
@@ -183,9 +180,8 @@ __device__ __forceinline__ void query_loads(const AttnArgs& a, const uint16_t* q
 // one wave from the pair words in.w: lane l owns channels 128 hf + 2 l,
 // 128 hf + 2 l + 1 of every head and half.  The heads advance together
 // through each cross-lane step (independent shuffles per wait); the records
-// go to LDS at rec + head * REC (with the per-16-channel limb sums when
-// SUM16).
-template <int ROT, int REC, bool SUM16, int NH>
+// go to LDS at rec + head * Rec<NH>::BYTES.
+template <int ROT, int NH>
 __device__ __forceinline__ void query_records(const AttnArgs& a, const QueryIn& in, int lane, uint8_t* rec) {
   constexpr int NHD = kHeadsPerWave;
   using RL = Rec<NH>;
@@ -338,43 +334,14 @@ __device__ __forceinline__ void query_records(const AttnArgs& a, const QueryIn& 
         li[h][2][e] = static_cast<int>(r3);
       }
     }
-    float sum[NHD][3];
-#pragma unroll
-    for (int h = 0; h < NHD; ++h)
-#pragma unroll
-      for (int limb = 0; limb < 3; ++limb) sum[h][limb] = static_cast<float>(li[h][limb][0] + li[h][limb][1]);
-    float sum16[NHD][3];      // after the steps over 8 lanes: sums per 16 channels
-#pragma unroll
-    for (int m = 1; m <= 8; m <<= 1) {
-      if (m == 8) {
-#pragma unroll
-        for (int h = 0; h < NHD; ++h)
-#pragma unroll
-          for (int limb = 0; limb < 3; ++limb) sum16[h][limb] = sum[h][limb];
-      }
-      float o[NHD][3];
-#pragma unroll
-      for (int h = 0; h < NHD; ++h)
-#pragma unroll
-        for (int limb = 0; limb < 3; ++limb) o[h][limb] = shfl_xor(sum[h][limb], m);
-#pragma unroll
-      for (int h = 0; h < NHD; ++h)
-#pragma unroll
-        for (int limb = 0; limb < 3; ++limb) sum[h][limb] += o[h][limb];
-    }
     const int gi = 4 * hf + grp;            // 32-channel group of the head vector
 #pragma unroll
     for (int h = 0; h < NHD; ++h) {
-      uint8_t* r = rec + h * REC;
+      uint8_t* r = rec + h * RL::BYTES;
 #pragma unroll
       for (int limb = 0; limb < 3; ++limb) {
         reinterpret_cast<uint16_t*>(r + 128 * NH * limb + 128 * hf)[lane] =
             static_cast<uint16_t>((li[h][limb][0] & 0xFF) | ((li[h][limb][1] & 0xFF) << 8));
-        if ((lane & 15) == 0)
-          reinterpret_cast<int*>(r + RL::SUM)[4 * NH * limb + gi] = static_cast<int>(sum[h][limb]);
-        if (SUM16 && (lane & 7) == 0)
-          reinterpret_cast<int*>(r + RL::SUM16)[8 * NH * limb + 8 * hf + (lane >> 3)] =
-              static_cast<int>(sum16[h][limb]);
       }
       if ((lane & 15) == 0) reinterpret_cast<float*>(r + RL::S)[gi] = amax[h] > 0.f ? amax[h] / 127.f : 0.f;
     }
@@ -543,7 +510,6 @@ struct QF {
   static constexpr int CBT = NH * HB;           // code bytes per token
   static constexpr int HS = G16 ? 16 : 8;       // scale bytes per token and half
   static constexpr int SBT = NH * HS;           // scale bytes per token
-  static constexpr int REC = NH * (G16 ? 544 : 448);   // query record bytes
 };
 
 // Lane (n16, kq), n16 = 4 g + h: QK column (32-channel slice g of each half,
@@ -647,8 +613,6 @@ __device__ __forceinline__ void load4(const Rows& r, uint32_t t0, uint32_t t_las
 template <int NH>
 struct StateQ {
   int4_t qb[NH][3][2];       // QK right operand: [half][limb][k-step]
-  int4_t corr[NH][3];        // int4 accumulator start: -8 * sum(Q) per limb
-  int4_t corr1[NH][3];       // int4 in groups of 16: the same for k-step 1
   float sfac[NH];            // s / 256 of column (group, head) in each half
   float4_t acc[NH][8];       // PV accumulators, MFMA c <-> channel 128 hf + 8 n16 + c
   float m_run;               // running max of this lane's head
@@ -663,14 +627,20 @@ __device__ __forceinline__ float quad_bcast(float x) {
 }
 
 // Combined QK score of one column from its three limb accumulators: 256 c1
-// + c2 is exact in int32; the third limb joins in fp32.
+// + c2 is exact in int32; the third limb joins in fp32.  BITS = 4: the codes
+// entered as 16 q, every sum is a multiple of 16, and the result is 16 times
+// the score (the shift by 4 is exact, so is 256 c1 + c2 as a float).
+template <int BITS>
 __device__ __forceinline__ float limb_score(const int4_t& c1, const int4_t& c2, const int4_t& c3, int i) {
+  if (BITS == 4) return fmaf(static_cast<float>((c1[i] * 256 + c2[i]) >> 4), 4096.f, static_cast<float>(c3[i]));
   return fmaf(static_cast<float>(c1[i] * 256 + c2[i]), 256.f, static_cast<float>(c3[i]));
 }
 
-// Low / high nibbles of the four bytes of a word as int8 lanes.
-__device__ __forceinline__ int lo_nib(uint32_t x) { return static_cast<int>(x & 0x0F0F0F0Fu); }
-__device__ __forceinline__ int hi_nib(uint32_t x) { return static_cast<int>((x >> 4) & 0x0F0F0F0Fu); }
+// The int4 codes q = n - 8 of the low / high nibbles n of the four bytes of
+// a word, as int8 lanes holding 16 q: the nibble placed in the top half of
+// its byte with its top bit flipped is 16 q in two's complement.
+__device__ __forceinline__ int lo_q16(uint32_t x) { return static_cast<int>(((x << 4) & 0xF0F0F0F0u) ^ 0x80808080u); }
+__device__ __forceinline__ int hi_q16(uint32_t x) { return static_cast<int>((x & 0xF0F0F0F0u) ^ 0x80808080u); }
 
 // QK of one half: this lane's column scores xs[i] (tokens 16 sb + 4 kq + i)
 // before the sum over the four groups of the half, added into xs.
@@ -683,53 +653,57 @@ __device__ __forceinline__ void qk_half(const StateQ<NH>& st, const Blk4<FMT, NH
   const float ks4[4] = {quad_bcast<0>(ksf), quad_bcast<1>(ksf), quad_bcast<2>(ksf), quad_bcast<3>(ksf)};
   if (FMT == 0) {
     const uint4 w = cur.k[sb][hf][0];
-    // unsigned nibbles as int8: k-step 0 = even channels, 1 = odd channels
-    const int4_t a0 = (int4_t){lo_nib(w.x), lo_nib(w.y), lo_nib(w.z), lo_nib(w.w)};
-    const int4_t a1 = (int4_t){hi_nib(w.x), hi_nib(w.y), hi_nib(w.z), hi_nib(w.w)};
-    int4_t c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[hf][0][0], st.corr[hf][0], 0, 0, 0);
+    // codes as int8 16 q: k-step 0 = even channels, 1 = odd channels
+    const int4_t a0 = (int4_t){lo_q16(w.x), lo_q16(w.y), lo_q16(w.z), lo_q16(w.w)};
+    const int4_t a1 = (int4_t){hi_q16(w.x), hi_q16(w.y), hi_q16(w.z), hi_q16(w.w)};
+    const int4_t z = (int4_t){0, 0, 0, 0};
+    int4_t c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[hf][0][0], z, 0, 0, 0);
     c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[hf][0][1], c1, 0, 0, 0);
-    int4_t c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[hf][1][0], st.corr[hf][1], 0, 0, 0);
+    int4_t c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[hf][1][0], z, 0, 0, 0);
     c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[hf][1][1], c2, 0, 0, 0);
-    int4_t c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[hf][2][0], st.corr[hf][2], 0, 0, 0);
+    int4_t c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.qb[hf][2][0], z, 0, 0, 0);
     c3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.qb[hf][2][1], c3, 0, 0, 0);
-    // sfac is this column's query scale
+    // sfac is this column's query scale (over 16)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xs[i] = fmaf(limb_score(c1, c2, c3, i) * st.sfac[hf], ks4[i], xs[i]);
+    for (int i = 0; i < 4; ++i) xs[i] = fmaf(limb_score<4>(c1, c2, c3, i) * st.sfac[hf], ks4[i], xs[i]);
   } else {
     // k-step s covers channels 32 kq + 16 s .. + 15 (int4: as low / high
     // nibble words; int8: the signed code bytes in order)
     int4_t av[2];
     if (F::BITS == 4) {
       const uint4 w = cur.k[sb][hf][0];
-      av[0] = (int4_t){lo_nib(w.x), hi_nib(w.x), lo_nib(w.y), hi_nib(w.y)};
-      av[1] = (int4_t){lo_nib(w.z), hi_nib(w.z), lo_nib(w.w), hi_nib(w.w)};
+      av[0] = (int4_t){lo_q16(w.x), hi_q16(w.x), lo_q16(w.y), hi_q16(w.y)};
+      av[1] = (int4_t){lo_q16(w.z), hi_q16(w.z), lo_q16(w.w), hi_q16(w.w)};
     } else {
       av[0] = __builtin_bit_cast(int4_t, cur.k[sb][hf][0]);
       av[1] = __builtin_bit_cast(int4_t, cur.k[sb][hf][F::W - 1]);
     }
+    const int4_t z = (int4_t){0, 0, 0, 0};
     if (!F::G16) {
       // one group per 32-channel slice: both k-steps into one sum
       int4_t c[3];
 #pragma unroll
       for (int limb = 0; limb < 3; ++limb) {
-        c[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], st.qb[hf][limb][0], st.corr[hf][limb], 0, 0, 0);
+        c[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], st.qb[hf][limb][0], z, 0, 0, 0);
         c[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[1], st.qb[hf][limb][1], c[limb], 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xs[i] = fmaf(limb_score(c[0], c[1], c[2], i) * st.sfac[hf], ks4[i], xs[i]);
+      for (int i = 0; i < 4; ++i)
+        xs[i] = fmaf(limb_score<F::BITS>(c[0], c[1], c[2], i) * st.sfac[hf], ks4[i], xs[i]);
     } else {
       // groups of 16: each k-step is one group with its own key scale
       int4_t c0[3], c1[3];
 #pragma unroll
       for (int limb = 0; limb < 3; ++limb) {
-        c0[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], st.qb[hf][limb][0], st.corr[hf][limb], 0, 0, 0);
-        c1[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[1], st.qb[hf][limb][1], st.corr1[hf][limb], 0, 0, 0);
+        c0[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], st.qb[hf][limb][0], z, 0, 0, 0);
+        c1[limb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[1], st.qb[hf][limb][1], z, 0, 0, 0);
       }
       const float kgf = f16_bits_to_f32(cur.ks[sb][hf] >> 16);
       const float kg4[4] = {quad_bcast<0>(kgf), quad_bcast<1>(kgf), quad_bcast<2>(kgf), quad_bcast<3>(kgf)};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        xs[i] = fmaf(fmaf(limb_score(c0[0], c0[1], c0[2], i), ks4[i], limb_score(c1[0], c1[1], c1[2], i) * kg4[i]),
+        xs[i] = fmaf(fmaf(limb_score<F::BITS>(c0[0], c0[1], c0[2], i), ks4[i],
+                          limb_score<F::BITS>(c1[0], c1[1], c1[2], i) * kg4[i]),
                      st.sfac[hf], xs[i]);
     }
   }
@@ -892,7 +866,7 @@ __global__ void __launch_bounds__(64, NH == 1 ? 2 : 1) attn_split_kernel(AttnArg
   using F = QF<FMT, NH>;
   constexpr int D = 128 * NH;
   // rotated query records of the wave's heads (quantized cache)
-  __shared__ __attribute__((aligned(16))) uint8_t qrec[INT4 ? kHeadsPerWave * F::REC : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t qrec[INT4 ? kHeadsPerWave * Rec<NH>::BYTES : 16];
   const int lane = threadIdx.x;
   const int n16 = lane & 15;
   const int kq = lane >> 4;
@@ -932,10 +906,10 @@ __global__ void __launch_bounds__(64, NH == 1 ? 2 : 1) attn_split_kernel(AttnArg
     // block's loads are in flight.
     auto init_query = [&]() {
       // all four records (heads past nh hold a zero word and are never read)
-      query_records<ROT, F::REC, F::G16 && F::BITS == 4, NH>(a, qin, lane, qrec);
+      query_records<ROT, NH>(a, qin, lane, qrec);
       // one wave: its LDS writes are visible once its LDS counter drains
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const uint8_t* rec = qrec + (head_ok ? my_head : 0) * F::REC;
+      const uint8_t* rec = qrec + (head_ok ? my_head : 0) * Rec<NH>::BYTES;
       const int grp = n16 >> 2;
       const bool live = head_ok && grp == kq;
 #pragma unroll
@@ -974,21 +948,10 @@ __global__ void __launch_bounds__(64, NH == 1 ? 2 : 1) attn_split_kernel(AttnArg
               st.qb[hf][limb][ks] = (int4_t){static_cast<int>(d[4 * ks]), static_cast<int>(d[4 * ks + 1]),
                                              static_cast<int>(d[4 * ks + 2]), static_cast<int>(d[4 * ks + 3])};
           }
-          // unsigned int4 nibbles (n = q + 8): the accumulators start at -8
-          // sum(Q) over the channels they cover; int8 codes are signed
-          int c0 = 0, c1 = 0;
-          if (F::BITS == 4 && !F::G16) {
-            c0 = -8 * (head_ok ? reinterpret_cast<const int*>(rec + Rec<NH>::SUM)[4 * NH * limb + 4 * hf + grp] : 0);
-          } else if (F::BITS == 4) {
-            const int* s16 = reinterpret_cast<const int*>(rec + Rec<NH>::SUM16) + 8 * NH * limb + 8 * hf + 2 * grp;
-            c0 = -8 * (head_ok ? s16[0] : 0);
-            c1 = -8 * (head_ok ? s16[1] : 0);
-          }
-          st.corr[hf][limb] = (int4_t){c0, c0, c0, c0};
-          st.corr1[hf][limb] = (int4_t){c1, c1, c1, c1};
         }
-        st.sfac[hf] =
-            head_ok ? reinterpret_cast<const float*>(rec + Rec<NH>::S)[4 * hf + grp] * (1.f / 65536.f) : 0.f;
+        // s / 2^16 for the limbs; int4 scores come out 16 times too large
+        constexpr float kSf = F::BITS == 4 ? 1.f / 1048576.f : 1.f / 65536.f;
+        st.sfac[hf] = head_ok ? reinterpret_cast<const float*>(rec + Rec<NH>::S)[4 * hf + grp] * kSf : 0.f;
       }
     };
 #pragma unroll

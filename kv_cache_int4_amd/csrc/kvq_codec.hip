@@ -901,14 +901,16 @@ __global__ void __launch_bounds__(64, 2) encode128_mfma_kernel(CodecArgs a) {
 // D = 128 tile layout with rows = half vectors (row 2v + h = channels
 // 128h .. 128h + 127 of vector v).  SRFT by decimation in time: lane 2v + h
 // takes the complex pairs 2k + h (k < 64), transforms them with the 64-point
-// FFT, the odd lane multiplies by W_128^m, and one butterfly across the pair
-// leaves Z_m on lane 0 and Z_{m+64} on lane 1.  SRHT (Sylvester H_256 =
+// FFT, the odd lane multiplies by W_128^m (by -W_128^m for m >= 33, a
+// rotation within pi/2, done by shears in place), and one butterfly across
+// the pair leaves Z_m on lane 0 and Z_{m+64} on lane 1.  SRHT (Sylvester H_256 =
 // H_2 (x) H_128 on the top index bit): the butterfly across the pair comes
 // first (x_lo + x_hi, x_lo - x_hi), then H_128 in each lane.  Either way a
 // lane ends with a contiguous half of the output channels and quantizes it
-// like a D = 128 vector.  The butterfly computes own + sign * partner, which
-// on the odd lane is the negated value; the sign is folded into that lane's
-// half of the lambda table.
+// like a D = 128 vector.  The butterfly computes own + sign * partner (the
+// sign negated on the pairs whose twiddle took the opposite angle), which
+// on the odd lane is the negated value except on those pairs; the sign is
+// folded into that lane's half of the lambda table.
 // ---------------------------------------------------------------------------
 // Chunk swizzle of row r of a D=256 tile.  The SRFT lanes read one row per
 // lane pair (rows 2v + R of every v at once): the swizzle by bits 1-4 of the
@@ -965,6 +967,16 @@ __device__ __forceinline__ uint32_t pair_mask256(const CodecArgs& a, int h, int 
   return 0u;
 }
 
+// Sign folded into lambda of channel c: the pair step leaves the odd lane's
+// half (channels 128 ..) negated, except, with SRFT, the pairs of
+// frequencies m + 64, m >= 33 (channels 194 ..), whose twiddles took the
+// opposite angle.
+template <int ROT>
+__host__ __device__ constexpr float lam_sign256(int c) {
+  if (ROT == KVQ_ROT_ID || c < 128) return 1.f;
+  return (ROT == KVQ_ROT_SRFT && c >= 128 + 2 * 33) ? 1.f : -1.f;
+}
+
 // MODE 0 writes codes and scales; MODE 1 writes the rotated values w =
 // lambda * R x in fp32 (the transform of this kernel, for checking).
 template <int ROT, int MODE, int FMT, bool ONE>
@@ -1005,7 +1017,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     // them is a store of the tile before, a transform ago)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lam_lds[lane + 64 * q] = (q < 2 || !kPair ? 1.f : -1.f) * lam_r[q];
+    for (int q = 0; q < 4; ++q) lam_lds[lane + 64 * q] = lam_sign256<ROT>(lane + 64 * q) * lam_r[q];
     uint32_t p[64];
     const uint4* masks = reinterpret_cast<const uint4*>(mask_lds);   // [hh * 16 + j]
     if (ROT == KVQ_ROT_SRFT) {
@@ -1048,11 +1060,8 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     float v[128];
     if (ROT == KVQ_ROT_SRFT) {
       rotate_packed<KVQ_ROT_SRFT>(p, v);
-      if (hh) {
-#pragma unroll
-        for (int m = 1; m < 64; ++m) twiddle<128, false>(v[2 * rev4(m)], v[2 * rev4(m) + 1], m);
-      }
-      pair_fma_all(v, sgn);
+      if (hh) pair_twiddles_srft<false>(v);
+      pair_fma_all_srft(v, sgn);
     } else {
 #pragma unroll
       for (int k = 0; k < 64; ++k) {
@@ -1482,7 +1491,11 @@ __device__ __forceinline__ uint64_t sign_word(const CodecArgs& a, int i) {
 // Sign mask of output pair kg (channels 2 kg, 2 kg + 1) of a D = 256 vector.
 template <int ROT>
 __device__ __forceinline__ uint32_t out_mask256(const CodecArgs& a, int kg) {
-  if (ROT == KVQ_ROT_SRFT) return ((sign_word(a, kg >> 6) >> (kg & 63)) & 1u) ? 0x80008000u : 0u;
+  if (ROT == KVQ_ROT_SRFT) {
+    // the odd lane's pairs 64 + k, k >= 33, leave the pair step negated
+    const uint32_t flip = kg >= 64 + 33 ? 0x80008000u : 0u;
+    return (((sign_word(a, kg >> 6) >> (kg & 63)) & 1u) ? 0x80008000u : 0u) ^ flip;
+  }
   if (ROT == KVQ_ROT_SRHT) {
     const uint64_t w = sign_word(a, kg >> 5);
     const int i = (2 * kg) & 63;
@@ -1594,11 +1607,8 @@ __global__ void __launch_bounds__(64, 2) decode256_kernel(CodecArgs a) {
 
     if (ROT == KVQ_ROT_SRFT) {
       fft64<true>(v);
-      if (hh) {
-#pragma unroll
-        for (int k = 1; k < 64; ++k) twiddle<128, true>(v[2 * rev4(k)], v[2 * rev4(k) + 1], k);
-      }
-      pair_fma_all(v, sgn);
+      if (hh) pair_twiddles_srft<true>(v);
+      pair_fma_all_srft(v, sgn);
     } else if (ROT == KVQ_ROT_SRHT) {
       pair_fma_all(v, sgn);
       wht128(v);
@@ -1711,7 +1721,7 @@ __global__ void __launch_bounds__(64, 2) decode_f32_kernel(CodecArgs a) {
         pair_fma_all(v, sgn);
         if (lane & 1) {
 #pragma unroll
-          for (int m = 0; m < 64; ++m) twiddle<128, true>(v[2 * m], v[2 * m + 1], m);
+          for (int m = 0; m < 64; ++m) twiddle_mul<128, true>(v[2 * m], v[2 * m + 1], m);
         }
       }
       fft64<true>(v);

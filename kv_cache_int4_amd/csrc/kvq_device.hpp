@@ -68,24 +68,75 @@ constexpr TwTable make_twiddles(int N) {
 
 constexpr TwTable kTw128 = make_twiddles(128);
 
+// Rotation by shears (Paeth): multiplying x + i y by exp(i phi) is the
+// product of three shears, x -= tan(phi/2) y, y += sin(phi) x,
+// x -= tan(phi/2) y, so a twiddle costs three in-place FMAs instead of two
+// products and two FMAs into new registers.  With |phi| <= pi/2 the shear
+// factors are at most 1 and the result is as accurate as the direct
+// product (within two ulps of the exact rotation).  Factors of the angles
+// phi = 2 pi r / 128, |r| <= 32, rounded once to float; r = 0 and the
+// quarter turns are exact.
+struct ShearTable {
+  float t[65];   // tan(phi / 2) at index r + 32
+  float s[65];   // sin(phi)
+};
+
+constexpr ShearTable make_shears() {
+  ShearTable h{};
+  for (int r = -32; r <= 32; ++r) {
+    const double x = 2.0 * kPi * r / 128.0;
+    const double sn = taylor_sin(x), cs = taylor_cos(x);
+    h.t[r + 32] = static_cast<float>(sn / (1.0 + cs));
+    h.s[r + 32] = static_cast<float>(sn);
+  }
+  h.t[32] = 0.f; h.s[32] = 0.f;
+  h.t[0] = -1.f; h.s[0] = -1.f;
+  h.t[64] = 1.f; h.s[64] = 1.f;
+  return h;
+}
+
+constexpr ShearTable kShear = make_shears();
+
+// (re + i im) *= exp(2 pi i r / 128) in place, |r| <= 32 (r a compile-time
+// constant): three FMAs on the operands' own registers, so the step can run
+// under a lane mask with no copies where the masked and unmasked values
+// meet.
+__device__ __forceinline__ void rot_shear(float& re, float& im, int r) {
+  if (r == 0) return;
+  const float t = kShear.t[r + 32], s = kShear.s[r + 32];
+  re = fmaf(-t, im, re);
+  im = fmaf(s, re, im);
+  re = fmaf(-t, im, re);
+}
+
 // (re + i im) *= exp(-+ 2 pi i e / N): INV = false takes the forward kernel
-// exp(-2 pi i e / N), INV = true its conjugate.  N divides 128.
+// exp(-2 pi i e / N), INV = true its conjugate.  N divides 128.  The angle
+// splits into the nearest quarter turn, applied by renaming the registers
+// and flipping signs (folded into the adds that use the result), and a
+// rest of at most pi/4, applied by three shears.
 template <int N, bool INV>
 __device__ __forceinline__ void twiddle(float& re, float& im, int e) {
   e %= N;
+  const int A = (INV ? e : (N - e) % N) * (128 / N);   // angle 2 pi A / 128
+  const int Q = (A + 16) / 32;                         // nearest quarter turn
+  const int r = A - 32 * Q;                            // -16 <= r < 16
+  rot_shear(re, im, r);
+  const float x = re, y = im;
+  switch (Q & 3) {
+    case 1: re = -y; im = x; break;     // times i
+    case 2: re = -x; im = -y; break;    // times -1
+    case 3: re = y; im = -x; break;     // times -i
+    default: break;
+  }
+}
+
+// The same product formed directly (two products, two FMAs into new
+// registers): for a twiddle step under a lane mask whose angles exceed the
+// range of rot_shear.
+template <int N, bool INV>
+__device__ __forceinline__ void twiddle_mul(float& re, float& im, int e) {
+  e %= N;
   if (e == 0) return;
-  if (2 * e == N) {
-    re = -re;
-    im = -im;
-    return;
-  }
-  const bool minus_i = (4 * e == N) != INV;     // multiply by -i
-  if (4 * e == N || 4 * e == 3 * N) {
-    const float t = re;
-    if (minus_i) { re = im; im = -t; }
-    else         { re = -im; im = t; }
-    return;
-  }
   const float c = kTw128.c[e * (128 / N)];
   const float s = INV ? -kTw128.s[e * (128 / N)] : kTw128.s[e * (128 / N)];
   // (re + i im)(c - i s) = (re c + im s) + i (im c - re s)
@@ -204,6 +255,53 @@ __device__ __forceinline__ void pair_fma8(float* v, float sign) {
 __device__ __forceinline__ void pair_fma_all(float (&v)[128], float sign) {
 #pragma unroll
   for (int i = 0; i < 128; i += 8) pair_fma8(v + i, sign);
+}
+
+// The radix-2 step between the halves of a D=256 SRFT vector where the odd
+// lane's twiddles of frequencies m >= 33 were applied as rotations by the
+// opposite angle (a factor -1, which keeps every shear angle within pi/2):
+// their register pairs rev4(m) take -sign.  Same form as pair_fma8, one
+// sign operand per register.
+__device__ __forceinline__ void pair_fma8s(float* v, const float (&sg)[8]) {
+  asm("s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %9 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %10 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %11 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %12 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %13 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %14 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %15 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+      : "v"(sg[0]), "v"(sg[1]), "v"(sg[2]), "v"(sg[3]), "v"(sg[4]), "v"(sg[5]), "v"(sg[6]), "v"(sg[7]));
+}
+
+// Whether register j of a lane's 64-point transform output (frequency
+// rev4(j / 2)) is one of those rotated by the opposite angle.
+__host__ __device__ constexpr bool srft_flipped(int j) { return rev4(j >> 1) >= 33; }
+
+__device__ __forceinline__ void pair_fma_all_srft(float (&v)[128], float sign) {
+  const float neg = -sign;
+#pragma unroll
+  for (int i = 0; i < 128; i += 8) {
+    float sg[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sg[k] = srft_flipped(i + k) ? neg : sign;
+    pair_fma8s(v + i, sg);
+  }
+}
+
+// The odd lane's twiddles of the D=256 SRFT step, W_128^(-+m) on frequency
+// m (held in register pair rev4(m)): m <= 32 as the rotation itself, m >= 33
+// as the rotation by the opposite angle (the factor -1 goes to the pair
+// step and to the sign of that lane's output channels).
+template <bool INV>
+__device__ __forceinline__ void pair_twiddles_srft(float (&v)[128]) {
+#pragma unroll
+  for (int m = 1; m < 64; ++m) {
+    const int r = m <= 32 ? (INV ? m : -m) : (INV ? m - 64 : 64 - m);
+    rot_shear(v[2 * rev4(m)], v[2 * rev4(m) + 1], r);
+  }
 }
 
 // Streaming 16-byte global load / store (touched once: nontemporal hint).
