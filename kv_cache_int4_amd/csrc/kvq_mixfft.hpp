@@ -85,31 +85,55 @@ constexpr double const_rsqrt(double n) {
   return y;
 }
 
+// Shear factors of the rotations by 2 pi k / (4 N), |k| <= N / 2 (at most
+// an eighth of a turn), at index k + N / 2: tan of half the angle and its
+// sine, in double, rounded once to float.
+template <int N>
+struct ShearN {
+  float t[N + 1];
+  float s[N + 1];
+};
+
+template <int N>
+constexpr ShearN<N> make_shear_n() {
+  ShearN<N> h{};
+  for (int k = -N / 2; k <= N / 2; ++k) {
+    const double x = 2.0 * kPi * k / (4.0 * N);
+    const double sn = taylor_sin(x), cs = taylor_cos(x);
+    h.t[k + N / 2] = static_cast<float>(sn / (1.0 + cs));
+    h.s[k + N / 2] = static_cast<float>(sn);
+  }
+  return h;
+}
+
+template <int N>
+struct ShearHold {
+  static constexpr ShearN<N> h = make_shear_n<N>();
+};
+
 // (re + i im) * exp(-+ 2 pi i e / N): INV = false takes the forward kernel.
-// The identity, half and quarter turns cost no multiply.
+// As the power-of-two twiddles: the nearest quarter turn by renaming and
+// sign flips (folded into the adds that use the result), the rest, at most
+// an eighth of a turn, by three in-place shears.
 template <int N, bool INV>
 __host__ __device__ __forceinline__ void mr_rot(float& re, float& im, int e) {
   e %= N;
-  if (e == 0) return;
-  if (2 * e == N) {
-    re = -re;
-    im = -im;
-    return;
+  const int A = INV ? e : (N - e) % N;        // angle 2 pi A / N
+  const int Q = (8 * A + N) / (2 * N);        // nearest quarter turn
+  const int k = 4 * A - Q * N;                // rest 2 pi k / (4 N)
+  if (k != 0) {
+    const float t = ShearHold<N>::h.t[k + N / 2], sn = ShearHold<N>::h.s[k + N / 2];
+    re = fmaf(-t, im, re);
+    im = fmaf(sn, re, im);
+    re = fmaf(-t, im, re);
   }
-  if (4 * e == N || 4 * e == 3 * N) {
-    const bool minus_i = (4 * e == N) != INV;
-    const float t = re;
-    if (minus_i) { re = im; im = -t; }
-    else         { re = -im; im = t; }
-    return;
+  const float x = re, y = im;
+  switch (Q & 3) {
+    case 1: re = -y; im = x; break;     // times i
+    case 2: re = -x; im = -y; break;    // times -1
+    case 3: re = y; im = -x; break;     // times -i
+    default: break;
   }
-  const float c = TwHold<N>::t.c[e];
-  const float s = INV ? -TwHold<N>::t.s[e] : TwHold<N>::t.s[e];
-  // (re + i im)(c - i s) = (re c + im s) + i (im c - re s)
-  const float r2 = fmaf(re, c, im * s);
-  const float i2 = fmaf(im, c, -(re * s));
-  re = r2;
-  im = i2;
 }
 
 // R-point DFT of (ar, ai) in place, forward kernel w = exp(-2 pi i / R) or
