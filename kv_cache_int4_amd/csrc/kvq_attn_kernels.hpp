@@ -945,40 +945,49 @@ __global__ void __launch_bounds__(64, NH == 1 ? 2 : 1) attn_split_kernel(AttnArg
     const int n_full = static_cast<int>(cnt) - (has_tail ? 1 : 0);
     const uint32_t step = kBlk * S;
     const uint32_t t_end = seq, t_last = seq - 1;
-    uint32_t t0 = kBlk * sp;
+    // The split's full blocks in a rotated order: block i at position
+    // (i + rot) mod n_full, rot = this unit's index.  At any moment the
+    // units then read different stretches of their rows, not the same
+    // offset of every row (rows lie a fixed stride apart, so equal offsets
+    // fall on few memory channels when the stride aliases the channel
+    // interleave; measured up to 10% on some cache placements).  The tail,
+    // if any, stays last.
+    const uint32_t t_first = kBlk * sp;
+    const uint32_t rot = n_full > 0 ? (static_cast<uint32_t>(blockIdx.x) / S) % static_cast<uint32_t>(n_full) : 0u;
+    auto t_blk = [&](int i) {
+      uint32_t j = static_cast<uint32_t>(i) + rot;
+      if (j >= static_cast<uint32_t>(n_full)) j -= static_cast<uint32_t>(n_full);
+      return t_first + j * step;
+    };
+    const uint32_t t_tail = t_first + static_cast<uint32_t>(n_full) * step;
     query_loads<ROT, NH>(a, a.q + qrow0 * D, nh, a.lambda_k + g * D, lane, qin);
     Blk4<FMT, NH> b0, b1;
     if (n_full == 0) {
-      if (has_tail) load4<FMT, true, NH>(rows, t0, t_last, o4, n16, kq, b0);
+      if (has_tail) load4<FMT, true, NH>(rows, t_tail, t_last, o4, n16, kq, b0);
       init_query();
-      if (has_tail) process4<FMT, true, NH>(st, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
+      if (has_tail) process4<FMT, true, NH>(st, b0, t_tail, t_end, kq, n16, mag_lo, mag_hi);
     } else {
-      load4<FMT, false, NH>(rows, t0, t_last, o4, n16, kq, b0);
+      load4<FMT, false, NH>(rows, t_blk(0), t_last, o4, n16, kq, b0);
       init_query();
       // b0 holds block i at the top; blocks i + 1 and i + 2 are full
       int i = 0;
       for (; i + 2 < n_full; i += 2) {
-        load4<FMT, false, NH>(rows, t0 + step, t_last, o4, n16, kq, b1);
-        process4<FMT, false, NH>(st, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
-        t0 += step;
-        load4<FMT, false, NH>(rows, t0 + step, t_last, o4, n16, kq, b0);
-        process4<FMT, false, NH>(st, b1, t0, t_end, kq, n16, mag_lo, mag_hi);
-        t0 += step;
+        load4<FMT, false, NH>(rows, t_blk(i + 1), t_last, o4, n16, kq, b1);
+        process4<FMT, false, NH>(st, b0, 0, t_end, kq, n16, mag_lo, mag_hi);
+        load4<FMT, false, NH>(rows, t_blk(i + 2), t_last, o4, n16, kq, b0);
+        process4<FMT, false, NH>(st, b1, 0, t_end, kq, n16, mag_lo, mag_hi);
       }
       // one or two full blocks left, then maybe the tail
       if (n_full - i == 2) {
-        load4<FMT, false, NH>(rows, t0 + step, t_last, o4, n16, kq, b1);
-        process4<FMT, false, NH>(st, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
-        t0 += step;
-        if (has_tail) load4<FMT, true, NH>(rows, t0 + step, t_last, o4, n16, kq, b0);
-        process4<FMT, false, NH>(st, b1, t0, t_end, kq, n16, mag_lo, mag_hi);
-        t0 += step;
-        if (has_tail) process4<FMT, true, NH>(st, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
+        load4<FMT, false, NH>(rows, t_blk(i + 1), t_last, o4, n16, kq, b1);
+        process4<FMT, false, NH>(st, b0, 0, t_end, kq, n16, mag_lo, mag_hi);
+        if (has_tail) load4<FMT, true, NH>(rows, t_tail, t_last, o4, n16, kq, b0);
+        process4<FMT, false, NH>(st, b1, 0, t_end, kq, n16, mag_lo, mag_hi);
+        if (has_tail) process4<FMT, true, NH>(st, b0, t_tail, t_end, kq, n16, mag_lo, mag_hi);
       } else {
-        if (has_tail) load4<FMT, true, NH>(rows, t0 + step, t_last, o4, n16, kq, b1);
-        process4<FMT, false, NH>(st, b0, t0, t_end, kq, n16, mag_lo, mag_hi);
-        t0 += step;
-        if (has_tail) process4<FMT, true, NH>(st, b1, t0, t_end, kq, n16, mag_lo, mag_hi);
+        if (has_tail) load4<FMT, true, NH>(rows, t_tail, t_last, o4, n16, kq, b1);
+        process4<FMT, false, NH>(st, b0, 0, t_end, kq, n16, mag_lo, mag_hi);
+        if (has_tail) process4<FMT, true, NH>(st, b1, t_tail, t_end, kq, n16, mag_lo, mag_hi);
       }
     }
 
