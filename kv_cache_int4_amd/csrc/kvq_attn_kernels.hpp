@@ -1049,12 +1049,20 @@ __global__ void __launch_bounds__(64, NH == 1 ? 2 : 1) attn_split_kernel(AttnArg
     // tile is four times larger: one buffer, occupancy hides latency.
     const uint32_t t_last = t_end - 1;
     const int n_full = static_cast<int>((t_end - t_begin) / kBlk);   // blocks entirely inside
-    uint32_t t0 = t_begin;
-    for (int i = 0; i < n_full; ++i, t0 += kBlk) {
+    // full blocks from a rotated start, as the quantized cache's stream
+    // (rows a fixed stride apart would otherwise be read at equal offsets
+    // at the same time); the tail stays last
+    const uint32_t rotf =
+        n_full > 0 ? (static_cast<uint32_t>(blockIdx.x) / static_cast<uint32_t>(a.S)) % static_cast<uint32_t>(n_full) : 0u;
+    for (int i = 0; i < n_full; ++i) {
+      uint32_t jj = static_cast<uint32_t>(i) + rotf;
+      if (jj >= static_cast<uint32_t>(n_full)) jj -= static_cast<uint32_t>(n_full);
+      const uint32_t tb = t_begin + jj * kBlk;
       BlkF<NH> bb;
-      load_blkf<false, NH>(rows, t0, t_last, n16, kq, bb);
-      process_blkf<false, NH>(st, bb, t0, t_end, kq);
+      load_blkf<false, NH>(rows, tb, t_last, n16, kq, bb);
+      process_blkf<false, NH>(st, bb, tb, t_end, kq);
     }
+    const uint32_t t0 = t_begin + static_cast<uint32_t>(n_full) * kBlk;
     if (t0 < t_end) {
       BlkF<NH> bb;
       load_blkf<true, NH>(rows, t0, t_last, n16, kq, bb);
