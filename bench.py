@@ -44,12 +44,12 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # the kernel sources they were taken on (sha256 prefix of the listed files);
 # reported as null once those change.
 TRAFFIC = {
-    "attn": {"files": ("kvq_attn.hip", "kvq_device.hpp"), "sha256": "bb54d73ef8dbcb53",
-             "bytes": (295682.9 + 2138.5) * 2 * 1024 + (4367.5 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "f04a5f5705f29b15",
-               "bytes": 57689.6 * 2 * 1024 + 32256.1 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "f04a5f5705f29b15",
-               "bytes": 16455.6 * 2 * 1024 + 114774.9 * 1024},
+    "attn": {"files": ("kvq_attn.hip", "kvq_attn_kernels.hpp", "kvq_device.hpp"), "sha256": "ede60afeb8f82f6d",
+             "bytes": (295661.3 + 2130.0) * 2 * 1024 + (4361.0 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "7f6fbf6fa45f40ad",
+               "bytes": 57680.7 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "7f6fbf6fa45f40ad",
+               "bytes": 16450.3 * 2 * 1024 + 114766.8 * 1024},
 }
 
 
