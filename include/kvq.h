@@ -155,7 +155,8 @@ kvq_status kvq_plan_info_ex(const kvq_plan* plan, int32_t* D, int32_t* G, int32_
  *   scales fp16  [B, H, Tcap, D/G]       (dense; 16-byte aligned at D = 256
  *                                         and at D = 128 with G = 16, else
  *                                         8-byte aligned).
- * Requires 0 <= t0, t0 + T <= Tcap.  B, H or T of 0 is a no-op.  The caller
+ * Requires 0 <= t0, t0 + T <= Tcap and a token stride x_st below 2^28
+ * elements (else KVQ_ERR_INVALID).  B, H or T of 0 is a no-op.  The caller
  * owns every buffer; nothing is allocated or synchronized. */
 kvq_status kvq_encode(const kvq_plan* plan, const uint16_t* x, int64_t B, int64_t H, int64_t T,
                       int64_t x_sb, int64_t x_sh, int64_t x_st,
@@ -171,7 +172,8 @@ kvq_status kvq_encode(const kvq_plan* plan, const uint16_t* x, int64_t B, int64_
  * y + b*y_sb + h*y_sh + t*y_st + j; fp16 rows must be 16-byte aligned, fp32
  * rows 8-byte aligned.  At D = 128 and 256 lambda must be 16-byte aligned
  * with lambda_sb a multiple of 4, and scales aligned as for kvq_encode.
- * Requires 0 <= t0, t0 + T <= Tcap; B, H or T of 0 is a no-op. */
+ * Requires 0 <= t0, t0 + T <= Tcap and y_st below 2^28 elements; B, H or T
+ * of 0 is a no-op. */
 kvq_status kvq_decode(const kvq_plan* plan, const uint8_t* codes, const uint16_t* scales,
                       int64_t B, int64_t H, int64_t Tcap, int64_t t0, int64_t T,
                       const float* lambda, int64_t lambda_sb,
@@ -206,7 +208,8 @@ kvq_status kvq_attn_workspace_size(int32_t D, int64_t B, int64_t Hq, int64_t seq
  * dense; out is fp16 or fp32 [B, Hq, D] dense.  Scores are taken in the
  * rotated basis (q . k^ = ((R q) / lambda_k) . (lambda_k R k^)) and the
  * value average is rotated back once per head.  Requires Hq % Hkv == 0,
- * 1 <= seq_len <= Tcap, and a workspace of kvq_attn_workspace_size bytes.
+ * 1 <= seq_len <= Tcap < 2^31, and a workspace of kvq_attn_workspace_size
+ * bytes.
  * Built for D = 128 and 256, every rotation, code width and group size of
  * the plan (codes [B, Hkv, Tcap, D*bits/8] 16-byte aligned, scales
  * [B, Hkv, Tcap, D/G] 8-byte aligned, lambda 16-byte aligned); plans at D =
@@ -238,7 +241,8 @@ kvq_status kvq_attn_decode_noalloc(const kvq_plan* plan, const uint16_t* q,
 /* The same attention over an unquantized fp16 cache k, v [B, Hkv, Tcap, D]
  * (dense, 16-byte aligned): the fp16 cache the abstract compares the int4
  * cache with.  Takes the head size D (128 or 256) instead of a plan, since
- * no quantizer is involved; otherwise as kvq_attn_decode. */
+ * no quantizer is involved; a row of the cache (Tcap * 2D bytes) must not
+ * pass 4 GiB; otherwise as kvq_attn_decode. */
 kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                int64_t B, int64_t Hq, int64_t Hkv, int64_t Tcap, int64_t seq_len,
                                float sm_scale, void* out, kvq_dtype out_dtype,

@@ -65,6 +65,13 @@ int32_t sign_count(const kvq_plan* p) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The codec kernels form a lane's offset from its tile's first row in 32
+// bits, up to 14 token strides of 2-byte elements: token strides stay below
+// 2^28 elements.  The attention kernels count tokens in 32 bits: Tcap stays
+// below 2^31.
+constexpr int64_t kMaxTokenStride = int64_t(1) << 28;
+constexpr int64_t kMaxAttnTcap = int64_t(1) << 31;
+
 // a * b * c * d within [0, 2^62]
 bool product_ok(int64_t a, int64_t b, int64_t c, int64_t d) {
   __int128 v = static_cast<__int128>(a) * b;
@@ -116,6 +123,7 @@ kvq_status check_x(const kvq_plan* p, const uint16_t* x, int64_t B, int64_t H, i
     return fail(KVQ_ERR_INVALID, "strides must be non-negative");
   if (sb % 8 || sh % 8 || st % 8)
     return fail(KVQ_ERR_ALIGN, "x strides must be multiples of 8 elements (16-byte rows)");
+  if (st >= kMaxTokenStride) return fail(KVQ_ERR_INVALID, "x token stride %lld is not below 2^28", (long long)st);
   if (!product_ok(B, H, T, p->D)) return fail(KVQ_ERR_INVALID, "shape too large");
   if (!extent_ok(B, H, T, sb, sh, st, p->D)) return fail(KVQ_ERR_INVALID, "x strides reach too far");
   return KVQ_OK;
@@ -333,6 +341,8 @@ kvq_status kvq_decode(const kvq_plan* plan, const uint8_t* codes, const uint16_t
     if (kvq_status s = check_scales_align(plan, scales)) return s;
     if (y_sb < 0 || y_sh < 0 || y_st < 0 || lambda_sb < 0)
       return fail(KVQ_ERR_INVALID, "strides must be non-negative");
+    if (y_st >= kMaxTokenStride)
+      return fail(KVQ_ERR_INVALID, "y token stride %lld is not below 2^28", (long long)y_st);
     if (plan->D == 128 || plan->D == 256) {
       // the decoders bring each lambda row into LDS with 16-byte direct loads
       if (!aligned(lambda, 16)) return fail(KVQ_ERR_ALIGN, "lambda is not 16-byte aligned (D=%d decode)", plan->D);
@@ -383,6 +393,7 @@ kvq_status check_attn_common(int32_t D, const uint16_t* q, int64_t B, int64_t Hq
                              int64_t seq_len, void* out, kvq_dtype out_dtype, void* workspace,
                              size_t workspace_bytes, bool check_workspace) {
   if (B < 0 || Hq < 0 || Hkv <= 0 || Tcap < 0) return fail(KVQ_ERR_INVALID, "bad shape");
+  if (Tcap >= kMaxAttnTcap) return fail(KVQ_ERR_INVALID, "Tcap=%lld is not below 2^31", (long long)Tcap);
   if (Hq % Hkv) return fail(KVQ_ERR_INVALID, "Hq=%lld is not a multiple of Hkv=%lld", (long long)Hq, (long long)Hkv);
   if (seq_len < 1 || seq_len > Tcap)
     return fail(KVQ_ERR_INVALID, "seq_len=%lld outside [1, Tcap=%lld]", (long long)seq_len, (long long)Tcap);
@@ -498,6 +509,10 @@ kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, 
     if (kvq_status s = check_attn_common(D, q, B, Hq, Hkv, Tcap, seq_len, out, out_dtype, workspace,
                                          workspace_bytes, true))
       return s;
+    // the fp16 kernel addresses a row's tokens with 32-bit byte offsets
+    if (Tcap * 2 * static_cast<int64_t>(D) > (int64_t(1) << 32))
+      return fail(KVQ_ERR_INVALID, "fp16 cache rows of Tcap * 2D = %lld bytes pass 4 GiB",
+                  (long long)(Tcap * 2 * static_cast<int64_t>(D)));
     if (!k || !v) return fail(KVQ_ERR_INVALID, "k or v is NULL");
     if (!aligned(k, 16) || !aligned(v, 16)) return fail(KVQ_ERR_ALIGN, "k and v must be 16-byte aligned");
     if (B == 0 || Hq == 0) return ok();

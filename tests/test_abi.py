@@ -159,6 +159,9 @@ def test_encode_validation():
     assert _encode(p, B=1 << 40, H=1 << 20) == INVALID  # overflowing shape
     assert _encode(p, B=2, sb=1 << 62) == INVALID        # strides reaching past 2^62 elements
     assert b"reach" in K.library().kvq_last_error()
+    assert _encode(p, st=1 << 28) == INVALID              # lane offsets are 32-bit
+    assert b"2^28" in K.library().kvq_last_error()
+    assert _encode(p, st=(1 << 28) - 8, codes=A + 8) == ALIGN   # below the limit: the next check decides
     # zero work is a no-op that touches nothing (NULL pointers allowed)
     assert _encode(p, T=0, x=None, lam=None, codes=None, scales=None) == OK
     assert K.library().kvq_last_error() == b""
@@ -177,6 +180,8 @@ def test_decode_and_rotate_validation():
     assert L.kvq_decode(h, None, A, 1, 1, 8, 0, 4, A, 0, A, 0, 2048, 2048, 256, None) == INVALID
     assert L.kvq_decode(h, A, A, 1, 1, 8, 0, 0, A, 0, A, 0, 2048, 2048, 256, None) == OK
     assert L.kvq_decode(h, A, A, 2, 1, 8, 0, 4, A, 0, A, 0, 1 << 62, 2048, 256, None) == INVALID
+    assert L.kvq_decode(h, A, A, 1, 1, 8, 0, 4, A, 0, A, 0, 2048, 2048, 1 << 28, None) == INVALID
+    assert b"2^28" in L.kvq_last_error()
     assert L.kvq_rotate(h, A, 1, 1, 4, 1024, 1024, 256, A, 0, None, None) == INVALID
     assert L.kvq_rotate(h, A, 1, 1, 4, 1024, 1024, 256, A, 0, A + 4, None) == ALIGN
     assert L.kvq_rotate(None, A, 1, 1, 4, 1024, 1024, 256, A, 0, A, None) == INVALID
@@ -236,6 +241,8 @@ def test_attention_validation():
     assert call(vc=None) == INVALID
     assert call(dt=5) == INVALID
     assert call(B=0) == OK                            # nothing to do
+    assert call(Tcap=1 << 31) == INVALID              # tokens are counted in 32 bits
+    assert b"2^31" in L.kvq_last_error()
     # head sizes with attention kernels: 128 and 256 (the mixed-radix sizes have none)
     p256 = K.Plan(256, 32, "srft", 3)
     assert L.kvq_attn_decode(p256.handle, A, A, A, A, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, 0,
@@ -247,6 +254,10 @@ def test_attention_validation():
     assert L.kvq_attn_decode_f16(256, A, A, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, 0, None) == WORKSPACE
     assert L.kvq_attn_decode_f16(128, A, A, A, 1, 3, 2, 8, 4, 0.1, A, 0, A, need, None) == INVALID
     assert L.kvq_attn_decode_f16(128, A, None, A, 1, 2, 1, 8, 4, 0.1, A, 0, A, need, None) == INVALID
+    # fp16 rows are addressed with 32-bit byte offsets: Tcap * 2D up to 4 GiB
+    big = K.attn_workspace_size(256, 1, 2, 4)
+    assert L.kvq_attn_decode_f16(256, A, A, A, 1, 2, 1, (1 << 23) + 1, 4, 0.1, A, 0, A, big, None) == INVALID
+    assert b"4 GiB" in L.kvq_last_error()
 
 
 def test_noalloc_attention_validation():
