@@ -421,8 +421,9 @@ def boundary_distances(w: np.ndarray, scale_used: np.ndarray, G: int = GROUP, bi
     Returns (code_dist [..., D], scale_rel_dist [..., D/G]):
       code_dist  = | w/scale - (k + 1/2) | for the nearest half-integer, in
                    code units, computed with the scale actually used;
-      scale_rel_dist = | a/qmax - m | / (a/qmax) for the nearest fp16
-                   rounding midpoint m (inf where a = 0).
+      scale_rel_dist = | a/qmax - m | / (a/qmax) for the midpoint m of the
+                   fp16 values lo <= a/qmax < hi, the one that decides
+                   between them (inf where a = 0).
     """
     qmax = code_range(bits)[1]
     w = np.asarray(w, dtype=np.float64)

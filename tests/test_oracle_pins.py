@@ -681,6 +681,36 @@ def test_boundary_distances_on_constructed_values():
     assert sd[0, 0] == 0
 
 
+def test_boundary_distances_against_brute_force():
+    """Code distances against a search over every half-integer in reach, and
+    scale distances against the fp16 neighbours found in a table of every
+    positive finite fp16 value, on random groups of both widths and group
+    sizes (including values at fp16 binade edges and subnormal scales)."""
+    pos = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)   # sorted
+    halves = np.arange(-300, 300) + 0.5
+    rng = _rng(11)
+    for bits, G in ((4, 32), (4, 16), (8, 32), (8, 16)):
+        qmax = O.code_range(bits)[1]
+        D = 64
+        w = rng.standard_normal((6, D)) * np.exp(rng.uniform(-12, 3, (6, 1)))
+        w[0, 0] = qmax * 2.0 ** -3            # a / qmax on a binade edge
+        w[1, :] *= 1e-6                       # subnormal fp16 scales
+        a = np.abs(w.reshape(6, D // G, G)).max(-1)
+        sc = O.fp16_of_quotient(a, qmax)
+        code_d, scale_d = O.boundary_distances(w, sc, G, bits)
+        assert np.any((sc > 0) & (sc < np.float16(2.0 ** -14)))    # subnormal scales are covered
+        s = np.repeat(sc.astype(np.float64), G, axis=-1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = np.where(s > 0, w / s, 0.0)
+        want_code = np.where(s > 0, np.abs(r[..., None] - halves).min(-1), np.inf)
+        assert np.array_equal(code_d, want_code)
+        t = a / qmax
+        i = np.searchsorted(pos, t, side="right")      # pos[i-1] <= t < pos[i]
+        lo = np.where(i > 0, pos[np.maximum(i - 1, 0)], 0.0)
+        mid = (lo + pos[i]) / 2
+        assert np.array_equal(scale_d, np.abs(t - mid) / t)
+
+
 # ------------------------------------------------------------- decode -----
 
 def test_decode_of_exact_construction():
