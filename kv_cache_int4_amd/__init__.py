@@ -218,7 +218,7 @@ def _lam_args(lam, B, H, D):
 
 
 def _x_args(x, D):
-    assert x.dim() == 4 and x.shape[3] == D and x.stride(3) == 1, "x must be [B, H, T, D] with unit D stride"
+    _req(x.dim() == 4 and x.shape[3] == D and x.stride(3) == 1, f"x must be [B, H, T, {D}] with unit D stride")
     return x.shape[0], x.shape[1], x.shape[2], x.stride(0), x.stride(1), x.stride(2)
 
 
@@ -226,13 +226,15 @@ def encode(plan: Plan, x, lam, codes, scales, t0: int = 0):
     """Quantize x [B, H, T, D] (fp16) into tokens t0..t0+T-1 of codes
     [B, H, Tcap, D*bits/8] (uint8) and scales [B, H, Tcap, D/G] (fp16)."""
     import torch
-    assert x.dtype == torch.float16 and codes.dtype == torch.uint8 and scales.dtype == torch.float16
-    assert lam.dtype == torch.float32 and lam.is_contiguous()
-    assert codes.is_contiguous() and scales.is_contiguous()
+    _req(x.dtype == torch.float16 and codes.dtype == torch.uint8 and scales.dtype == torch.float16,
+         "x must be fp16, codes uint8, scales fp16")
+    _req(lam.dtype == torch.float32 and lam.is_contiguous(), "lambda must be contiguous fp32")
+    _req(codes.is_contiguous() and scales.is_contiguous(), "codes and scales must be contiguous")
     B, H, T, sb, sh, st = _x_args(x, plan.D)
+    _req(codes.dim() == 4, "codes must be [B, H, Tcap, D*bits/8]")
     Tcap = codes.shape[2]
-    assert codes.dim() == 4 and tuple(codes.shape) == (B, H, Tcap, plan.code_bytes), "codes shape"
-    assert scales.dim() == 4 and tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), "scales shape"
+    _req(tuple(codes.shape) == (B, H, Tcap, plan.code_bytes), f"codes must be {(B, H, Tcap, plan.code_bytes)}")
+    _req(tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), f"scales must be {(B, H, Tcap, plan.D // plan.G)}")
     lsb = _lam_args(lam, B, H, plan.D)
     idx = _device(x, lam, codes, scales)
     _check(_on(idx, library().kvq_encode, plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam),
@@ -242,12 +244,16 @@ def encode(plan: Plan, x, lam, codes, scales, t0: int = 0):
 def decode(plan: Plan, codes, scales, lam, y, t0: int = 0):
     """Dequantize tokens t0..t0+T-1 into y [B, H, T, D] (fp16 or fp32)."""
     import torch
-    assert codes.is_contiguous() and scales.is_contiguous() and lam.is_contiguous()
-    assert codes.dtype == torch.uint8 and scales.dtype == torch.float16 and lam.dtype == torch.float32
+    _req(codes.is_contiguous() and scales.is_contiguous() and lam.is_contiguous(),
+         "codes, scales and lambda must be contiguous")
+    _req(codes.dtype == torch.uint8 and scales.dtype == torch.float16 and lam.dtype == torch.float32,
+         "codes must be uint8, scales fp16, lambda fp32")
+    _req(codes.dim() == 4 and codes.shape[3] == plan.code_bytes, "codes must be [B, H, Tcap, D*bits/8]")
     B, H, Tcap = codes.shape[0], codes.shape[1], codes.shape[2]
-    assert codes.dim() == 4 and codes.shape[3] == plan.code_bytes, "codes shape"
-    assert tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), "scales shape"
-    assert y.dim() == 4 and y.shape[:2] == (B, H) and y.shape[3] == plan.D and y.stride(3) == 1
+    _req(tuple(scales.shape) == (B, H, Tcap, plan.D // plan.G), f"scales must be {(B, H, Tcap, plan.D // plan.G)}")
+    _req(y.dim() == 4 and tuple(y.shape[:2]) == (B, H) and y.shape[3] == plan.D and y.stride(3) == 1,
+         f"y must be [{B}, {H}, T, {plan.D}] with unit D stride")
+    _req(y.dtype in (torch.float16, torch.float32), "y must be fp16 or fp32")
     dt = {torch.float16: _F16, torch.float32: _F32}[y.dtype]
     lsb = _lam_args(lam, B, H, plan.D)
     idx = _device(codes, scales, lam, y)
@@ -259,10 +265,11 @@ def decode(plan: Plan, codes, scales, lam, y, t0: int = 0):
 def rotate(plan: Plan, x, lam, w):
     """w [B, H, T, D] fp32 = lambda * (R x) (the encoder's transform alone)."""
     import torch
-    assert x.dtype == torch.float16 and lam.dtype == torch.float32 and w.dtype == torch.float32
-    assert lam.is_contiguous()
+    _req(x.dtype == torch.float16 and lam.dtype == torch.float32 and w.dtype == torch.float32,
+         "x must be fp16, lambda and w fp32")
+    _req(lam.is_contiguous(), "lambda must be contiguous")
     B, H, T, sb, sh, st = _x_args(x, plan.D)
-    assert w.is_contiguous() and tuple(w.shape) == (B, H, T, plan.D)
+    _req(w.is_contiguous() and tuple(w.shape) == (B, H, T, plan.D), f"w must be contiguous {(B, H, T, plan.D)}")
     lsb = _lam_args(lam, B, H, plan.D)
     idx = _device(x, lam, w)
     _check(_on(idx, library().kvq_rotate, plan.handle, _ptr(x), B, H, T, sb, sh, st, _ptr(lam),
@@ -289,6 +296,7 @@ def _attn_checks(plan, q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, ou
     for lam in (lam_k, lam_v):
         _req(lam.dtype == torch.float32 and tuple(lam.shape) == (Hkv, D), f"lambda must be fp32 [{Hkv}, {D}]")
     _req(tuple(out.shape) == (B, Hq, D), f"out must be [{B}, {Hq}, {D}]")
+    _req(out.dtype in (torch.float16, torch.float32), "out must be fp16 or fp32")
     for t in (q, k_codes, k_scales, lam_k, v_codes, v_scales, lam_v, out):
         _req(t.is_contiguous(), "attention tensors must be contiguous")
 
@@ -334,8 +342,9 @@ def attn_decode_f16(q, k, v, seq_len: int, sm_scale: float, out, workspace):
     _req(v.dtype == torch.float16 and v.shape == k.shape, "v must match k")
     Hkv, Tcap = k.shape[1], k.shape[2]
     _req(tuple(out.shape) == (B, Hq, D), f"out must be [{B}, {Hq}, {D}]")
+    _req(out.dtype in (torch.float16, torch.float32), "out must be fp16 or fp32")
     for t in (q, k, v, out, workspace):
-        assert t.is_contiguous()
+        _req(t.is_contiguous(), "attention tensors must be contiguous")
     dt = {torch.float16: _F16, torch.float32: _F32}[out.dtype]
     idx = _device(q, k, v, out, workspace)
     _check(_on(idx, library().kvq_attn_decode_f16, D, _ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Tcap, seq_len,

@@ -328,3 +328,33 @@ def test_binding_refuses_host_tensors():
     # shapes that do not match the plan are refused first
     with pytest.raises(ValueError, match="codes must be"):
         K.attn_decode(p, q, codes[..., :32], scales, lam, codes, scales, lam, 8, 0.1, out, ws)
+
+
+def test_binding_shape_checks_are_not_asserts():
+    """The binding's shape and dtype checks raise ValueError (they stay in
+    force under python -O, where asserts vanish): a codes or output tensor
+    too small for the call is refused before its pointer reaches a kernel."""
+    p = K.Plan(128, 32, "srft", 1)
+    x = torch.zeros((1, 2, 4, 128), dtype=torch.float16)
+    lam = torch.ones((2, 128), dtype=torch.float32)
+    codes = torch.zeros((1, 2, 8, 64), dtype=torch.uint8)
+    scales = torch.zeros((1, 2, 8, 4), dtype=torch.float16)
+    with pytest.raises(ValueError, match="codes must be"):
+        K.encode(p, x, lam, codes[:, :1], scales)
+    with pytest.raises(ValueError, match="scales must be"):
+        K.encode(p, x, lam, codes, scales[..., :2])
+    with pytest.raises(ValueError, match="x must be fp16"):
+        K.encode(p, x.float(), lam, codes, scales)
+    with pytest.raises(ValueError, match="y must be"):
+        K.decode(p, codes, scales, lam, torch.zeros((1, 1, 8, 128), dtype=torch.float16))
+    with pytest.raises(ValueError, match="y must be fp16 or fp32"):
+        K.decode(p, codes, scales, lam, torch.zeros((1, 2, 8, 128), dtype=torch.float64))
+    with pytest.raises(ValueError, match="w must be"):
+        K.rotate(p, x, lam, torch.zeros((1, 2, 3, 128), dtype=torch.float32))
+    q = torch.zeros((1, 4, 128), dtype=torch.float16)
+    ws = torch.zeros(K.attn_workspace_size(128, 1, 4, 8), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="out must be fp16 or fp32"):
+        K.attn_decode(p, q, codes, scales, lam, codes, scales, lam, 8, 0.1,
+                      torch.zeros((1, 4, 128), dtype=torch.float64), ws)
+    src = open(K.__file__).read()
+    assert "\n    assert " not in src and "\n        assert " not in src
