@@ -45,11 +45,11 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # reported as null once those change.
 TRAFFIC = {
     "attn": {"files": ("kvq_attn.hip", "kvq_attn_kernels.hpp", "kvq_device.hpp"), "sha256": "ede60afeb8f82f6d",
-             "bytes": (295661.5 + 2130.0) * 2 * 1024 + (4362.3 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "010cfa18c382a088",
-               "bytes": 57680.9 * 2 * 1024 + 32256.0 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "010cfa18c382a088",
-               "bytes": 16450.3 * 2 * 1024 + 114786.7 * 1024},
+             "bytes": (295661.6 + 2130.0) * 2 * 1024 + (4361.4 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "999febb0bebe738c",
+               "bytes": 57688.2 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "999febb0bebe738c",
+               "bytes": 16451.2 * 2 * 1024 + 114742.7 * 1024},
 }
 
 
