@@ -203,6 +203,32 @@ __device__ __forceinline__ void mquant_group(const float (&v)[D], int g, float r
   }
 }
 
+typedef uint32_t mx_u32x2 __attribute__((ext_vector_type(2)));
+
+// The tile's code rows, dense in memory from cbase (nb bytes), from the
+// staging buffer stg (row = lane, CB bytes each) as non-temporal stores of
+// 16 bytes (CB a multiple of 16) or 8 bytes per lane and instruction.
+// Against each lane storing its own row: encode 4-7% faster (int4) and 21%
+// (int8), codes bit-identical.
+template <typename F>
+__device__ __forceinline__ void store_staged_rows(uint8_t* cbase, int nb, const uint8_t* stg, int lane) {
+  constexpr int U = F::CU == 16 ? 16 : 8;
+  constexpr int kInst = (64 * F::CB / U + 63) / 64;
+#pragma unroll
+  for (int i = 0; i < kInst; ++i) {
+    const int off = U * (64 * i + lane);
+    if (off < nb) {
+      if (U == 16) {
+        st_stream16(cbase + off, *reinterpret_cast<const uint4*>(stg + off));
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(stg + off);
+        const mx_u32x2 v = {w.x, w.y};
+        __builtin_nontemporal_store(v, reinterpret_cast<mx_u32x2*>(cbase + off));
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Encode (MODE 0: codes + scales) and rotate (MODE 1: fp32 w = lambda R x)
 // ---------------------------------------------------------------------------
@@ -213,6 +239,9 @@ __global__ void __launch_bounds__(64, 2) mix_encode_kernel(MixArgs a) {
   constexpr int M = G::M;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::kTileBytes];
   __shared__ __attribute__((aligned(16))) float lam_lds[D];
+  // code rows of the previous tile (row = lane), stored with the next
+  // tile's loads out
+  __shared__ __attribute__((aligned(16))) uint8_t stg[MODE == 0 ? 64 * F::CB : 16];
   const int lane = threadIdx.x;
   constexpr float kScale = mix_scale<ROT, D>();
 
@@ -233,11 +262,11 @@ __global__ void __launch_bounds__(64, 2) mix_encode_kernel(MixArgs a) {
   }
   // codes and scales of the previous tile, stored once the next tile's
   // loads are on their way
-  uint32_t pend_c[F::CW] = {};
   uint32_t pend_s[F::NG] = {};
   bool pend_valid = false;
-  uint8_t* pend_cp = nullptr;
   uint16_t* pend_sp = nullptr;
+  uint8_t* pend_cb = nullptr;     // the staged tile's first code byte
+  int pend_nb = 0;                // and its code bytes
   for (; tile < a.n_tiles; tile += gridDim.x) {
     const MTile t = mtile(a, tile);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -262,19 +291,12 @@ __global__ void __launch_bounds__(64, 2) mix_encode_kernel(MixArgs a) {
       lam_r0 = lr[lane];
       if (lane + 64 < D) lam_r1 = lr[lane + 64];
     }
-    if (MODE == 0 && pend_valid) {
-      if (F::CU == 16) {
+    if (MODE == 0 && pend_nb > 0) {
+      store_staged_rows<F>(pend_cb, pend_nb, stg, lane);
+      if (pend_valid) {
 #pragma unroll
-        for (int q = 0; q < F::CB / 16; ++q)
-          *reinterpret_cast<uint4*>(pend_cp + 16 * q) =
-              make_uint4(pend_c[4 * q], pend_c[4 * q + 1], pend_c[4 * q + 2], pend_c[4 * q + 3]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < F::CB / 8; ++q)
-          *reinterpret_cast<uint2*>(pend_cp + 8 * q) = make_uint2(pend_c[2 * q], pend_c[2 * q + 1]);
+        for (int g = 0; g < F::NG; ++g) pend_sp[g] = static_cast<uint16_t>(pend_s[g]);
       }
-#pragma unroll
-      for (int g = 0; g < F::NG; ++g) pend_sp[g] = static_cast<uint16_t>(pend_s[g]);
     }
 
     float v[D];
@@ -336,28 +358,32 @@ __global__ void __launch_bounds__(64, 2) mix_encode_kernel(MixArgs a) {
         for (int g = 0; g < F::NG; ++g) mquant_group<ROT, D, FMT, true>(v, g, r[g], cw + F::WPG * g);
       }
       const int64_t cell = t.row * a.Tcap + a.t0 + t.t_start + lane;
-      pend_cp = a.codes + cell * F::CB;
       pend_sp = a.scales + cell * F::NG;
+      // the lane's code row into the staging buffer (the staged rows of the
+      // tile before were stored above, a transform ago)
+      if (F::CU == 16) {
 #pragma unroll
-      for (int q = 0; q < F::CW; ++q) pend_c[q] = cw[q];
+        for (int q = 0; q < F::CB / 16; ++q)
+          *reinterpret_cast<uint4*>(stg + lane * F::CB + 16 * q) =
+              make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < F::CB / 8; ++q)
+          *reinterpret_cast<uint2*>(stg + lane * F::CB + 8 * q) = make_uint2(cw[2 * q], cw[2 * q + 1]);
+      }
+      pend_cb = a.codes + (t.row * a.Tcap + a.t0 + t.t_start) * F::CB;
+      pend_nb = t.nv * F::CB;
 #pragma unroll
       for (int g = 0; g < F::NG; ++g) pend_s[g] = sc[g];
       pend_valid = valid;
     }
   }
-  if (MODE == 0 && pend_valid) {
-    if (F::CU == 16) {
+  if (MODE == 0 && pend_nb > 0) {
+    store_staged_rows<F>(pend_cb, pend_nb, stg, lane);
+    if (pend_valid) {
 #pragma unroll
-      for (int q = 0; q < F::CB / 16; ++q)
-        *reinterpret_cast<uint4*>(pend_cp + 16 * q) =
-            make_uint4(pend_c[4 * q], pend_c[4 * q + 1], pend_c[4 * q + 2], pend_c[4 * q + 3]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < F::CB / 8; ++q)
-        *reinterpret_cast<uint2*>(pend_cp + 8 * q) = make_uint2(pend_c[2 * q], pend_c[2 * q + 1]);
+      for (int g = 0; g < F::NG; ++g) pend_sp[g] = static_cast<uint16_t>(pend_s[g]);
     }
-#pragma unroll
-    for (int g = 0; g < F::NG; ++g) pend_sp[g] = static_cast<uint16_t>(pend_s[g]);
   }
 }
 
