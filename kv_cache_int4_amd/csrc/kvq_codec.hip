@@ -885,7 +885,9 @@ __global__ void __launch_bounds__(64, 2) encode128_mfma_kernel(CodecArgs a) {
       out_s[g] = sc[0] | (sc[1] << 16);
     }
     if (MODE == 0) {
-      // codes: row v, bytes r * CB / 4 ..; scales: entries v * NG + r * NGL ..
+      // codes: row v, bytes r * CB / 4 .. (1 KiB per group of 16 vectors, as
+      // non-temporal stores: 2.5-4.5% faster than normal ones); scales:
+      // entries v * NG + r * NGL ..
       constexpr int NGL = 32 / F::G;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -893,7 +895,7 @@ __global__ void __launch_bounds__(64, 2) encode128_mfma_kernel(CodecArgs a) {
         if (v < t.nv) {
           char* cb = reinterpret_cast<char*>(a.codes + (cell0 + v) * F::CB) + r * (F::CB / 4);
 #pragma unroll
-          for (int q = 0; q < F::BITS / 4; ++q) *reinterpret_cast<uint4*>(cb + 16 * q) = out_c[g][q];
+          for (int q = 0; q < F::BITS / 4; ++q) st_stream16(cb + 16 * q, out_c[g][q]);
           uint16_t* sp = a.scales + (cell0 + v) * F::NG + r * NGL;
           if (NGL == 1) *sp = static_cast<uint16_t>(out_s[g]);
           else *reinterpret_cast<uint32_t*>(sp) = out_s[g];
