@@ -628,25 +628,36 @@ def main():
 
     # The K steps run phase-major (K encodes, K decodes, K appends, K
     # attention steps: the same work as K passes of the whole path, each
-    # decode reading codes its set's encode wrote), with one event at each
-    # phase boundary, so per-launch times are not padded by event records
+    # decode reading codes its set's encode wrote), with a pair of events
+    # around each phase, so per-launch times are not padded by event records
     # between launches.
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+    # After each phase (outside its events) a one-wave probe reads the shader
+    # clock: the power manager lowers it under sustained load, and the
+    # attention kernel, half bound by its arithmetic, slows with it.
+    ev_start = [torch.cuda.Event(enable_timing=True) for _ in phases]
+    ev_end = [torch.cuda.Event(enable_timing=True) for _ in phases]
+    clk = torch.zeros((len(phases) + 1, 3), dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     if args.profile_marks:
         torch.cuda._sleep(MARK_CYCLES)
         torch.cuda.synchronize()
     t_start = time.perf_counter()
-    events[0].record(stream)
+    K.diag_shader_clock(clk[0])
     for j, p in enumerate(phases):
+        ev_start[j].record(stream)
         for i in range(args.steps):
             run_phase(p, i)
-        events[j + 1].record(stream)
+        ev_end[j].record(stream)
+        K.diag_shader_clock(clk[j + 1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"timed {args.steps} steps in {wall:.3f} s")
 
-    ms = {p: events[j].elapsed_time(events[j + 1]) / args.steps for j, p in enumerate(phases)}
+    ms = {p: ev_start[j].elapsed_time(ev_end[j]) / args.steps for j, p in enumerate(phases)}
+    khz = K.diag_wall_clock_khz()
+    ck = clk.cpu().tolist()
+    sclk = {name: round(c[0] / c[1] * khz / 1e6, 3) if c[1] > 0 else None
+            for name, c in zip(("start",) + tuple(f"after_{p}" for p in phases), ck)}
 
     # ---- fp16-cache comparator, same shape ----
     f16_us = timed_loop(torch, stream, lambda i: K.attn_decode_f16(q, k16, v16, L, sm, out, ws),
@@ -740,6 +751,7 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "sclk_ghz": sclk,
         "encode": {"us": round(ms["encode"] * 1e3, 2), "Mvec_s": round(n_vec / enc_s / 1e6, 1),
                    "ns_per_vec": round(enc_s / n_vec * 1e9, 4), "GB_s": round(enc_gbs, 1),
                    "frac_hbm": round(enc_gbs / HBM_PEAK_GBS, 4),

@@ -248,6 +248,23 @@ kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, 
                                float sm_scale, void* out, kvq_dtype out_dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Measurement aids (not part of the quantizer; the pages define no
+ * such call) ---- */
+
+/* Shader clock probe, for reading benchmark timings: enqueues on `stream`
+ * one wave that spins on a dependent chain of `iters` fp32 FMAs (1 to 2^24;
+ * 200 take about 4 us at 2.4 GHz) and writes to `out` (device memory, at
+ * least 3 uint64, 8-byte aligned, caller-owned) out[0] = shader-clock ticks
+ * and out[1] = wall-clock ticks over the chain (out[2] is overwritten too).
+ * out[0] / out[1] times the wall-clock rate (kvq_diag_wall_clock_khz) is
+ * the shader clock the GPU ran at right after the work queued before it.
+ * Errors: KVQ_ERR_INVALID (NULL out, iters out of range), KVQ_ERR_ALIGN,
+ * KVQ_ERR_HIP (launch). */
+kvq_status kvq_diag_shader_clock(uint64_t* out, int32_t iters, void* stream);
+
+/* Rate of the wall clock the probe reads, in kHz, on the current device. */
+kvq_status kvq_diag_wall_clock_khz(int32_t* khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ __all__ = [
     "KvqError", "Plan", "OPT_MFMA_ROTATION", "SRFT", "SRHT", "IDENTITY", "GROUP",
     "library", "library_path", "encode", "decode", "rotate",
     "attn_workspace_size", "attn_decode", "attn_decode_noalloc", "attn_decode_f16",
-    "cache_shapes",
+    "cache_shapes", "diag_shader_clock", "diag_wall_clock_khz",
 ]
 
 SRFT, SRHT, IDENTITY = 0, 1, 2
@@ -85,6 +85,8 @@ def library() -> ctypes.CDLL:
                                                    _i64, _i64, _i64, _i64, _i64, _f32, _vp, ctypes.c_int, _vp]),
         "kvq_attn_decode_f16": (ctypes.c_int, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
                                                _vp, ctypes.c_int, _vp, _sz, _vp]),
+        "kvq_diag_shader_clock": (ctypes.c_int, [_vp, _i32, _vp]),
+        "kvq_diag_wall_clock_khz": (ctypes.c_int, [ctypes.POINTER(_i32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -350,3 +352,26 @@ def attn_decode_f16(q, k, v, seq_len: int, sm_scale: float, out, workspace):
     _check(_on(idx, library().kvq_attn_decode_f16, D, _ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Tcap, seq_len,
                float(sm_scale), _ptr(out), dt, _ptr(workspace),
                workspace.numel() * workspace.element_size(), _stream(idx)))
+
+
+def diag_shader_clock(out, iters: int = 200):
+    """Measurement aid: enqueue the shader-clock probe on the current stream
+    of out's device; out is a device int64 tensor of at least 3 elements and
+    receives (shader-clock ticks, wall-clock ticks, scratch); 200 iterations
+    take about 4 us at 2.4 GHz (one loop step is about 44 cycles).  The clock in
+    GHz is out[0] / out[1] * diag_wall_clock_khz() / 1e6, once the stream
+    has reached the probe."""
+    import torch
+    _req(out.dtype == torch.int64 and out.numel() >= 3 and out.is_contiguous(),
+         "out must be a contiguous int64 tensor of at least 3 elements")
+    idx = _device(out)
+    _check(_on(idx, library().kvq_diag_shader_clock, _ptr(out), int(iters), _stream(idx)))
+
+
+def diag_wall_clock_khz(device: int | None = None) -> int:
+    """Rate of the probe's wall clock on a device (the current one by default)."""
+    import torch
+    idx = torch.cuda.current_device() if device is None else int(device)
+    khz = ctypes.c_int32(0)
+    _check(_on(idx, library().kvq_diag_wall_clock_khz, ctypes.byref(khz)))
+    return int(khz.value)

@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
 
-SOURCES = ["kvq_api.cpp", "kvq_codec.hip", "kvq_mixed.hip", "kvq_attn.hip", "kvq_attn_f16.hip", "kvq_noalloc.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_codec.hip", "kvq_mixed.hip", "kvq_attn.hip", "kvq_attn_f16.hip", "kvq_noalloc.hip",
+           "kvq_diag.hip"]
 
 # Per-source flags.  Attention: matrix instructions write their results to
 # VGPRs even where the kernel also uses AGPRs (its D=256 form needs more

@@ -535,4 +535,28 @@ kvq_status kvq_attn_decode_f16(int32_t D, const uint16_t* q, const uint16_t* k, 
   }
 }
 
+kvq_status kvq_diag_shader_clock(uint64_t* out, int32_t iters, void* stream) {
+  try {
+    if (!out) return fail(KVQ_ERR_INVALID, "out is NULL");
+    if (!aligned(out, 8)) return fail(KVQ_ERR_ALIGN, "out is not 8-byte aligned");
+    if (iters < 1 || iters > (1 << 24)) return fail(KVQ_ERR_INVALID, "iters must be in [1, 2^24] (got %d)", iters);
+    return hip_status(kvq::launch_shader_clock(out, iters, static_cast<hipStream_t>(stream)),
+                      "kvq_diag_shader_clock launch");
+  } catch (...) {
+    return fail(KVQ_ERR_INVALID, "internal error");
+  }
+}
+
+kvq_status kvq_diag_wall_clock_khz(int32_t* khz) {
+  if (!khz) return fail(KVQ_ERR_INVALID, "khz is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  int rate = 0;
+  e = hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return hip_status(e, "hipDeviceGetAttribute(WallClockRate)");
+  *khz = rate;
+  return ok();
+}
+
 }  // extern "C"

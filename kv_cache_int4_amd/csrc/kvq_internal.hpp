@@ -84,4 +84,8 @@ hipError_t launch_attention(const AttnDesc& d);
 constexpr size_t kAttnScratchBytes = static_cast<size_t>(16) << 20;
 hipError_t attn_scratch(void** ptr);
 
+// Measurement aid: one wave records shader-clock and wall-clock ticks over
+// a dependent chain of iters FMAs into out[0], out[1] (out[2]: scratch).
+hipError_t launch_shader_clock(uint64_t* out, int iters, hipStream_t stream);
+
 }  // namespace kvq

@@ -280,6 +280,20 @@ def test_noalloc_attention_validation():
     assert b"per-GPU buffer" in L.kvq_last_error()
 
 
+def test_diag_shader_clock_validation():
+    """The clock probe's argument checks run on the host (fake pointers:
+    nothing here reaches a launch)."""
+    L = K.library()
+    assert L.kvq_diag_shader_clock(None, 2000, None) == INVALID
+    assert L.kvq_diag_shader_clock(A + 4, 2000, None) == ALIGN
+    assert L.kvq_diag_shader_clock(A, 0, None) == INVALID
+    assert L.kvq_diag_shader_clock(A, (1 << 24) + 1, None) == INVALID
+    assert b"iters" in L.kvq_last_error()
+    assert L.kvq_diag_wall_clock_khz(None) == INVALID
+    with pytest.raises(ValueError):
+        K.diag_shader_clock(torch.zeros(2, dtype=torch.int64))
+
+
 def test_workspace_size_monotone():
     a = K.attn_workspace_size(128, 2, 8, 100)
     b = K.attn_workspace_size(128, 2, 8, 100000)
