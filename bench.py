@@ -333,7 +333,8 @@ def attn256_leg(K, W, torch, stream, dev, n):
     """The decode step at Gemma-3 1B's head shape: batch 64, 4 query heads
     over 1 KV head, D=256, 32768 cached tokens; append one token (K and V in
     one call over the stacked [2B, 1, Tcap] caches), then int4 attention over
-    32769 tokens, against the same attention over the fp16 cache."""
+    32769 tokens, timed as whole steps back to back, against the same
+    attention over the fp16 cache."""
     dc = W.CONFIGS["decode256"]
     B, Hkv, Hq, D, T0 = dc.B, dc.H, dc.Hq, dc.D, dc.T
     L, Tcap = T0 + 1, T0 + 256
@@ -348,10 +349,23 @@ def attn256_leg(K, W, torch, stream, dev, n):
     ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     sm = 1.0 / math.sqrt(D)
-    app = timed_loop(torch, stream, lambda i: K.encode(plan, kv_new, lam_kv, kvc, kvs, T0), n)
+    kc, ks, vc, vs = kvc[:B], kvs[:B], kvc[B:], kvs[B:]
+
+    def attn(i):
+        K.attn_decode(plan, q, kc, ks, lam_k, vc, vs, lam_v, L, sm, out, ws)
+
+    def step(i):
+        K.encode(plan, kv_new, lam_kv, kvc, kvs, T0)
+        attn(i)
+
+    # whole steps back to back (the host queues the next append while the
+    # attention runs, as in a decode loop); the append's share of a step is
+    # the step less the attention alone.  An append timed on its own from
+    # Python is paced by the host (about 10 us per call), not the GPU.
+    stp = timed_loop(torch, stream, step, n)
+    att = timed_loop(torch, stream, attn, n)
+    app = max(stp - att, 0.0)
     app_g = graph_loop(torch, stream, lambda: K.encode(plan, kv_new, lam_kv, kvc, kvs, T0))
-    att = timed_loop(torch, stream, lambda i: K.attn_decode(plan, q, kvc[:B], kvs[:B], lam_k, kvc[B:], kvs[B:],
-                                                            lam_v, L, sm, out, ws), n)
     f16 = timed_loop(torch, stream, lambda i: K.attn_decode_f16(q, k16, v16, L, sm, out, ws), max(5, n // 2))
     ab = B * Hkv * L * 2 * (D // 2 + 2 * (D // 32))
     fb = B * Hkv * L * 2 * 2 * D
@@ -359,10 +373,10 @@ def attn256_leg(K, W, torch, stream, dev, n):
         "workload": "decode step at Gemma-3-1B head shape: batch 64, Hq 4 / Hkv 1, D=256, 32768 cached tokens + 1 "
                     "appended, SRFT, group 32",
         "append_us": round(app, 2), "append_graph_us": round(app_g, 2), "int4_attn_us": round(att, 2),
-        "int4_us_per_step": round(app + att, 2),
+        "int4_us_per_step": round(stp, 2),
         "int4_attn_bytes": ab, "int4_attn_frac_hbm": round(ab / att / 1e3 / HBM_PEAK_GBS, 4),
         "fp16_us_per_step": round(f16, 2), "fp16_frac_hbm": round(fb / f16 / 1e3 / HBM_PEAK_GBS, 4),
-        "int4_over_fp16": round((app + att) / f16, 4),
+        "int4_over_fp16": round(stp / f16, 4),
     }
 
 
