@@ -989,14 +989,22 @@ __host__ __device__ constexpr float lam_sign256(int c) {
   return (ROT == KVQ_ROT_SRFT && c >= 128 + 2 * 33) ? 1.f : -1.f;
 }
 
+// Word offsets of the second half's sign masks and lambda row in LDS: one
+// 16-byte chunk past a whole number of bank rows.
+constexpr int kMaskH256 = 64 + 4;
+constexpr int kLamH256 = 128 + 4;
+
 // MODE 0 writes codes and scales; MODE 1 writes the rotated values w =
 // lambda * R x in fp32 (the transform of this kernel, for checking).
 template <int ROT, int MODE, int FMT, bool ONE>
 __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
   using F = Fmt<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
-  __shared__ __attribute__((aligned(16))) uint32_t mask_lds[128];   // [h][k]
-  __shared__ __attribute__((aligned(16))) float lam_lds[256];       // [h][local channel], sign folded
+  // [h][k] and [h][local channel] (sign folded), each half kPad256 words
+  // past the one before it: the two halves' 16-byte reads at the same
+  // position then fall on different banks
+  __shared__ __attribute__((aligned(16))) uint32_t mask_lds[kMaskH256 + 64];
+  __shared__ __attribute__((aligned(16))) float lam_lds[kLamH256 + 128];
   const int lane = threadIdx.x;
   const int hh = lane & 1;                  // half of the vector
   constexpr float kScale = rot_scale<256, ROT>();
@@ -1006,7 +1014,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
   constexpr bool kPair = ROT != KVQ_ROT_ID;
 
   mask_lds[lane] = pair_mask256<ROT>(a, 0, lane);
-  mask_lds[64 + lane] = pair_mask256<ROT>(a, 1, lane);
+  mask_lds[kMaskH256 + lane] = pair_mask256<ROT>(a, 1, lane);
   // lambda of a tile: lane l holds channels l, l + 64, l + 128, l + 192
   float lam_r[4] = {0.f, 0.f, 0.f, 0.f};
   int64_t tile = blockIdx.x;
@@ -1029,9 +1037,10 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     // them is a store of the tile before, a transform ago)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lam_lds[lane + 64 * q] = lam_sign256<ROT>(lane + 64 * q) * lam_r[q];
+    for (int q = 0; q < 4; ++q)
+      lam_lds[lane + 64 * q + (q >= 2 ? kLamH256 - 128 : 0)] = lam_sign256<ROT>(lane + 64 * q) * lam_r[q];
     uint32_t p[64];
-    const uint4* masks = reinterpret_cast<const uint4*>(mask_lds);   // [hh * 16 + j]
+    const uint4* masks = reinterpret_cast<const uint4*>(mask_lds + kMaskH256 * hh);   // [j]
     if (ROT == KVQ_ROT_SRFT) {
       // pairs 2k + hh: rows 2v (k < 32) and 2v + 1, two dwords per 16-byte chunk
       const int v2 = lane & ~1;
@@ -1054,7 +1063,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const uint4 m = masks[16 * hh + j];
+      const uint4 m = masks[j];
       p[4 * j] ^= m.x; p[4 * j + 1] ^= m.y; p[4 * j + 2] ^= m.z; p[4 * j + 3] ^= m.w;
     }
     // the tile is in registers: the buffer takes the next one
@@ -1087,7 +1096,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
     }
     // keep the lambda reads below the transform
     asm volatile("" ::: "memory");
-    const float4* lam4 = reinterpret_cast<const float4*>(lam_lds);   // [hh * 32 + j / 4]
+    const float4* lam4 = reinterpret_cast<const float4*>(lam_lds + kLamH256 * hh);   // [j / 4]
     const bool valid = (lane >> 1) < t.nv;
 
     if (MODE == 1) {
@@ -1096,7 +1105,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
       if (valid) {
 #pragma unroll
         for (int j = 0; j < 128; j += 4) {
-          const float4 l4 = lam4[32 * hh + j / 4];
+          const float4 l4 = lam4[j / 4];
           float4 o;
           o.x = v[chan_reg<ROT>(j)] * l4.x * kScale;
           o.y = v[chan_reg<ROT>(j + 1)] * l4.y * kScale;
@@ -1118,7 +1127,7 @@ __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
 #pragma unroll
       for (int jj = 0; jj < F::G; jj += 4) {
         const int j = F::G * g + jj;
-        const float4 l4 = lam4[32 * hh + j / 4];
+        const float4 l4 = lam4[j / 4];
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
