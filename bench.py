@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--profile-marks", action="store_true",
                     help="bracket the timed steps with marker kernels and add a calibration copy "
                          "of known size, for --trace-summary of a rocprofv3 run")
+    ap.add_argument("--clock-windows", type=int, default=0, metavar="N",
+                    help="after an idle pause, time N windows of 20 decode-step attention calls, read the "
+                         "shader clock after each, print them as a Markdown table, then exit")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarize a rocprofv3 kernel_trace.csv or counter_collection.csv written "
                          "by a --profile-marks run, then exit")
@@ -556,6 +559,41 @@ def graph_leg(K, torch, stream, plan, kv_new, lam_kv, lam_k, lam_v, cache, T0, q
     return timed_loop(torch, stream, lambda i: g.replay(), n)
 
 
+def clock_windows(K, torch, stream, dev, n_windows, call, encode_burst):
+    """The decode-step attention call against the shader clock: n_windows
+    windows of 20 calls each, the clock read right after every window;
+    first from an idle GPU, then right after a burst of 40 prefix encodes."""
+    import statistics
+    khz = K.diag_wall_clock_khz()
+    clk = torch.zeros((2 * n_windows, 3), dtype=torch.int64, device=dev)
+    rows = []
+    for phase in ("after 0.3 s idle", "after 40 prefix encodes"):
+        torch.cuda.synchronize()
+        if phase.startswith("after 0.3"):
+            time.sleep(0.3)
+        else:
+            encode_burst(40)
+        evs = []
+        for w in range(n_windows):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+            ev[0].record(stream)
+            for i in range(20):
+                call(i)
+                ev[i + 1].record(stream)
+            K.diag_shader_clock(clk[len(rows) + w])
+            evs.append(ev)
+        torch.cuda.synchronize()
+        for w, ev in enumerate(evs):
+            ts = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(20)]
+            rows.append((phase, w, statistics.median(ts), min(ts), max(ts)))
+    ck = clk.cpu().tolist()
+    out = ["| start | window | median us | min us | max us | shader clock after (GHz) |", "|---|---|---|---|---|---|"]
+    for j, (phase, w, med, lo, hi) in enumerate(rows):
+        c = ck[j]
+        out.append(f"| {phase} | {w} | {med:.1f} | {lo:.1f} | {hi:.1f} | {c[0] / c[1] * khz / 1e6:.3f} |")
+    return "\n".join(out)
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -617,6 +655,21 @@ def main():
     ws = torch.empty(K.attn_workspace_size(D, B, Hq, L), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     sm = 1.0 / math.sqrt(D)
+    if args.clock_windows:
+        kc, ks, vc, vs, _, _ = caches[0]
+
+        def call(i):
+            K.attn_decode(aplan, q, kc, ks, lam_k, vc, vs, lam_v, L, sm, out, ws)
+
+        def encode_burst(n):
+            for i in range(n):
+                x, lam, codes, scales, _ = sets[i % len(sets)]
+                K.encode(plan, x, lam, codes, scales)
+
+        for i in range(5):
+            call(i)
+        print(clock_windows(K, torch, stream, dev, args.clock_windows, call, encode_burst), flush=True)
+        return
     g_cfg, g_sets = d256_setup(K, W, torch, dev, args.sets)
     torch.cuda.synchronize()
     log("decode-step caches and D=256 batches ready")
