@@ -45,11 +45,11 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # reported as null once those change.
 TRAFFIC = {
     "attn": {"files": ("kvq_attn.hip", "kvq_attn_kernels.hpp", "kvq_device.hpp"), "sha256": "ede60afeb8f82f6d",
-             "bytes": (295661.9 + 2130.0) * 2 * 1024 + (4361.9 + 128.0) * 1024},
-    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "f2cf76359433493d",
-               "bytes": 57688.4 * 2 * 1024 + 32256.0 * 1024},
-    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "f2cf76359433493d",
-               "bytes": 16451.5 * 2 * 1024 + 114741.9 * 1024},
+             "bytes": (295661.2 + 2130.0) * 2 * 1024 + (4362.1 + 128.0) * 1024},
+    "encode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "6bc5d18ba8a893be",
+               "bytes": 57688.2 * 2 * 1024 + 32256.0 * 1024},
+    "decode": {"files": ("kvq_codec.hip", "kvq_device.hpp"), "sha256": "6bc5d18ba8a893be",
+               "bytes": 16451.5 * 2 * 1024 + 114715.9 * 1024},
 }
 
 

@@ -1000,9 +1000,9 @@ template <int ROT, int MODE, int FMT, bool ONE>
 __global__ void __launch_bounds__(64, 2) encode256_kernel(CodecArgs a) {
   using F = Fmt<FMT>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsTile];
-  // [h][k] and [h][local channel] (sign folded), each half kPad256 words
-  // past the one before it: the two halves' 16-byte reads at the same
-  // position then fall on different banks
+  // [h][k] and [h][local channel] (sign folded); half 1 starts kMaskH256 /
+  // kLamH256 words in, so the two halves' 16-byte reads at the same
+  // position fall on different banks
   __shared__ __attribute__((aligned(16))) uint32_t mask_lds[kMaskH256 + 64];
   __shared__ __attribute__((aligned(16))) float lam_lds[kLamH256 + 128];
   const int lane = threadIdx.x;
